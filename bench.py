@@ -1,0 +1,202 @@
+#!/usr/bin/env python3
+"""Throughput of the fused mel-spectrogram forward pass on one MI355X.
+
+A step is one fm_forward launch over one whole batch of the chosen workload
+(default: 8 x 480000 float32 samples, n_fft 400, hop 160, 128 HTK mels, the
+Whisper-shaped case).  Inputs are resident in HBM before timing starts.  To
+keep the 256 MB Infinity Cache from serving the data, the steps rotate over
+enough input/output buffer sets to exceed 2 x 256 MB.
+
+Prints ONE JSON line (rank 0, N = 1):
+  value        mel frames per second over the K timed steps (events around
+               the whole timed region, torch's current stream);
+  roofline     achieved HBM GB/s of the kernel: algorithmic bytes (input +
+               output) / mean per-launch duration from event pairs around
+               each launch on the launch stream, against 8 TB/s;
+  cpu_baseline the f64 oracle timed on this host on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from stft_mel_spectrogram_amd import workloads as W  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "mel frames/sec and achieved HBM GB/s (% roofline), 8×480000 n_fft=400 128 mels"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--workload", default="whisper", choices=sorted(W.WORKLOADS))
+    ap.add_argument("--sets", type=int, default=0, help="rotating buffer sets (0: enough for 512 MB)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-copy-probe", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle sample")
+    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                    help="measured HBM bytes per launch (from rocprofv3 --pmc), if present")
+    return ap.parse_args()
+
+
+def cpu_baseline(cfg: dict, budget_s: float) -> dict:
+    """The oracle as it stands, on whole signals of the workload, repeated
+    until about `budget_s` seconds of CPU work; frames/s."""
+    from oracle import mel_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    targs = W.transform_args(cfg)
+    x = W.make_signal(W.workload(cfg["name"], batch=1))
+    t0 = time.perf_counter()
+    frames = 0
+    runs = 0
+    while True:
+        y = O.mel_spectrogram(x, **targs)
+        frames += y.shape[0] * y.shape[-1]
+        runs += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": frames / dt, "unit": "frames/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{runs} x one {cfg['length']}-sample signal of the {cfg['name']} workload "
+                      f"({frames} frames, {dt:.1f} s, numpy f64 with BLAS threads)"}
+
+
+def copy_probe(torch, dev, nbytes: int, reps: int = 50) -> dict:
+    """Device-to-device copy of a known size (torch's copy kernel), rotating
+    over buffers larger than the Infinity Cache: the measured copy peak, and
+    the reference kernel for scaling HBM byte counters."""
+    n = nbytes // 4
+    sets = max(2, int(np.ceil(2 * 256e6 / (2 * nbytes))) + 1)
+    src = [torch.ones(n, device=dev) for _ in range(sets)]
+    dst = [torch.empty(n, device=dev) for _ in range(sets)]
+    for i in range(5):
+        dst[i % sets].copy_(src[i % sets])
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(reps):
+        dst[i % sets].copy_(src[i % sets])
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    return {"bytes_read": n * 4, "bytes_written": n * 4, "ms": ms,
+            "gbps": 2 * n * 4 / (ms * 1e-3) / 1e9}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(frames are independent: a batch would shard across GPUs with no exchange).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from stft_mel_spectrogram_amd import MelSpectrogram
+
+    cfg = W.workload(args.workload)
+    x_np = W.make_signal(cfg)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    mel = MelSpectrogram(device=dev, **W.transform_args(cfg))
+    B, L = x_np.shape
+    T = mel.out_frames(L)
+    in_bytes = x_np.nbytes
+    out_bytes = B * cfg["n_mels"] * T * 4
+    algo_bytes = in_bytes + out_bytes
+    frames = B * T
+
+    sets = args.sets or max(2, int(np.ceil(2 * 256e6 / algo_bytes)) + 1)
+    x0 = torch.from_numpy(x_np).to(dev)
+    xs = [x0] + [x0.clone() for _ in range(sets - 1)]
+    ys = [torch.empty((B, cfg["n_mels"], T), dtype=torch.float32, device=dev) for _ in range(sets)]
+    stream = torch.cuda.current_stream(dev)
+
+    for i in range(args.warmup):
+        mel(xs[i % sets], out=ys[i % sets])
+    torch.cuda.synchronize()
+
+    # (1) throughput: events around the whole timed region
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for i in range(args.steps):
+        mel(xs[i % sets], out=ys[i % sets])
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = ev0.elapsed_time(ev1)
+    ms_per_step = total_ms / args.steps
+
+    # (2) per-launch kernel duration: an event pair around every launch
+    n_k = min(args.steps, 200)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(n_k)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(n_k)]
+    torch.cuda.synchronize()
+    for i in range(n_k):
+        starts[i].record(stream)
+        mel(xs[i % sets], out=ys[i % sets])
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    durs = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+    kern_ms = float(np.mean(durs))
+    achieved = algo_bytes / (kern_ms * 1e-3) / 1e9
+
+    traffic = None
+    if os.path.exists(args.traffic_json):
+        try:
+            t = json.load(open(args.traffic_json))
+            if t.get("workload") == cfg["name"]:
+                traffic = t.get("bytes_per_launch")
+        except Exception:
+            traffic = None
+
+    res = {
+        "metric": METRIC,
+        "value": frames / (ms_per_step * 1e-3),
+        "unit": "frames/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i16->f32" if cfg["dtype"] == "i16" else "f32",
+        "data": "synthetic (seeded; see workloads.py)",
+        "config": {"workload": f"{cfg['name']}: {B}x{L} {cfg['dtype']}, n_fft={cfg['n_fft']} "
+                               f"hop={cfg['hop_length']} {cfg['n_mels']} mels, power={cfg['power']}",
+                   "batch": B, "length": L, "n_frames": T, "buffer_sets": sets,
+                   "parallelism": "single GPU"},
+        "hbm_gbps_step": algo_bytes / (ms_per_step * 1e-3) / 1e9,
+        "kernel_ms_mean": kern_ms,
+        "kernel_ms_median": float(np.median(durs)),
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
+                     "algorithmic_bytes": algo_bytes},
+    }
+    if not args.no_copy_probe:
+        res["copy_probe"] = copy_probe(torch, dev, in_bytes)
+        res["copy_probe_large"] = copy_probe(torch, dev, 512 << 20, reps=20)
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,166 @@
+/*
+ * fm.h -- C ABI of the fused mel-spectrogram forward pass for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The operation is the one the flashmel 0.1.0 page (PyPI sdist diff view)
+ * describes: a torchaudio-MelSpectrogram-compatible forward pass -- centre
+ * padding, framing at hop_length, periodic Hann window, real-to-complex FFT of
+ * size n_fft, |X|^power and a projection onto a sparse triangular mel
+ * filterbank -- in a single kernel launch (README "How it works"; argument
+ * list and shape contract in README "Usage"; window and filterbank packing in
+ * flashmel/filters.py).
+ *
+ * Conventions for every entry point:
+ *   - Return value: FM_OK (0) on success, a negative FM_E_* code otherwise.
+ *     On failure a message is kept per thread; fm_last_error() returns it.
+ *   - Pointers named `in`/`out` are DEVICE pointers owned by the caller.
+ *     Plans own their device tables; fm_plan_destroy frees them.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *   - Nothing here synchronises the device; fm_forward only enqueues.
+ */
+#ifndef FM_H_
+#define FM_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------- */
+#define FM_OK 0
+#define FM_E_INVAL (-1)       /* invalid argument (bad value, null pointer)  */
+#define FM_E_UNSUPPORTED (-2) /* valid for torchaudio, not built here         */
+#define FM_E_HIP (-3)         /* a HIP runtime call failed                    */
+#define FM_E_NOMEM (-4)       /* host or device allocation failed            */
+#define FM_E_NODEVICE (-5)    /* plan has no device tables (host-only plan)  */
+
+/* ---- enumerations -------------------------------------------------------- */
+/* pad_mode: how frames read beyond the signal when center != 0 (README "How
+ * it works": all four pad modes are index arithmetic).                      */
+#define FM_PAD_REFLECT 0   /* x[-i] = x[i], edge sample not repeated         */
+#define FM_PAD_CONSTANT 1  /* zeros                                          */
+#define FM_PAD_REPLICATE 2 /* edge sample repeated                           */
+#define FM_PAD_CIRCULAR 3  /* periodic wrap                                  */
+
+/* mel_scale and norm: passed through to the filterbank construction
+ * (flashmel/filters.py pack_fbank).                                        */
+#define FM_MEL_HTK 0
+#define FM_MEL_SLANEY 1
+#define FM_NORM_NONE 0
+#define FM_NORM_SLANEY 1
+
+/* input sample type (README "Usage": float32, or int16 raw PCM scaled by
+ * 1/32768).                                                                */
+#define FM_F32 0
+#define FM_I16 1
+
+typedef struct fm_plan fm_plan;
+
+/*
+ * fm_plan_create -- build a plan on the CURRENT HIP device.
+ *
+ * Arguments are torchaudio MelSpectrogram's (README "Usage"):
+ *   sample_rate > 0; n_fft in {400, 1024, 2048} (others: FM_E_UNSUPPORTED;
+ *   README "Usage" allows 400 and powers of two 64..16384);
+ *   0 < win_length <= n_fft (a shorter window is zero-padded centred,
+ *   flashmel/filters.py make_window); hop_length > 0;
+ *   1 <= n_mels <= 256 (README "Usage");
+ *   0 <= f_min < f_max <= sample_rate/2;  power > 0 (2: power spectrum,
+ *   1: magnitude);  center 0/1;  pad_mode FM_PAD_*;  mel_scale FM_MEL_*;
+ *   norm FM_NORM_*.
+ *
+ * The window, the CSR filterbank (per mel: first bin, run length, offset,
+ * weights), the FFT twiddle tables and the tile geometry are built in
+ * float64 on the host, rounded once to float32 and uploaded.  *out receives
+ * a plan that owns that device memory; it is immutable and may be used
+ * concurrently from several streams of the same device.
+ *
+ * Errors: FM_E_INVAL / FM_E_UNSUPPORTED for arguments, FM_E_NOMEM,
+ * FM_E_HIP (no device, upload failed).  *out is set to NULL on failure.
+ */
+int fm_plan_create(fm_plan** out, int sample_rate, int n_fft, int win_length,
+                   int hop_length, int n_mels, double f_min, double f_max,
+                   double power, int center, int pad_mode, int mel_scale,
+                   int norm);
+
+/*
+ * fm_plan_create_host -- same arguments and validation as fm_plan_create,
+ * but builds only the host tables and touches no GPU.  Such a plan serves
+ * fm_plan_info / fm_plan_tables / fm_out_frames; fm_forward on it returns
+ * FM_E_NODEVICE.
+ */
+int fm_plan_create_host(fm_plan** out, int sample_rate, int n_fft,
+                        int win_length, int hop_length, int n_mels,
+                        double f_min, double f_max, double power, int center,
+                        int pad_mode, int mel_scale, int norm);
+
+/*
+ * fm_forward -- enqueue one mel-spectrogram forward pass on `stream`.
+ *
+ *   in     device pointer to [batch, length] samples, row-major, contiguous,
+ *          of type in_dtype (FM_F32: float, FM_I16: int16_t).
+ *   out    device pointer to [batch, n_mels, n_frames] float32, row-major,
+ *          contiguous (frames fastest), n_frames = fm_out_frames(plan,
+ *          length).  Every element is written.
+ *   batch  >= 0 (0 is a no-op); length >= 1, and with center + reflect
+ *          padding length > n_fft/2 (a single reflection), otherwise
+ *          FM_E_INVAL; without center length >= n_fft.
+ *
+ * One kernel launch; no allocation, no synchronisation.  Launch errors are
+ * reported as FM_E_HIP.  The plan must live on the device that is current.
+ */
+int fm_forward(const fm_plan* plan, const void* in, int in_dtype,
+               int64_t batch, int64_t length, float* out, void* stream);
+
+/*
+ * fm_out_frames -- frames per signal for a given length:
+ *   center: 1 + floor(length / hop) for even n_fft (generally
+ *           1 + floor((length + 2*(n_fft/2) - n_fft) / hop));
+ *   else:   1 + floor((length - n_fft) / hop).
+ * Returns a negative FM_E_* code if the length is invalid for the plan.
+ */
+int64_t fm_out_frames(const fm_plan* plan, int64_t length);
+
+/* fm_plan_destroy -- free the plan and its device tables.  NULL is a no-op. */
+int fm_plan_destroy(fm_plan* plan);
+
+/* Human-readable text for a status code (static storage).                 */
+const char* fm_strerror(int status);
+
+/* Message of the last failure on this thread ("" if none).                */
+const char* fm_last_error(void);
+
+/* ---- host-side inspection (used by CPU tests; no GPU needed) ------------ */
+
+typedef struct fm_plan_info {
+  int n_fft, win_length, hop_length, n_mels, n_freqs; /* n_freqs = n_fft/2+1 */
+  int nnz;          /* nonzero filterbank weights (CSR length)              */
+  int w_max;        /* widest filter (bins)                                 */
+  int fft_n1, fft_n2; /* complex FFT of n_fft/2 = fft_n1 * fft_n2 points    */
+  int tile_frames;  /* frames per workgroup tile                            */
+  int threads;      /* threads per workgroup                                */
+  int lds_bytes;    /* dynamic LDS per workgroup                            */
+  int has_device;   /* 1 if the plan owns device tables                     */
+} fm_plan_info;
+
+int fm_plan_info_get(const fm_plan* plan, fm_plan_info* info);
+
+/*
+ * fm_plan_tables -- copy the host tables of a plan.  Any pointer may be NULL
+ * to skip that table.  Sizes: window[n_fft] (float32, unscaled; the device
+ * copy is scaled by 1/2 for the real-FFT post-processing);
+ * mel_first[n_mels], mel_len[n_mels], mel_off[n_mels] (int32; CSR rows,
+ * len 0 for an empty filter); mel_w[nnz] (float32);
+ * tw_m[2*(n_fft/2)] interleaved re,im of exp(-2*pi*i*j/(n_fft/2));
+ * tw_n[2*(n_fft/2)] interleaved re,im of exp(-2*pi*i*k/n_fft).
+ */
+int fm_plan_tables(const fm_plan* plan, float* window, int32_t* mel_first,
+                   int32_t* mel_len, int32_t* mel_off, float* mel_w,
+                   float* tw_m, float* tw_n);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FM_H_ */

@@ -1,0 +1,133 @@
+// C ABI of the fused mel-spectrogram forward pass (declared in include/fm.h).
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "fm_internal.h"
+
+struct fm_plan {
+  fm::Plan p;
+};
+
+namespace fm {
+
+namespace {
+thread_local std::string g_last_error;
+}
+
+int set_error(int code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+const char* last_error_cstr() { return g_last_error.c_str(); }
+
+}  // namespace fm
+
+namespace {
+
+int create(fm_plan** out, bool with_device, int sample_rate, int n_fft, int win_length,
+           int hop_length, int n_mels, double f_min, double f_max, double power, int center,
+           int pad_mode, int mel_scale, int norm) {
+  if (!out) return fm::set_error(FM_E_INVAL, "out must not be NULL");
+  *out = nullptr;
+  fm_plan* h = new (std::nothrow) fm_plan();
+  if (!h) return fm::set_error(FM_E_NOMEM, "host allocation failed");
+  int st = fm::build_host_plan(h->p, sample_rate, n_fft, win_length, hop_length, n_mels, f_min,
+                               f_max, power, center, pad_mode, mel_scale, norm);
+  if (st == FM_OK && with_device) st = fm::upload_plan(h->p);
+  if (st != FM_OK) {
+    fm::free_plan_device(h->p);
+    delete h;
+    return st;
+  }
+  *out = h;
+  return FM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fm_plan_create(fm_plan** out, int sample_rate, int n_fft, int win_length, int hop_length,
+                   int n_mels, double f_min, double f_max, double power, int center, int pad_mode,
+                   int mel_scale, int norm) {
+  return create(out, true, sample_rate, n_fft, win_length, hop_length, n_mels, f_min, f_max,
+                power, center, pad_mode, mel_scale, norm);
+}
+
+int fm_plan_create_host(fm_plan** out, int sample_rate, int n_fft, int win_length,
+                        int hop_length, int n_mels, double f_min, double f_max, double power,
+                        int center, int pad_mode, int mel_scale, int norm) {
+  return create(out, false, sample_rate, n_fft, win_length, hop_length, n_mels, f_min, f_max,
+                power, center, pad_mode, mel_scale, norm);
+}
+
+int fm_forward(const fm_plan* plan, const void* in, int in_dtype, int64_t batch, int64_t length,
+               float* out, void* stream) {
+  if (!plan) return fm::set_error(FM_E_INVAL, "plan must not be NULL");
+  return fm::launch_forward(plan->p, in, in_dtype, batch, length, out, stream);
+}
+
+int64_t fm_out_frames(const fm_plan* plan, int64_t length) {
+  if (!plan) return fm::set_error(FM_E_INVAL, "plan must not be NULL");
+  return fm::out_frames(plan->p, length);
+}
+
+int fm_plan_destroy(fm_plan* plan) {
+  if (!plan) return FM_OK;
+  fm::free_plan_device(plan->p);
+  delete plan;
+  return FM_OK;
+}
+
+const char* fm_strerror(int status) {
+  switch (status) {
+    case FM_OK: return "success";
+    case FM_E_INVAL: return "invalid argument";
+    case FM_E_UNSUPPORTED: return "unsupported configuration";
+    case FM_E_HIP: return "HIP runtime error";
+    case FM_E_NOMEM: return "out of memory";
+    case FM_E_NODEVICE: return "plan has no device tables";
+    default: return "unknown status";
+  }
+}
+
+const char* fm_last_error(void) { return fm::last_error_cstr(); }
+
+int fm_plan_info_get(const fm_plan* plan, fm_plan_info* info) {
+  if (!plan || !info) return fm::set_error(FM_E_INVAL, "plan and info must not be NULL");
+  const fm::Plan& p = plan->p;
+  info->n_fft = p.n_fft;
+  info->win_length = p.win_length;
+  info->hop_length = p.hop;
+  info->n_mels = p.n_mels;
+  info->n_freqs = p.n_freqs;
+  info->nnz = p.nnz;
+  info->w_max = p.w_max;
+  info->fft_n1 = p.fft.n1;
+  info->fft_n2 = p.fft.n2;
+  info->tile_frames = p.tile_frames;
+  info->threads = p.threads;
+  info->lds_bytes = p.lds_bytes;
+  info->has_device = p.has_device ? 1 : 0;
+  return FM_OK;
+}
+
+int fm_plan_tables(const fm_plan* plan, float* window, int32_t* mel_first, int32_t* mel_len,
+                   int32_t* mel_off, float* mel_w, float* tw_m, float* tw_n) {
+  if (!plan) return fm::set_error(FM_E_INVAL, "plan must not be NULL");
+  const fm::Plan& p = plan->p;
+  if (window) std::memcpy(window, p.window.data(), p.window.size() * sizeof(float));
+  for (int m = 0; m < p.n_mels; ++m) {
+    if (mel_first) mel_first[m] = p.rows[m].first;
+    if (mel_len) mel_len[m] = p.rows[m].len;
+    if (mel_off) mel_off[m] = p.rows[m].off;
+  }
+  if (mel_w && p.nnz) std::memcpy(mel_w, p.mel_w.data(), p.mel_w.size() * sizeof(float));
+  if (tw_m) std::memcpy(tw_m, p.tw_m.data(), p.tw_m.size() * sizeof(float));
+  if (tw_n) std::memcpy(tw_n, p.tw_n.data(), p.tw_n.size() * sizeof(float));
+  return FM_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,223 @@
+// Host plan builder for the fused mel-spectrogram forward pass.
+//
+// Everything the kernel reads besides the signal is built here once per plan,
+// in float64, and rounded once to float32:
+//   * the STFT window: periodic Hann of win_length, zero-padded centred to
+//     n_fft (flashmel 0.1.0 page, flashmel/filters.py make_window);
+//   * the triangular mel filterbank in CSR form -- per mel the first bin of
+//     its contiguous support, the run length and the weights -- with empty
+//     filters kept as zero-length rows (flashmel/filters.py pack_fbank keeps
+//     per-mel start/width rows; README "How it works": the projection loop
+//     runs over each filter's actual width);
+//   * the twiddle tables of the complex FFT of n_fft/2 points that carries
+//     the real FFT, and of the real-FFT post-processing step;
+//   * the tile geometry of the kernel launch.
+// No GPU is touched here, so CPU tests can inspect every table.
+#include <algorithm>
+#include <cmath>
+#include <cstdlib>
+#include <sstream>
+
+#include "fm_internal.h"
+
+namespace fm {
+
+namespace {
+
+constexpr double kPi = 3.14159265358979323846264338327950288;
+
+// cos and sin of 2*pi*j/n with the angle folded into [0, pi/4] in exact
+// integer arithmetic before any rounding, so table entries are within one
+// float64 rounding of the true values (before the final float32 rounding).
+void cos_sin_2pi(int64_t j, int64_t n, double* c, double* s) {
+  int64_t d = 8 * n;                      // angle = 2*pi*a/d
+  int64_t a = ((j % n) + n) % n * 8;      // a in [0, d)
+  // Reduce to [0, d/8] tracking the octant symmetries.
+  double sc = 1.0, ss = 1.0;
+  if (a > d / 2) { a = d - a; ss = -1.0; }             // theta -> 2pi - theta
+  if (a > d / 4) { a = d / 2 - a; sc = -sc; }          // theta -> pi - theta
+  bool swap = false;
+  if (a > d / 8) { a = d / 4 - a; swap = true; }       // theta -> pi/2 - theta
+  double th = 2.0 * kPi * static_cast<double>(a) / static_cast<double>(d);
+  double cr = std::cos(th), sr = std::sin(th);
+  if (swap) std::swap(cr, sr);
+  *c = sc * cr;
+  *s = ss * sr;
+}
+
+double hz_to_mel(double f, int scale) {
+  if (scale == FM_MEL_HTK) return 2595.0 * std::log10(1.0 + f / 700.0);
+  // Slaney: linear below 1 kHz (200/3 Hz per mel), log above (27 mel per x6.4)
+  const double f_sp = 200.0 / 3.0, min_log_hz = 1000.0;
+  const double min_log_mel = min_log_hz / f_sp, logstep = std::log(6.4) / 27.0;
+  if (f >= min_log_hz) return min_log_mel + std::log(f / min_log_hz) / logstep;
+  return f / f_sp;
+}
+
+double mel_to_hz(double m, int scale) {
+  if (scale == FM_MEL_HTK) return 700.0 * (std::pow(10.0, m / 2595.0) - 1.0);
+  const double f_sp = 200.0 / 3.0, min_log_hz = 1000.0;
+  const double min_log_mel = min_log_hz / f_sp, logstep = std::log(6.4) / 27.0;
+  if (m >= min_log_mel) return min_log_hz * std::exp(logstep * (m - min_log_mel));
+  return f_sp * m;
+}
+
+// Complex FFT of M = n_fft/2 points split as n1 * n2: the first pass runs
+// n2 transforms of n1 points, the second n1 transforms of n2 points.
+bool fft_shape_for(int n_fft, FftShape* s) {
+  switch (n_fft) {
+    case 400: *s = {8, 25}; return true;    // 200 = 8 * 25 (radix 2*4, 5*5)
+    case 1024: *s = {32, 16}; return true;  // 512 = 32 * 16 (radix 4*8, 4*4)
+    case 2048: *s = {32, 32}; return true;  // 1024 = 32 * 32
+    default: return false;
+  }
+}
+
+int default_tile_frames(int n_fft) {
+  switch (n_fft) {
+    case 400: return 32;
+    case 1024: return 16;
+    default: return 8;
+  }
+}
+
+std::string fmt(const char* what, double v) {
+  std::ostringstream o;
+  o << what << " (got " << v << ")";
+  return o.str();
+}
+
+}  // namespace
+
+int64_t out_frames(const Plan& p, int64_t length) {
+  if (length < 1) return set_error(FM_E_INVAL, "length must be >= 1");
+  if (p.center) {
+    if (p.pad_mode == FM_PAD_REFLECT && length <= p.pad_left)
+      return set_error(FM_E_INVAL,
+                       "reflect padding needs length > n_fft/2 (one reflection)");
+    int64_t lp = length + 2 * static_cast<int64_t>(p.pad_left);
+    if (lp < p.n_fft) return set_error(FM_E_INVAL, "signal shorter than one frame");
+    return 1 + (lp - p.n_fft) / p.hop;
+  }
+  if (length < p.n_fft) return set_error(FM_E_INVAL, "length < n_fft without centring");
+  return 1 + (length - p.n_fft) / p.hop;
+}
+
+int build_host_plan(Plan& p, int sample_rate, int n_fft, int win_length,
+                    int hop_length, int n_mels, double f_min, double f_max,
+                    double power, int center, int pad_mode, int mel_scale,
+                    int norm) {
+  // ---- validation (all host-side integer / float checks) ------------------
+  if (sample_rate <= 0) return set_error(FM_E_INVAL, fmt("sample_rate must be > 0", sample_rate));
+  if (n_fft <= 0) return set_error(FM_E_INVAL, fmt("n_fft must be > 0", n_fft));
+  if (win_length <= 0 || win_length > n_fft)
+    return set_error(FM_E_INVAL, fmt("need 0 < win_length <= n_fft", win_length));
+  if (hop_length <= 0) return set_error(FM_E_INVAL, fmt("hop_length must be > 0", hop_length));
+  if (n_mels <= 0) return set_error(FM_E_INVAL, fmt("n_mels must be > 0", n_mels));
+  if (!(f_min >= 0.0) || !(f_max > f_min))
+    return set_error(FM_E_INVAL, "need 0 <= f_min < f_max");
+  if (f_max > sample_rate / 2.0)
+    return set_error(FM_E_INVAL, fmt("f_max must be <= sample_rate/2", f_max));
+  if (!(power > 0.0) || !std::isfinite(power))
+    return set_error(FM_E_INVAL, fmt("power must be a positive finite number", power));
+  if (center != 0 && center != 1) return set_error(FM_E_INVAL, "center must be 0 or 1");
+  if (pad_mode < FM_PAD_REFLECT || pad_mode > FM_PAD_CIRCULAR)
+    return set_error(FM_E_INVAL, fmt("unknown pad_mode", pad_mode));
+  if (mel_scale != FM_MEL_HTK && mel_scale != FM_MEL_SLANEY)
+    return set_error(FM_E_INVAL, fmt("unknown mel_scale", mel_scale));
+  if (norm != FM_NORM_NONE && norm != FM_NORM_SLANEY)
+    return set_error(FM_E_INVAL, fmt("unknown norm", norm));
+  if (n_mels > 256) return set_error(FM_E_UNSUPPORTED, fmt("n_mels > 256 is not supported", n_mels));
+  FftShape fs;
+  if (!fft_shape_for(n_fft, &fs))
+    return set_error(FM_E_UNSUPPORTED, fmt("n_fft not built (supported: 400, 1024, 2048)", n_fft));
+
+  p.sample_rate = sample_rate; p.n_fft = n_fft; p.win_length = win_length;
+  p.hop = hop_length; p.n_mels = n_mels; p.f_min = f_min; p.f_max = f_max;
+  p.power = power; p.center = center; p.pad_mode = pad_mode;
+  p.mel_scale = mel_scale; p.norm = norm;
+  p.n_freqs = n_fft / 2 + 1;
+  p.pad_left = center ? n_fft / 2 : 0;
+  p.fft = fs;
+  const int M = n_fft / 2;
+
+  // ---- window: periodic Hann of win_length, centred in n_fft --------------
+  p.window.assign(n_fft, 0.0f);
+  const int left = (n_fft - win_length) / 2;
+  for (int n = 0; n < win_length; ++n) {
+    double c, s;
+    cos_sin_2pi(n, win_length, &c, &s);
+    p.window[left + n] = static_cast<float>(0.5 - 0.5 * c);
+  }
+
+  // ---- mel filterbank: triangles on the mel scale, CSR rows ---------------
+  std::vector<double> fpts(n_mels + 2);
+  const double m_lo = hz_to_mel(f_min, mel_scale), m_hi = hz_to_mel(f_max, mel_scale);
+  for (int i = 0; i < n_mels + 2; ++i)
+    fpts[i] = mel_to_hz(m_lo + i * (m_hi - m_lo) / (n_mels + 1), mel_scale);
+  const double half_sr = static_cast<double>(sample_rate / 2);
+  p.rows.assign(n_mels, MelRow{0, 0, 0, 0});
+  p.mel_w.clear();
+  p.w_max = 0;
+  std::vector<double> wrow(p.n_freqs);
+  for (int m = 0; m < n_mels; ++m) {
+    const double lo = fpts[m], mid = fpts[m + 1], hi = fpts[m + 2];
+    const double scale = (norm == FM_NORM_SLANEY) ? 2.0 / (hi - lo) : 1.0;
+    int first = -1, last = -1;
+    for (int k = 0; k < p.n_freqs; ++k) {
+      const double f = static_cast<double>(k) * half_sr / static_cast<double>(p.n_freqs - 1);
+      const double up = (f - lo) / (mid - lo);
+      const double down = (hi - f) / (hi - mid);
+      double w = std::min(up, down);
+      w = w > 0.0 ? w * scale : 0.0;
+      wrow[k] = w;
+      if (w > 0.0) {
+        if (first < 0) first = k;
+        last = k;
+      }
+    }
+    MelRow r{0, 0, static_cast<int32_t>(p.mel_w.size()), 0};
+    if (first >= 0) {
+      r.first = first;
+      r.len = last - first + 1;
+      for (int k = first; k <= last; ++k) p.mel_w.push_back(static_cast<float>(wrow[k]));
+      p.w_max = std::max(p.w_max, r.len);
+    }
+    p.rows[m] = r;
+  }
+  p.nnz = static_cast<int>(p.mel_w.size());
+
+  // ---- twiddles ------------------------------------------------------------
+  p.tw_m.assign(2 * M, 0.0f);
+  p.tw_n.assign(2 * M, 0.0f);
+  for (int j = 0; j < M; ++j) {
+    double c, s;
+    cos_sin_2pi(j, M, &c, &s);
+    p.tw_m[2 * j] = static_cast<float>(c);
+    p.tw_m[2 * j + 1] = static_cast<float>(-s);
+    cos_sin_2pi(j, n_fft, &c, &s);
+    p.tw_n[2 * j] = static_cast<float>(c);
+    p.tw_n[2 * j + 1] = static_cast<float>(-s);
+  }
+
+  // ---- tile geometry -------------------------------------------------------
+  int tile = default_tile_frames(n_fft);
+  if (const char* e = std::getenv("FM_TILE_FRAMES")) {
+    int v = std::atoi(e);
+    if (v >= 1 && v <= 64) tile = v;
+  }
+  // The second FFT pass gives each thread one pair of n2-point transforms.
+  while (tile > 1 && tile * (fs.n1 / 2) > p.threads) --tile;
+  p.tile_frames = tile;
+  p.lds_y_bytes = tile * M * 8;  // complex exchange buffer; power tile aliases it
+  const int pw_bytes = tile * p.n_freqs * 4;
+  if (pw_bytes > p.lds_y_bytes) p.lds_y_bytes = pw_bytes;
+  p.lds_y_bytes = (p.lds_y_bytes + 15) / 16 * 16;
+  const int w_bytes = (p.nnz + 3) / 4 * 16;
+  p.lds_bytes = p.lds_y_bytes + w_bytes + n_mels * static_cast<int>(sizeof(MelRow));
+  if (p.lds_bytes > 160 * 1024)
+    return set_error(FM_E_UNSUPPORTED, "tile does not fit in 160 KB of LDS");
+  return FM_OK;
+}
+
+}  // namespace fm

@@ -1,0 +1,199 @@
+"""GPU parity: the HIP path (through the C ABI) against the f64 oracle.
+
+Bar: max |gpu - ref| <= 1e-4 * (1 + |ref|) elementwise (the fp32 tolerance
+atol = rtol = 1e-4 the flashmel page states against torchaudio, README
+"Development", here against the f64 definition).
+"""
+import numpy as np
+import pytest
+
+from oracle import mel_oracle as O
+from stft_mel_spectrogram_amd import workloads as W
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-4
+
+
+def _require_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def run_gpu(x_np, **targs):
+    from stft_mel_spectrogram_amd import MelSpectrogram
+    _require_gpu()
+    mel = MelSpectrogram(**targs)
+    x = torch.from_numpy(np.ascontiguousarray(x_np)).to("cuda")
+    y = mel(x)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+def oracle(x_np, **targs):
+    return O.mel_spectrogram(x_np, chunk=4, **targs)
+
+
+def assert_parity(got, ref, what=""):
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), what
+    err = np.abs(got.astype(np.float64) - ref)
+    bound = TOL * (1.0 + np.abs(ref))
+    worst = np.unravel_index(np.argmax(err / bound), err.shape)
+    ratio = float((err / bound)[worst])
+    print(f"[parity] {what}: max err/bound = {ratio:.3g} at {worst} "
+          f"(gpu {got[worst]:.6g}, ref {ref[worst]:.6g}), max abs err {err.max():.3g}", flush=True)
+    assert ratio <= 1.0, what
+
+
+# ------------------------------------------------------------------ small cases: every output
+
+SMALL = [
+    ("tiny", dict()),                                     # 1 x 16000, 101 frames (4 tiles, ragged)
+    ("whisper", dict(batch=3, length=48_000)),           # 301 frames per signal
+    ("int16", dict(batch=2, length=48_000)),
+    ("pow2", dict()),                                     # full size: 8 x 32768
+    ("large", dict(batch=3)),                             # 3 x 220500, n_fft 2048, power 1
+]
+
+
+@pytest.mark.parametrize("name,over", SMALL, ids=[s[0] for s in SMALL])
+def test_parity_small(name, over):
+    cfg = W.workload(name, **over)
+    x = W.make_signal(cfg)
+    targs = W.transform_args(cfg)
+    print(f"[case] {name} {x.shape} {x.dtype}", flush=True)
+    assert_parity(run_gpu(x, **targs), oracle(x, **targs), name)
+
+
+# ------------------------------------------------------------------ full workloads
+
+@pytest.mark.parametrize("name", ["whisper", "int16"])
+def test_parity_full_whisper_shape(name):
+    cfg = W.workload(name)
+    x = W.make_signal(cfg)
+    targs = W.transform_args(cfg)
+    print(f"[case] full {name} {x.shape}", flush=True)
+    assert_parity(run_gpu(x, **targs), oracle(x, **targs), f"full {name}")
+
+
+def test_parity_full_large_sampled_rows():
+    """64 x 220500: every output is checked for finiteness and sign; the
+    oracle recomputes 6 whole rows (first, last and four inside)."""
+    cfg = W.workload("large")
+    x = W.make_signal(cfg)
+    targs = W.transform_args(cfg)
+    got = run_gpu(x, **targs)
+    assert got.shape == (64, 128, 431)
+    assert np.all(np.isfinite(got)) and np.all(got >= 0)
+    rows = [0, 1, 17, 31, 50, 63]
+    assert_parity(got[rows], oracle(x[rows], **targs), "full large (sampled rows)")
+
+
+# ------------------------------------------------------------------ edge cases
+
+EDGE_LENGTHS = [201, 202, 399, 400, 401, 1000, 5119, 5121, 16001]
+
+
+@pytest.mark.parametrize("L", EDGE_LENGTHS)
+def test_short_and_ragged_lengths(L):
+    """Lengths just above n_fft/2, not multiples of hop, one tile straddling
+    both signal edges, odd lengths (unpaired-load path)."""
+    x = np.random.default_rng(L).standard_normal((2, L)).astype(np.float32) * 0.3
+    targs = dict(sample_rate=16000, n_fft=400, hop_length=160, n_mels=80, f_max=8000.0)
+    assert_parity(run_gpu(x, **targs), oracle(x, **targs), f"L={L}")
+
+
+@pytest.mark.parametrize("n_fft,hop", [(1024, 256), (2048, 512), (1024, 100)])
+def test_ragged_large_fft(n_fft, hop):
+    x = np.random.default_rng(n_fft).standard_normal((2, 9001)).astype(np.float32)
+    targs = dict(sample_rate=22050, n_fft=n_fft, hop_length=hop, n_mels=96)
+    assert_parity(run_gpu(x, **targs), oracle(x, **targs), f"{n_fft}/{hop}")
+
+
+@pytest.mark.parametrize("pad_mode", ["constant", "replicate", "circular"])
+def test_other_pad_modes(pad_mode):
+    x = np.random.default_rng(3).standard_normal((2, 5000)).astype(np.float32)
+    targs = dict(sample_rate=16000, n_fft=400, hop_length=160, n_mels=64, pad_mode=pad_mode)
+    assert_parity(run_gpu(x, **targs), oracle(x, **targs), pad_mode)
+
+
+def test_center_false_and_general_power_and_slaney():
+    x = np.random.default_rng(4).standard_normal((3, 7000)).astype(np.float32)
+    for targs in (dict(n_fft=400, hop_length=100, n_mels=64, center=False),
+                  dict(n_fft=1024, hop_length=256, n_mels=80, power=1.5),
+                  dict(n_fft=400, hop_length=160, n_mels=40, mel_scale="slaney", norm="slaney"),
+                  dict(n_fft=400, hop_length=160, n_mels=60, f_min=125.0, f_max=7000.0),
+                  dict(n_fft=400, win_length=320, hop_length=160, n_mels=60)):
+        assert_parity(run_gpu(x, sample_rate=16000, **targs), oracle(x, sample_rate=16000, **targs),
+                      str(targs))
+
+
+def test_int16_odd_length_and_misaligned_input():
+    from stft_mel_spectrogram_amd import MelSpectrogram
+    _require_gpu()
+    q = np.random.default_rng(5).integers(-32768, 32768, size=(2, 6001)).astype(np.int16)
+    targs = dict(sample_rate=16000, n_fft=400, hop_length=160, n_mels=80)
+    assert_parity(run_gpu(q, **targs), oracle(q, **targs), "i16 odd length")
+    # input that starts one sample into an allocation: no paired loads allowed
+    x = np.random.default_rng(6).standard_normal((2, 6001)).astype(np.float32)
+    base = torch.empty(2 * 6000 + 1, device="cuda")
+    base[1:] = torch.from_numpy(x[:, :6000].reshape(-1)).to("cuda")
+    shifted = base[1:].view(2, 6000)          # data_ptr is 4 bytes past a 256-B boundary
+    assert shifted.data_ptr() % 8 == 4
+    y = MelSpectrogram(**targs)(shifted)
+    torch.cuda.synchronize()
+    assert_parity(y.cpu().numpy(), oracle(x[:, :6000], **targs), "misaligned f32")
+
+
+def test_every_output_written_and_deterministic():
+    from stft_mel_spectrogram_amd import MelSpectrogram
+    _require_gpu()
+    cfg = W.workload("whisper", batch=2, length=30_000)
+    x = torch.from_numpy(W.make_signal(cfg)).cuda()
+    mel = MelSpectrogram(**W.transform_args(cfg))
+    T = mel.out_frames(30_000)
+    out1 = torch.full((2, 128, T), float("nan"), device="cuda")
+    out2 = torch.full((2, 128, T), float("nan"), device="cuda")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        mel(x, out=out1)
+        mel(x, out=out2)
+    torch.cuda.synchronize()
+    assert not torch.isnan(out1).any()
+    assert torch.equal(out1, out2)
+    # empty filters (no bin inside) are exactly zero
+    for m in (0, 3, 6, 13):
+        assert torch.all(out1[:, m] == 0)
+
+
+def test_leading_dims_and_empty_batch():
+    from stft_mel_spectrogram_amd import MelSpectrogram
+    _require_gpu()
+    mel = MelSpectrogram(sample_rate=16000, n_fft=400, hop_length=160, n_mels=40)
+    x = np.random.default_rng(7).standard_normal((2, 3, 4000)).astype(np.float32)
+    y = mel(torch.from_numpy(x).cuda())
+    torch.cuda.synchronize()
+    assert tuple(y.shape) == (2, 3, 40, 26)
+    assert_parity(y.cpu().numpy(), oracle(x, sample_rate=16000, n_fft=400, hop_length=160, n_mels=40),
+                  "leading dims")
+    z = mel(torch.empty((0, 4000), device="cuda"))
+    assert tuple(z.shape) == (0, 40, 26)
+
+
+def test_rejects_bad_inputs():
+    from stft_mel_spectrogram_amd import MelSpectrogram
+    _require_gpu()
+    mel = MelSpectrogram(n_fft=400, hop_length=160, n_mels=40)
+    with pytest.raises(ValueError):
+        mel(torch.zeros(4000))                                  # host tensor
+    with pytest.raises(TypeError):
+        mel(torch.zeros(4000, dtype=torch.float64, device="cuda"))
+    with pytest.raises(RuntimeError):
+        mel(torch.zeros(4000, device="cuda", requires_grad=True))
+    with pytest.raises(ValueError):
+        mel(torch.zeros(2, 4000, device="cuda").t())             # non-contiguous
+    from stft_mel_spectrogram_amd._native import FmError
+    with pytest.raises(FmError):
+        mel(torch.zeros(150, device="cuda"))                     # reflect needs L > 200

@@ -1,0 +1,179 @@
+"""CPU tests of the C ABI: exported symbols, host-plan tables against the
+oracle's own constructions, argument validation and error codes.  No GPU
+work is launched (host-only plans)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import mel_oracle as O
+from stft_mel_spectrogram_amd import _native as N
+from stft_mel_spectrogram_amd import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "fm.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fm_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = header_functions()
+    assert {"fm_plan_create", "fm_forward", "fm_plan_destroy", "fm_out_frames",
+            "fm_strerror", "fm_last_error", "fm_plan_tables"} <= set(names)
+    lib = ctypes.CDLL(N.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in fm.h but not exported"
+
+
+def test_product_path_never_touches_the_oracle():
+    pkg = os.path.join(ROOT, "stft_mel_spectrogram_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".cpp", ".hip", ".h")):
+                src = open(os.path.join(dirpath, f), errors="ignore").read()
+                assert not re.search(r"^\s*(from|import)\s+oracle", src, re.M), f
+                assert "mel_oracle" not in src, f
+
+
+def host_plan(cfg, **kw):
+    args = dict(W.transform_args(cfg))
+    args.update(kw)
+    return N.Plan(device=False, **args)
+
+
+@pytest.mark.parametrize("name", ["tiny", "whisper", "pow2", "large"])
+def test_window_matches_oracle(name):
+    cfg = W.WORKLOADS[name]
+    t = host_plan(cfg).tables()
+    ref = O.make_window(cfg["n_fft"], cfg["win_length"], False)
+    np.testing.assert_allclose(t["window"], ref, rtol=1.2e-7, atol=1e-30)
+
+
+def test_window_shorter_than_nfft_is_centred():
+    p = N.Plan(device=False, sample_rate=16000, n_fft=400, win_length=300, hop_length=100, n_mels=40)
+    np.testing.assert_allclose(p.tables()["window"], O.make_window(400, 300, False), rtol=1.2e-7, atol=1e-30)
+
+
+@pytest.mark.parametrize("name", ["tiny", "whisper", "pow2", "large"])
+@pytest.mark.parametrize("scale,norm", [("htk", None), ("slaney", "slaney"), ("htk", "slaney")])
+def test_csr_filterbank_matches_oracle(name, scale, norm):
+    cfg = W.WORKLOADS[name]
+    p = host_plan(cfg, mel_scale=scale, norm=norm)
+    t = p.tables()
+    fb = O.mel_filterbank(cfg["n_fft"] // 2 + 1, cfg["f_min"], cfg["f_max"], cfg["n_mels"],
+                          cfg["sample_rate"], norm, scale)
+    dense = np.zeros_like(fb)
+    for m in range(cfg["n_mels"]):
+        a, ln, off = t["first"][m], t["len"][m], t["off"][m]
+        dense[a:a + ln, m] = t["weights"][off:off + ln]
+        support = np.nonzero(fb[:, m] > 0)[0]
+        if ln == 0:
+            assert len(support) == 0 or fb[support, m].max() < 1e-12
+        else:
+            assert t["weights"][off] > 0 and t["weights"][off + ln - 1] > 0
+    np.testing.assert_allclose(dense, fb, rtol=1.2e-7, atol=1e-12)
+    assert p.info().nnz == int(np.sum(t["len"]))
+
+
+def test_csr_statistics_of_the_workloads():
+    # nonzeros / widest filter / empty filters of the four distinct filterbanks
+    expect = {"tiny": (393, 14, []), "whisper": (395, 9, [0, 3, 6, 13]),
+              "pow2": (1005, 34, []), "large": (2022, 46, [])}
+    for name, (nnz, wmax, empty) in expect.items():
+        p = host_plan(W.WORKLOADS[name])
+        inf = p.info()
+        t = p.tables()
+        assert (inf.nnz, inf.w_max) == (nnz, wmax), name
+        assert [m for m in range(inf.n_mels) if t["len"][m] == 0] == empty, name
+
+
+@pytest.mark.parametrize("n_fft", [400, 1024, 2048])
+def test_twiddles(n_fft):
+    p = N.Plan(device=False, sample_rate=16000, n_fft=n_fft, hop_length=n_fft // 4, n_mels=40)
+    t = p.tables()
+    M = n_fft // 2
+    j = np.arange(M)
+    np.testing.assert_allclose(t["tw_m"], np.exp(-2j * np.pi * j / M), rtol=0, atol=6e-8)
+    np.testing.assert_allclose(t["tw_n"], np.exp(-2j * np.pi * j / n_fft), rtol=0, atol=6e-8)
+    inf = p.info()
+    assert inf.fft_n1 * inf.fft_n2 == M
+
+
+@pytest.mark.parametrize("L", [201, 202, 1000, 16000, 480000, 220500])
+def test_out_frames_closed_form(L):
+    for n_fft, hop in ((400, 160), (1024, 256), (2048, 512)):
+        if L <= n_fft // 2:
+            continue
+        p = N.Plan(device=False, n_fft=n_fft, hop_length=hop, n_mels=40)
+        assert p.out_frames(L) == O.frame_count(L, n_fft, hop, center=True)
+        if L >= n_fft:
+            q = N.Plan(device=False, n_fft=n_fft, hop_length=hop, n_mels=40, center=False)
+            assert q.out_frames(L) == O.frame_count(L, n_fft, hop, center=False)
+
+
+def test_geometry_fits_the_hardware():
+    for name in ("tiny", "whisper", "pow2", "large"):
+        inf = host_plan(W.WORKLOADS[name]).info()
+        assert inf.lds_bytes <= 160 * 1024
+        assert inf.tile_frames * inf.fft_n1 // 2 <= inf.threads
+        assert inf.has_device == 0
+
+
+BAD = [
+    (dict(n_fft=512), N.FM_E_UNSUPPORTED),
+    (dict(n_mels=257), N.FM_E_UNSUPPORTED),
+    (dict(f_min=8000.0, f_max=8000.0), N.FM_E_INVAL),
+    (dict(f_max=8001.0), N.FM_E_INVAL),
+    (dict(f_min=-1.0), N.FM_E_INVAL),
+    (dict(hop_length=0), N.FM_E_INVAL),
+    (dict(win_length=401), N.FM_E_INVAL),
+    (dict(power=0.0), N.FM_E_INVAL),
+    (dict(sample_rate=0), N.FM_E_INVAL),
+    (dict(n_mels=0), N.FM_E_INVAL),
+]
+
+
+@pytest.mark.parametrize("kw,code", BAD)
+def test_invalid_arguments(kw, code):
+    args = dict(sample_rate=16000, n_fft=400, hop_length=160, n_mels=80, f_max=8000.0)
+    args.update(kw)
+    with pytest.raises(N.FmError) as e:
+        N.Plan(device=False, **args)
+    assert e.value.status == code
+
+
+def test_raw_enum_validation_and_null_handling():
+    lib = N.lib
+    h = ctypes.c_void_p()
+    base = [16000, 400, 400, 160, 80, 0.0, 8000.0, 2.0]
+    assert lib.fm_plan_create_host(ctypes.byref(h), *base, 1, 9, 0, 0) == N.FM_E_INVAL   # pad_mode
+    assert lib.fm_plan_create_host(ctypes.byref(h), *base, 1, 0, 5, 0) == N.FM_E_INVAL   # mel_scale
+    assert lib.fm_plan_create_host(ctypes.byref(h), *base, 1, 0, 0, 7) == N.FM_E_INVAL   # norm
+    assert lib.fm_plan_create_host(ctypes.byref(h), *base, 2, 0, 0, 0) == N.FM_E_INVAL   # center
+    assert lib.fm_plan_create_host(None, *base, 1, 0, 0, 0) == N.FM_E_INVAL
+    assert lib.fm_plan_destroy(None) == N.FM_OK
+    assert lib.fm_forward(None, None, 0, 1, 1000, None, None) == N.FM_E_INVAL
+    assert lib.fm_out_frames(None, 100) == N.FM_E_INVAL
+    assert b"NULL" in lib.fm_last_error()
+    assert lib.fm_strerror(N.FM_E_UNSUPPORTED) == b"unsupported configuration"
+
+
+def test_forward_on_host_plan_and_bad_lengths():
+    p = N.Plan(device=False, n_fft=400, hop_length=160, n_mels=80)
+    with pytest.raises(N.FmError) as e:
+        p.forward_ptr(0, N.FM_F32, 1, 1000, 0)
+    assert e.value.status == N.FM_E_NODEVICE
+    with pytest.raises(N.FmError) as e:
+        p.out_frames(200)          # reflect needs length > n_fft/2
+    assert e.value.status == N.FM_E_INVAL
+    assert p.out_frames(201) == 2
+    q = N.Plan(device=False, n_fft=400, hop_length=160, n_mels=80, pad_mode="constant")
+    assert q.out_frames(1) == 1     # zero padding has no length bound beyond one sample
+    r = N.Plan(device=False, n_fft=400, hop_length=160, n_mels=80, center=False)
+    with pytest.raises(N.FmError):
+        r.out_frames(399)
