@@ -107,7 +107,7 @@ int fm_plan_info_get(const fm_plan* plan, fm_plan_info* info) {
   info->w_max = p.w_max;
   info->fft_n1 = p.fft.n1;
   info->fft_n2 = p.fft.n2;
-  info->tile_frames = p.tile_frames;
+  info->tile_frames = p.tile_max;
   info->threads = p.threads;
   info->lds_bytes = p.lds_bytes;
   info->has_device = p.has_device ? 1 : 0;

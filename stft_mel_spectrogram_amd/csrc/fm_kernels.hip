@@ -19,6 +19,7 @@
 // buffer.  The mel projection walks each filter's CSR run only.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 
 #include "fm_dft.h"
@@ -34,22 +35,25 @@ struct KArgs {
   const float2* win2;   // [M]  0.5*(w[2m], w[2m+1])
   const float2* tw_m;   // [M]  exp(-2 pi i j / M)
   const float2* tw_n;   // [M]  exp(-2 pi i k / N)
-  const MelRow* rows;   // [n_mels]
-  const float* mel_w;   // [nnz]
   long long length;     // samples per signal
   int n_frames;         // frames per signal
   int hop;
   int pad;              // left padding (n_fft/2 with centring, else 0)
   int n_mels;
-  int nnz;
-  int tile;             // frames per workgroup
+  int tile;             // frames per workgroup tile (<= 64)
   int tiles_per_signal;
   int pad_mode;
-  int power_mode;       // 0: |X|^2, 1: |X|, 2: |X|^power
   float half_power;     // power / 2
   int vec_ok;           // interior tiles may use paired (2-sample) loads
-  int lds_y_bytes;
+  const SweepStep* steps;  // mel sweep steps of all waves
+  const int* empty_mels;   // filters with no bin
+  WaveSweep sweep[4];      // each wave's share of the mel stage
 };
+
+// Tables read with wave-uniform indices are reached through the constant
+// address space so they load as scalars (SGPR operands of the FMAs).
+using CStep = const __attribute__((address_space(4))) SweepStep;
+using CInt = const __attribute__((address_space(4))) int;
 
 template <typename T>
 __device__ __forceinline__ float sample_to_float(T v);
@@ -60,186 +64,311 @@ __device__ __forceinline__ float sample_to_float<int16_t>(int16_t v) {
   return static_cast<float>(v) * (1.0f / 32768.0f);  // exact
 }
 
-// Value of the padded signal at position i (i relative to sample 0).
-template <typename T>
-__device__ __forceinline__ float padded_sample(const T* x, long long i, long long L, int mode) {
-  if (i < 0 || i >= L) {
-    switch (mode) {
-      case FM_PAD_CONSTANT:
-        return 0.0f;
-      case FM_PAD_REPLICATE:
-        i = i < 0 ? 0 : L - 1;
-        break;
-      case FM_PAD_CIRCULAR:
-        i %= L;
-        if (i < 0) i += L;
-        break;
-      default:  // reflect, single reflection (pad < L checked on the host)
-        i = i < 0 ? -i : 2 * (L - 1) - i;
-        break;
-    }
+// Source index of position i of the padded signal (i relative to sample 0),
+// or -1 for a constant-zero position.  The host guarantees that frames
+// reach at most one signal length beyond either end, so one reflection or
+// wrap suffices; all indices fit in 32 bits.
+__device__ __forceinline__ int padded_index(int i, int L, int mode) {
+  if (static_cast<unsigned>(i) < static_cast<unsigned>(L)) return i;
+  switch (mode) {
+    case FM_PAD_CONSTANT: return -1;
+    case FM_PAD_REPLICATE: return i < 0 ? 0 : L - 1;
+    case FM_PAD_CIRCULAR: return i < 0 ? i + L : i - L;
+    default: return i < 0 ? -i : 2 * (L - 1) - i;  // reflect
   }
-  return sample_to_float<T>(x[i]);
 }
 
 // Two consecutive samples starting at an even position of an interior frame.
-__device__ __forceinline__ float2 load_pair(const float* x, long long i) {
+__device__ __forceinline__ float2 load_pair(const float* x, int i) {
   return *reinterpret_cast<const float2*>(x + i);
 }
-__device__ __forceinline__ float2 load_pair(const int16_t* x, long long i) {
+// int16 pairs come back unscaled: the 2^-15 PCM scale is folded into the
+// (register-held) window, which keeps the product exact.
+__device__ __forceinline__ float2 load_pair_raw(const float* x, int i) { return load_pair(x, i); }
+__device__ __forceinline__ float2 load_pair_raw(const int16_t* x, int i) {
   const short2 v = *reinterpret_cast<const short2*>(x + i);
-  return make_float2(static_cast<float>(v.x) * (1.0f / 32768.0f),
-                     static_cast<float>(v.y) * (1.0f / 32768.0f));
+  return make_float2(static_cast<float>(v.x), static_cast<float>(v.y));
 }
+template <typename T>
+__device__ __forceinline__ float padded_sample_raw(const T* x, int i, int L, int mode) {
+  const int j = padded_index(i, L, mode);
+  if constexpr (std::is_same<T, int16_t>::value) return j < 0 ? 0.0f : static_cast<float>(x[j]);
+  else return j < 0 ? 0.0f : x[j];
+}
+template <typename T>
+constexpr float kSampleScale = std::is_same<T, int16_t>::value ? (1.0f / 32768.0f) : 1.0f;
 
-__device__ __forceinline__ float power_of(float sq, int mode, float half_power) {
-  if (mode == 0) return sq;
-  if (mode == 1) return sqrtf(sq);
-  return powf(sq, half_power);
+// |X|^p from |X|^2: PMODE 0 -> p = 2, 1 -> p = 1, 2 -> any p > 0 (hp = p/2).
+template <int PMODE>
+__device__ __forceinline__ float power_of(float sq, float hp) {
+  if constexpr (PMODE == 0) {
+    return sq;
+  } else if constexpr (PMODE == 1) {
+    return __builtin_amdgcn_sqrtf(sq);  // v_sqrt_f32, within 1 ulp
+  } else {
+    // |X|^p = 2^(p/2 * log2 |X|^2) with v_log_f32 / v_exp_f32 (1 ulp each)
+    return sq > 0.0f ? __builtin_amdgcn_exp2f(hp * __builtin_amdgcn_logf(sq)) : 0.0f;
+  }
 }
 
 // Real-spectrum split for the bin pair (k, M-k) and their powers.
+template <int PMODE>
 __device__ __forceinline__ void split_pair(float* prow, int k, int kmirror, float2 zk, float2 zm,
-                                           float2 w, int mode, float hp) {
+                                           float2 w, float hp) {
   const float2 e = make_float2(zk.x + zm.x, zk.y - zm.y);  // Z[k] + conj Z[M-k]
   const float2 o = make_float2(zk.x - zm.x, zk.y + zm.y);  // Z[k] - conj Z[M-k]
   const float2 v = cmul(w, o);
   const float ax = e.x + v.y, ay = e.y - v.x;  // X[k]   = e - i v
   const float bx = e.x - v.y, by = e.y + v.x;  // X[M-k] = conj(e + i v)
-  prow[k] = power_of(fmaf(ax, ax, ay * ay), mode, hp);
-  prow[kmirror] = power_of(fmaf(bx, bx, by * by), mode, hp);
+  prow[k] = power_of<PMODE>(fmaf(ax, ax, ay * ay), hp);
+  prow[kmirror] = power_of<PMODE>(fmaf(bx, bx, by * by), hp);
+}
+
+template <int N1, int N2, typename InT, int PMODE>
+__global__ __launch_bounds__(256) void mel_forward_kernel(KArgs a) {
+  constexpr int M = N1 * N2;
+  constexpr int K = M + 1;        // one-sided bins; odd, so P rows are bank-skewed
+  constexpr int NF = 2 * M;       // n_fft
+  constexpr int NPAIR = N1 / 2;   // pass-2 threads per frame
+  constexpr int SLOTS = 256 / N2; // frames per pass-1 round (one thread per n2)
+  constexpr bool kHoist = N1 <= 8;   // window and twiddles in registers,
+                                     // next frame's samples prefetched
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  float2* Y = reinterpret_cast<float2*>(lds);  // Y[f][k1][n2]
+  float* P = reinterpret_cast<float*>(lds);    // P[f][k], aliases Y
+
+  const int tid = threadIdx.x;
+  const int G = a.tile;
+  const int L = static_cast<int>(a.length);
+
+  // pass-1 role of this thread: fixed n2, frames slot, slot+SLOTS, ...
+  const int n2 = tid % N2;
+  const int slot = tid / N2;
+  // pass-2 role: frame f2, pair p of first-pass outputs
+  const int f2 = tid / NPAIR;
+  const int p = tid - f2 * NPAIR;
+  // mel role: wave -> contiguous range of mel rows, lane -> frame
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+
+  // One tile per workgroup.  (Looping over tiles would let the compiler hoist
+  // the per-thread table loads out of the loop and keep them live across
+  // every pass, which costs more registers than it saves.)
+  {
+    const int tile = blockIdx.x;
+    const int b = tile / a.tiles_per_signal;
+    const int t0 = (tile - b * a.tiles_per_signal) * G;
+    const int nvalid = min(G, a.n_frames - t0);
+    const InT* x = static_cast<const InT*>(a.in) + static_cast<long long>(b) * L;
+
+    // ---- pass 1: window + N1-point DFTs, twiddle, exchange through LDS ----
+    if (slot < SLOTS) {
+      float2 win[kHoist ? N1 : 1], twv[kHoist ? N1 : 1];
+      if constexpr (kHoist) {
+#pragma unroll
+        for (int n1 = 0; n1 < N1; ++n1) win[n1] = a.win2[N2 * n1 + n2];
+        if constexpr (!std::is_same<InT, float>::value) {
+#pragma unroll
+          for (int n1 = 0; n1 < N1; ++n1)
+            win[n1] = make_float2(win[n1].x * kSampleScale<InT>, win[n1].y * kSampleScale<InT>);
+        }
+        twv[0] = make_float2(1.0f, 0.0f);
+#pragma unroll
+        for (int k1 = 1; k1 < N1; ++k1) twv[k1] = a.tw_m[n2 * k1];
+      }
+      auto fetch = [&](int f, float2 (&s)[N1]) {
+        const int base = (t0 + f) * a.hop - a.pad;
+        if (a.vec_ok && base >= 0 && base + NF <= L) {  // interior frame
+#pragma unroll
+          for (int n1 = 0; n1 < N1; ++n1) s[n1] = load_pair_raw(x, base + 2 * (N2 * n1 + n2));
+        } else {
+#pragma unroll
+          for (int n1 = 0; n1 < N1; ++n1) {
+            const int i = base + 2 * (N2 * n1 + n2);
+            s[n1] = make_float2(padded_sample_raw(x, i, L, a.pad_mode),
+                                padded_sample_raw(x, i + 1, L, a.pad_mode));
+          }
+        }
+      };
+      auto compute = [&](int f, const float2 (&s)[N1]) {
+        float2 v[N1];
+#pragma unroll
+        for (int n1 = 0; n1 < N1; ++n1) {
+          float2 w;
+          if constexpr (kHoist) {
+            w = win[kHoist ? n1 : 0];  // already scaled for int16
+          } else {
+            w = a.win2[N2 * n1 + n2];
+            w = make_float2(w.x * kSampleScale<InT>, w.y * kSampleScale<InT>);
+          }
+          v[n1] = make_float2(s[n1].x * w.x, s[n1].y * w.y);
+        }
+        Dft<N1>::run(v);
+        float2* yrow = Y + f * M + n2;
+        yrow[0] = v[0];
+#pragma unroll
+        for (int k1 = 1; k1 < N1; ++k1)
+          yrow[k1 * N2] = cmul(v[k1], kHoist ? twv[kHoist ? k1 : 0] : a.tw_m[n2 * k1]);
+      };
+      if constexpr (kHoist) {
+        // every frame of this thread is fetched before any is computed, so
+        // the whole tile's loads are in flight at once
+        constexpr int RMAX = (64 + SLOTS - 1) / SLOTS;
+        float2 sb[RMAX][N1];
+#pragma unroll
+        for (int r = 0; r < RMAX; ++r)
+          if (slot + SLOTS * r < nvalid) fetch(slot + SLOTS * r, sb[r]);
+#pragma unroll
+        for (int r = 0; r < RMAX; ++r)
+          if (slot + SLOTS * r < nvalid) compute(slot + SLOTS * r, sb[r]);
+      } else {
+        for (int f = slot; f < nvalid; f += SLOTS) {
+          float2 s0[N1];
+          fetch(f, s0);
+          compute(f, s0);
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- pass 2: paired N2-point DFTs, real split, power -> P (aliases Y) --
+    const bool has = f2 < nvalid;
+    constexpr bool kTwPrefetch = M <= 256;  // registers allow it for small FFTs
+    float2 za[N2], zb[N2], wv[kTwPrefetch ? N2 + 1 : 1];
+    auto tw_at = [&](int idx, int k) -> float2 {
+      return kTwPrefetch ? wv[kTwPrefetch ? idx : 0] : a.tw_n[k];
+    };
+    if (has) {
+      if constexpr (kTwPrefetch) {  // split twiddles load under the DFTs
+        if (p != 0) {
+#pragma unroll
+          for (int k2 = 0; k2 < N2; ++k2) wv[k2] = a.tw_n[p + N1 * k2];
+        } else {
+#pragma unroll
+          for (int k2 = 0; k2 <= N2 / 2; ++k2) wv[k2] = a.tw_n[N1 * k2];
+#pragma unroll
+          for (int k2 = 0; k2 <= (N2 - 1) / 2; ++k2) wv[N2 / 2 + 1 + k2] = a.tw_n[N1 / 2 + N1 * k2];
+        }
+      }
+      const int ka = p;
+      const int kb = (p == 0) ? N1 / 2 : N1 - p;
+      const float2* ra = Y + f2 * M + ka * N2;
+      const float2* rb = Y + f2 * M + kb * N2;
+#pragma unroll
+      for (int j = 0; j < N2; ++j) {
+        za[j] = ra[j];
+        zb[j] = rb[j];
+      }
+      Dft<N2>::run(za);
+      Dft<N2>::run(zb);
+    }
+    __syncthreads();
+    if (has) {
+      float* prow = P + f2 * K;
+      const float hp = a.half_power;
+      if (p != 0) {
+        // bins k = p + N1*k2 (za) and M - k = (N1 - p) + N1*(N2-1-k2) (zb)
+#pragma unroll
+        for (int k2 = 0; k2 < N2; ++k2) {
+          const int k = p + N1 * k2;
+          split_pair<PMODE>(prow, k, M - k, za[k2], zb[N2 - 1 - k2], tw_at(k2, k), hp);
+        }
+      } else {
+        // k1 = 0: bins N1*k2 pair with N1*(N2-k2) inside za
+#pragma unroll
+        for (int k2 = 0; k2 <= N2 / 2; ++k2) {
+          const int k = N1 * k2;
+          split_pair<PMODE>(prow, k, M - k, za[k2], za[(N2 - k2) % N2], tw_at(k2, k), hp);
+        }
+        // k1 = N1/2: bins N1/2 + N1*k2 pair with N1/2 + N1*(N2-1-k2) inside zb
+#pragma unroll
+        for (int k2 = 0; k2 <= (N2 - 1) / 2; ++k2) {
+          const int k = N1 / 2 + N1 * k2;
+          split_pair<PMODE>(prow, k, M - k, zb[k2], zb[N2 - 1 - k2], tw_at(N2 / 2 + 1 + k2, k), hp);
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- mel projection: lane = frame; each wave sweeps the bins of its
+    //      filters once, with at most two filters open at a time ------------
+    {
+      const WaveSweep ws = a.sweep[wave];
+      const float* pp = P + min(lane, G - 1) * K + ws.k0;
+      float* obase = a.out + static_cast<long long>(b) * a.n_mels * a.n_frames + t0 + lane;
+      const bool store = lane < nvalid;
+      CInt* empt = (CInt*)(a.empty_mels) + ws.empty_off;  // address-space cast
+      for (int i = 0; i < ws.n_empty; ++i)
+        if (store) obase[static_cast<long long>(empt[i]) * a.n_frames] = 0.0f;
+      CStep* st = (CStep*)(a.steps) + ws.step_off;  // address-space cast
+      float acc_a = 0.0f, acc_b = 0.0f;
+      // steps come in chunks of 8: the next chunk's scalars load while this
+      // one's power values and FMAs are in flight
+      float cwa[8], cwb[8];
+      int ccode[8];
+      auto load_chunk = [&](int s0, float (&wa)[8], float (&wb)[8], int (&code)[8]) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          wa[u] = st[s0 + u].wa;
+          wb[u] = st[s0 + u].wb;
+          code[u] = st[s0 + u].code;
+        }
+      };
+      if (ws.nsteps > 0) load_chunk(0, cwa, cwb, ccode);
+      for (int s0 = 0; s0 < ws.nsteps; s0 += 8, pp += 8) {
+        float pv[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) pv[u] = pp[u];
+        float nwa[8], nwb[8];
+        int ncode[8];
+        if (s0 + 8 < ws.nsteps) load_chunk(s0 + 8, nwa, nwb, ncode);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int code = ccode[u];
+          acc_a = fmaf(cwa[u], pv[u], acc_a);
+          acc_b = fmaf(cwb[u], pv[u], acc_b);
+          if (code & 3) {
+            if (store) obase[static_cast<long long>((code >> 8) & 0xff) * a.n_frames] = acc_a;
+            if ((code & 3) == 2) {
+              if (store) obase[static_cast<long long>((code >> 16) & 0xff) * a.n_frames] = acc_b;
+              acc_a = 0.0f;
+            } else {
+              acc_a = acc_b;
+            }
+            acc_b = 0.0f;
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          cwa[u] = nwa[u];
+          cwb[u] = nwb[u];
+          ccode[u] = ncode[u];
+        }
+      }
+    }
+  }
 }
 
 template <int N1, int N2, typename InT>
-__global__ __launch_bounds__(256) void mel_forward_kernel(KArgs a) {
-  constexpr int M = N1 * N2;
-  constexpr int K = M + 1;       // one-sided bins; odd, so P rows are bank-skewed
-  constexpr int NF = 2 * M;      // n_fft
-  constexpr int NPAIR = N1 / 2;  // pass-2 threads per frame
-  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
-  float2* Y = reinterpret_cast<float2*>(lds);
-  float* P = reinterpret_cast<float*>(lds);
-  float* Wm = reinterpret_cast<float*>(lds + a.lds_y_bytes);
-  MelRow* rows = reinterpret_cast<MelRow*>(Wm + ((a.nnz + 3) & ~3));
-
-  const int tid = threadIdx.x;
-  const int b = blockIdx.x / a.tiles_per_signal;
-  const int t0 = (blockIdx.x - b * a.tiles_per_signal) * a.tile;
-  const int nvalid = min(a.tile, a.n_frames - t0);
-  const long long L = a.length;
-  const InT* x = static_cast<const InT*>(a.in) + static_cast<long long>(b) * L;
-
-  for (int i = tid; i < a.nnz; i += blockDim.x) Wm[i] = a.mel_w[i];
-  for (int i = tid; i < a.n_mels; i += blockDim.x) rows[i] = a.rows[i];
-
-  const long long s_first = static_cast<long long>(t0) * a.hop - a.pad;
-  const long long s_last = static_cast<long long>(t0 + nvalid - 1) * a.hop - a.pad + NF - 1;
-  const bool interior = a.vec_ok && s_first >= 0 && s_last < L;
-
-  // ---- pass 1: window + N1-point DFTs, twiddle, exchange through LDS ------
-  for (int job = tid; job < a.tile * N2; job += blockDim.x) {
-    const int f = job / N2;
-    const int n2 = job - f * N2;
-    if (f >= nvalid) break;
-    const long long base = static_cast<long long>(t0 + f) * a.hop - a.pad;
-    float2 v[N1];
-    if (interior) {
-#pragma unroll
-      for (int n1 = 0; n1 < N1; ++n1) {
-        const int m = N2 * n1 + n2;
-        const float2 s = load_pair(x, base + 2 * m);
-        const float2 w = a.win2[m];
-        v[n1] = make_float2(s.x * w.x, s.y * w.y);
-      }
-    } else {
-#pragma unroll
-      for (int n1 = 0; n1 < N1; ++n1) {
-        const int m = N2 * n1 + n2;
-        const float2 w = a.win2[m];
-        v[n1] = make_float2(padded_sample(x, base + 2 * m, L, a.pad_mode) * w.x,
-                            padded_sample(x, base + 2 * m + 1, L, a.pad_mode) * w.y);
-      }
-    }
-    Dft<N1>::run(v);
-    float2* yrow = Y + (f * N1) * N2 + n2;
-    yrow[0] = v[0];
-#pragma unroll
-    for (int k1 = 1; k1 < N1; ++k1) yrow[k1 * N2] = cmul(v[k1], a.tw_m[n2 * k1]);
-  }
-  __syncthreads();
-
-  // ---- pass 2: paired N2-point DFTs, real split, power -> P (aliases Y) ----
-  const int f2 = tid / NPAIR;
-  const int p = tid - f2 * NPAIR;
-  const bool has = tid < a.tile * NPAIR && f2 < nvalid;
-  float2 za[N2], zb[N2];
-  if (has) {
-    const int ka = p;
-    const int kb = (p == 0) ? N1 / 2 : N1 - p;
-    const float2* ra = Y + (f2 * N1 + ka) * N2;
-    const float2* rb = Y + (f2 * N1 + kb) * N2;
-#pragma unroll
-    for (int n2 = 0; n2 < N2; ++n2) {
-      za[n2] = ra[n2];
-      zb[n2] = rb[n2];
-    }
-    Dft<N2>::run(za);
-    Dft<N2>::run(zb);
-  }
-  __syncthreads();
-  if (has) {
-    float* prow = P + f2 * K;
-    const int mode = a.power_mode;
-    const float hp = a.half_power;
-    if (p != 0) {
-      // bins k = p + N1*k2 (from za) and M - k = (N1 - p) + N1*(N2-1-k2) (from zb)
-#pragma unroll
-      for (int k2 = 0; k2 < N2; ++k2) {
-        const int k = p + N1 * k2;
-        split_pair(prow, k, M - k, za[k2], zb[N2 - 1 - k2], a.tw_n[k], mode, hp);
-      }
-    } else {
-      // k1 = 0: bins N1*k2 pair with N1*(N2-k2) inside za
-#pragma unroll
-      for (int k2 = 0; k2 <= N2 / 2; ++k2) {
-        const int k = N1 * k2;
-        split_pair(prow, k, M - k, za[k2], za[(N2 - k2) % N2], a.tw_n[k], mode, hp);
-      }
-      // k1 = N1/2: bins N1/2 + N1*k2 pair with N1/2 + N1*(N2-1-k2) inside zb
-#pragma unroll
-      for (int k2 = 0; k2 <= (N2 - 1) / 2; ++k2) {
-        const int k = N1 / 2 + N1 * k2;
-        split_pair(prow, k, M - k, zb[k2], zb[N2 - 1 - k2], a.tw_n[k], mode, hp);
-      }
-    }
-  }
-  __syncthreads();
-
-  // ---- mel projection over each filter's CSR run, frames-contiguous store ---
-  const int G = a.tile;
-  for (int job = tid; job < a.n_mels * G; job += blockDim.x) {
-    const int m = job / G;
-    const int f = job - m * G;
-    if (f >= nvalid) continue;
-    const MelRow r = rows[m];
-    const float* pr = P + f * K + r.first;
-    const float* wr = Wm + r.off;
-    float acc = 0.0f;
-    for (int j = 0; j < r.len; ++j) acc = fmaf(wr[j], pr[j], acc);
-    a.out[(static_cast<long long>(b) * a.n_mels + m) * a.n_frames + t0 + f] = acc;
-  }
+void* kernel_for_power(int pmode) {
+  if (pmode == 0) return reinterpret_cast<void*>(&mel_forward_kernel<N1, N2, InT, 0>);
+  if (pmode == 1) return reinterpret_cast<void*>(&mel_forward_kernel<N1, N2, InT, 1>);
+  return reinterpret_cast<void*>(&mel_forward_kernel<N1, N2, InT, 2>);
 }
 
 template <int N1, int N2>
-void* kernel_for(int in_dtype) {
-  if (in_dtype == FM_I16) return reinterpret_cast<void*>(&mel_forward_kernel<N1, N2, int16_t>);
-  return reinterpret_cast<void*>(&mel_forward_kernel<N1, N2, float>);
+void* kernel_for(int in_dtype, int pmode) {
+  if (in_dtype == FM_I16) return kernel_for_power<N1, N2, int16_t>(pmode);
+  return kernel_for_power<N1, N2, float>(pmode);
 }
 
+int power_mode(const Plan& p) { return p.power == 2.0 ? 0 : (p.power == 1.0 ? 1 : 2); }
+
 void* select_kernel(const Plan& p, int in_dtype) {
-  if (p.fft.n1 == 8 && p.fft.n2 == 25) return kernel_for<8, 25>(in_dtype);
-  if (p.fft.n1 == 32 && p.fft.n2 == 16) return kernel_for<32, 16>(in_dtype);
-  if (p.fft.n1 == 32 && p.fft.n2 == 32) return kernel_for<32, 32>(in_dtype);
+  const int pm = power_mode(p);
+  if (p.fft.n1 == 8 && p.fft.n2 == 25) return kernel_for<8, 25>(in_dtype, pm);
+  if (p.fft.n1 == 32 && p.fft.n2 == 16) return kernel_for<32, 16>(in_dtype, pm);
+  if (p.fft.n1 == 32 && p.fft.n2 == 32) return kernel_for<32, 32>(in_dtype, pm);
   return nullptr;
 }
 
@@ -253,6 +382,8 @@ int hip_fail(hipError_t e, const char* what) {
 int upload_plan(Plan& p) {
   hipError_t e = hipGetDevice(&p.device);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  e = hipDeviceGetAttribute(&p.n_cu, hipDeviceAttributeMultiprocessorCount, p.device);
+  if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
   const int M = p.n_fft / 2;
   // one block: win2 | tw_m | tw_n | rows | mel_w, each 256-byte aligned
   auto al = [](size_t n) { return (n + 255) / 256 * 256; };
@@ -261,7 +392,9 @@ int upload_plan(Plan& p) {
   const size_t o_twn = o_twm + al(M * sizeof(float2));
   const size_t o_rows = o_twn + al(M * sizeof(float2));
   const size_t o_w = o_rows + al(p.n_mels * sizeof(MelRow));
-  const size_t total = o_w + al(static_cast<size_t>(p.nnz > 0 ? p.nnz : 1) * sizeof(float));
+  const size_t o_st = o_w + al(static_cast<size_t>(p.nnz > 0 ? p.nnz : 1) * sizeof(float));
+  const size_t o_em = o_st + al(std::max<size_t>(p.steps.size(), 1) * sizeof(SweepStep));
+  const size_t total = o_em + al(std::max<size_t>(p.empty_mels.size(), 1) * sizeof(int32_t));
   std::vector<unsigned char> host(total, 0);
   float* win2 = reinterpret_cast<float*>(host.data() + o_win);
   for (int j = 0; j < p.n_fft; ++j) win2[j] = 0.5f * p.window[j];  // exact scaling
@@ -269,6 +402,8 @@ int upload_plan(Plan& p) {
   std::copy(p.tw_n.begin(), p.tw_n.end(), reinterpret_cast<float*>(host.data() + o_twn));
   std::copy(p.rows.begin(), p.rows.end(), reinterpret_cast<MelRow*>(host.data() + o_rows));
   std::copy(p.mel_w.begin(), p.mel_w.end(), reinterpret_cast<float*>(host.data() + o_w));
+  std::copy(p.steps.begin(), p.steps.end(), reinterpret_cast<SweepStep*>(host.data() + o_st));
+  std::copy(p.empty_mels.begin(), p.empty_mels.end(), reinterpret_cast<int32_t*>(host.data() + o_em));
   void* d = nullptr;
   e = hipMalloc(&d, total);
   if (e != hipSuccess) return set_error(FM_E_NOMEM, std::string("hipMalloc: ") + hipGetErrorString(e));
@@ -284,6 +419,8 @@ int upload_plan(Plan& p) {
   p.d_tw_n = base + o_twn;
   p.d_rows = base + o_rows;
   p.d_mel_w = base + o_w;
+  p.d_steps = base + o_st;
+  p.d_empty = base + o_em;
   // Tiles above 64 KB of LDS need the per-kernel opt-in.
   for (int dt : {FM_F32, FM_I16}) {
     void* k = select_kernel(p, dt);
@@ -307,6 +444,29 @@ void free_plan_device(Plan& p) {
   p.has_device = false;
 }
 
+namespace {
+
+// Frames per tile for this call: the largest tile whose busiest compute
+// unit holds the fewest frames (all tiles resident at once when they fit).
+int choose_tile(const Plan& p, int64_t batch, int64_t T) {
+  if (p.tile_override > 0) return p.tile_override;
+  const int ncu = p.n_cu > 0 ? p.n_cu : 256;
+  int best = p.tile_max;
+  int64_t best_cost = INT64_MAX;
+  for (int g = p.tile_max; g >= 1 && g * 2 >= p.tile_max; --g) {
+    const int64_t tiles = batch * ((T + g - 1) / g);
+    const int64_t per_cu = (tiles + ncu - 1) / ncu;
+    const int64_t cost = per_cu * g;
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = g;
+    }
+  }
+  return best;
+}
+
+}  // namespace
+
 int launch_forward(const Plan& p, const void* in, int in_dtype, int64_t batch, int64_t length,
                    float* out, void* stream) {
   if (!p.has_device) return set_error(FM_E_NODEVICE, "plan was built without device tables");
@@ -320,8 +480,12 @@ int launch_forward(const Plan& p, const void* in, int in_dtype, int64_t batch, i
   hipError_t e = hipGetDevice(&cur);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
   if (cur != p.device) return set_error(FM_E_INVAL, "plan belongs to another device than the current one");
-  const int64_t tiles = (T + p.tile_frames - 1) / p.tile_frames;
-  if (T > INT32_MAX || tiles * batch > INT32_MAX) return set_error(FM_E_INVAL, "problem too large for one launch");
+  const int G = choose_tile(p, batch, T);
+  const int64_t tiles = (T + G - 1) / G;
+  if (length > (1 << 29) || tiles * batch > INT32_MAX)
+    return set_error(FM_E_INVAL, "problem too large for one launch (length <= 2^29, tiles < 2^31)");
+  const int lds = tile_lds_bytes(p, G);
+  const int64_t n_tiles = tiles * batch;
 
   KArgs a;
   a.in = in;
@@ -329,29 +493,27 @@ int launch_forward(const Plan& p, const void* in, int in_dtype, int64_t batch, i
   a.win2 = static_cast<const float2*>(p.d_win2);
   a.tw_m = static_cast<const float2*>(p.d_tw_m);
   a.tw_n = static_cast<const float2*>(p.d_tw_n);
-  a.rows = static_cast<const MelRow*>(p.d_rows);
-  a.mel_w = static_cast<const float*>(p.d_mel_w);
   a.length = length;
   a.n_frames = static_cast<int>(T);
   a.hop = p.hop;
   a.pad = p.pad_left;
   a.n_mels = p.n_mels;
-  a.nnz = p.nnz;
-  a.tile = p.tile_frames;
+  a.tile = G;
   a.tiles_per_signal = static_cast<int>(tiles);
   a.pad_mode = p.pad_mode;
-  a.power_mode = (p.power == 2.0) ? 0 : (p.power == 1.0 ? 1 : 2);
   a.half_power = static_cast<float>(p.power * 0.5);
   const size_t esz = (in_dtype == FM_I16) ? 2 : 4;
   const uintptr_t ia = reinterpret_cast<uintptr_t>(in);
   a.vec_ok = (ia % (2 * esz) == 0) && (length % 2 == 0) && (p.hop % 2 == 0) && (p.pad_left % 2 == 0);
-  a.lds_y_bytes = p.lds_y_bytes;
+  a.steps = static_cast<const SweepStep*>(p.d_steps);
+  a.empty_mels = static_cast<const int*>(p.d_empty);
+  for (int w = 0; w < 4; ++w) a.sweep[w] = p.sweep[w];
 
   void* k = select_kernel(p, in_dtype);
   if (!k) return set_error(FM_E_UNSUPPORTED, "no kernel for this n_fft");
   void* args[] = {&a};
-  e = hipLaunchKernel(k, dim3(static_cast<unsigned>(tiles * batch)), dim3(p.threads), args,
-                      static_cast<size_t>(p.lds_bytes), static_cast<hipStream_t>(stream));
+  e = hipLaunchKernel(k, dim3(static_cast<unsigned>(n_tiles)), dim3(p.threads), args,
+                      static_cast<size_t>(lds), static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
   e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "kernel launch");

@@ -73,14 +73,6 @@ bool fft_shape_for(int n_fft, FftShape* s) {
   }
 }
 
-int default_tile_frames(int n_fft) {
-  switch (n_fft) {
-    case 400: return 32;
-    case 1024: return 16;
-    default: return 8;
-  }
-}
-
 std::string fmt(const char* what, double v) {
   std::ostringstream o;
   o << what << " (got " << v << ")";
@@ -89,12 +81,29 @@ std::string fmt(const char* what, double v) {
 
 }  // namespace
 
+int tile_exchange_bytes(const Plan& p, int frames) {
+  // complex exchange buffer Y[frames][n_fft/2]; the power tile
+  // P[frames][n_fft/2 + 1] aliases it.
+  const int M = p.n_fft / 2;
+  long y = static_cast<long>(frames) * M * 8;
+  long pw = static_cast<long>(std::max(frames, 1)) * (M + 1) * 4;
+  long b = std::max(y, pw);
+  return static_cast<int>((b + 15) / 16 * 16);
+}
+
+int tile_lds_bytes(const Plan& p, int frames) {
+  // the mel sweep reads up to 7 padding bins past a power row
+  return tile_exchange_bytes(p, frames) + 32;
+}
+
 int64_t out_frames(const Plan& p, int64_t length) {
   if (length < 1) return set_error(FM_E_INVAL, "length must be >= 1");
   if (p.center) {
     if (p.pad_mode == FM_PAD_REFLECT && length <= p.pad_left)
       return set_error(FM_E_INVAL,
                        "reflect padding needs length > n_fft/2 (one reflection)");
+    if (p.pad_mode == FM_PAD_CIRCULAR && length < p.pad_left)
+      return set_error(FM_E_INVAL, "circular padding needs length >= n_fft/2 (one wrap)");
     int64_t lp = length + 2 * static_cast<int64_t>(p.pad_left);
     if (lp < p.n_fft) return set_error(FM_E_INVAL, "signal shorter than one frame");
     return 1 + (lp - p.n_fft) / p.hop;
@@ -201,22 +210,86 @@ int build_host_plan(Plan& p, int sample_rate, int n_fft, int win_length,
   }
 
   // ---- tile geometry -------------------------------------------------------
-  int tile = default_tile_frames(n_fft);
+  // At most 64 frames per workgroup tile (one per lane in the mel stage);
+  // the second FFT pass gives each thread one pair of n2-point transforms,
+  // and the complex exchange buffer must fit the 160 KB of LDS.
+  int tmax = 64;
+  while (tmax > 1 && tmax * (fs.n1 / 2) > p.threads) --tmax;
+  while (tmax > 1 && tile_lds_bytes(p, tmax) > 160 * 1024) --tmax;
+  p.tile_max = tmax;
+  p.lds_bytes = tile_lds_bytes(p, tmax);
+  p.tile_override = 0;
   if (const char* e = std::getenv("FM_TILE_FRAMES")) {
     int v = std::atoi(e);
-    if (v >= 1 && v <= 64) tile = v;
+    if (v >= 1 && v <= tmax) p.tile_override = v;
   }
-  // The second FFT pass gives each thread one pair of n2-point transforms.
-  while (tile > 1 && tile * (fs.n1 / 2) > p.threads) --tile;
-  p.tile_frames = tile;
-  p.lds_y_bytes = tile * M * 8;  // complex exchange buffer; power tile aliases it
-  const int pw_bytes = tile * p.n_freqs * 4;
-  if (pw_bytes > p.lds_y_bytes) p.lds_y_bytes = pw_bytes;
-  p.lds_y_bytes = (p.lds_y_bytes + 15) / 16 * 16;
-  const int w_bytes = (p.nnz + 3) / 4 * 16;
-  p.lds_bytes = p.lds_y_bytes + w_bytes + n_mels * static_cast<int>(sizeof(MelRow));
-  if (p.lds_bytes > 160 * 1024)
-    return set_error(FM_E_UNSUPPORTED, "tile does not fit in 160 KB of LDS");
+  // Mel rows split over the 4 waves of a workgroup with about equal work
+  // (weights plus a per-row overhead), in contiguous row ranges.
+  {
+    const int kWaves = 4, kRowCost = 3;
+    long total = 0;
+    for (int m = 0; m < n_mels; ++m) total += p.rows[m].len + kRowCost;
+    p.mel_split[0] = 0;
+    long acc = 0;
+    int w = 1;
+    for (int m = 0; m < n_mels && w < kWaves; ++m) {
+      acc += p.rows[m].len + kRowCost;
+      while (w < kWaves && acc * kWaves >= total * w) p.mel_split[w++] = m + 1;
+    }
+    while (w <= kWaves) p.mel_split[w++] = n_mels;
+  }
+  // Each wave sweeps the bins of its filters once.  Triangular filters are
+  // contiguous, start and end in filter order, and overlap pairwise, so at
+  // most two are open at any bin; a filter ends when the sweep passes its
+  // last bin.
+  p.steps.clear();
+  p.empty_mels.clear();
+  for (int w = 0; w < 4; ++w) {
+    WaveSweep ws{0, static_cast<int32_t>(p.steps.size()), 0,
+                 static_cast<int32_t>(p.empty_mels.size()), 0};
+    std::vector<int> live;
+    for (int m = p.mel_split[w]; m < p.mel_split[w + 1]; ++m) {
+      if (p.rows[m].len == 0) p.empty_mels.push_back(m);
+      else live.push_back(m);
+    }
+    ws.n_empty = static_cast<int32_t>(p.empty_mels.size()) - ws.empty_off;
+    if (!live.empty()) {
+      int k_lo = p.rows[live[0]].first, k_hi = 0;
+      for (int m : live) {
+        k_lo = std::min(k_lo, static_cast<int>(p.rows[m].first));
+        k_hi = std::max(k_hi, static_cast<int>(p.rows[m].first + p.rows[m].len - 1));
+      }
+      ws.k0 = k_lo;
+      std::vector<int> open;
+      size_t next = 0;
+      for (int k = k_lo; k <= k_hi; ++k) {
+        while (next < live.size() && p.rows[live[next]].first == k) open.push_back(live[next++]);
+        if (open.size() > 2)
+          return set_error(FM_E_UNSUPPORTED, "filterbank has more than two filters at one bin");
+        auto weight = [&](int m) {
+          const MelRow& r = p.rows[m];
+          return (k >= r.first && k < r.first + r.len) ? p.mel_w[r.off + k - r.first] : 0.0f;
+        };
+        SweepStep st{0.0f, 0.0f, 0, 0};
+        if (!open.empty()) st.wa = weight(open[0]);
+        if (open.size() > 1) st.wb = weight(open[1]);
+        int n_end = 0;
+        while (n_end < static_cast<int>(open.size()) &&
+               p.rows[open[n_end]].first + p.rows[open[n_end]].len - 1 == k) ++n_end;
+        for (size_t j = n_end; j < open.size(); ++j)
+          if (p.rows[open[j]].first + p.rows[open[j]].len - 1 == k)
+            return set_error(FM_E_UNSUPPORTED, "filters do not end in order");
+        if (n_end > 0) st.code = n_end | (open[0] << 8) | (n_end > 1 ? (open[1] << 16) : 0);
+        open.erase(open.begin(), open.begin() + n_end);
+        p.steps.push_back(st);
+      }
+      if (next != live.size() || !open.empty())
+        return set_error(FM_E_UNSUPPORTED, "filters do not start in order");
+    }
+    while ((p.steps.size() - ws.step_off) % 8) p.steps.push_back(SweepStep{0.0f, 0.0f, 0, 0});
+    ws.nsteps = static_cast<int32_t>(p.steps.size()) - ws.step_off;
+    p.sweep[w] = ws;
+  }
   return FM_OK;
 }
 
