@@ -29,9 +29,13 @@ class MelSpectrogram:
                                power=power, center=center, pad_mode=pad_mode,
                                mel_scale=mel_scale, norm=norm, device=True)
         self.n_mels = n_mels
+        self._frames = {}
 
     def out_frames(self, length: int) -> int:
-        return self.plan.out_frames(length)
+        T = self._frames.get(length)
+        if T is None:
+            T = self._frames[length] = self.plan.out_frames(length)
+        return T
 
     def __call__(self, x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
         if not isinstance(x, torch.Tensor) or x.device != self.device:
@@ -51,14 +55,17 @@ class MelSpectrogram:
         lead = tuple(x.shape[:-1])
         length = int(x.shape[-1])
         batch = math.prod(lead) if lead else 1
-        T = self.plan.out_frames(length)
+        T = self.out_frames(length)
         shape = lead + (self.n_mels, T)
         if out is None:
             out = torch.empty(shape, dtype=torch.float32, device=self.device)
         elif (tuple(out.shape) != shape or out.dtype != torch.float32 or out.device != self.device
               or not out.is_contiguous()):
             raise ValueError(f"out must be a contiguous float32 tensor of shape {shape} on {self.device}")
-        with torch.cuda.device(self.device):
-            stream = torch.cuda.current_stream(self.device).cuda_stream
+        stream = torch.cuda.current_stream(self.device).cuda_stream
+        if torch.cuda.current_device() == self.device.index:
             self.plan.forward_ptr(x.data_ptr(), dt, batch, length, out.data_ptr(), stream)
+        else:
+            with torch.cuda.device(self.device):
+                self.plan.forward_ptr(x.data_ptr(), dt, batch, length, out.data_ptr(), stream)
         return out
