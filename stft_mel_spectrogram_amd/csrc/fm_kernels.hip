@@ -111,17 +111,17 @@ __device__ __forceinline__ float power_of(float sq, float hp) {
   }
 }
 
-// Real-spectrum split for the bin pair (k, M-k) and their powers.
+// Real-spectrum split for the bin pair (k, M-k): powers to *pk and *pm.
 template <int PMODE>
-__device__ __forceinline__ void split_pair(float* prow, int k, int kmirror, float2 zk, float2 zm,
-                                           float2 w, float hp) {
+__device__ __forceinline__ void split_pair(float* pk, float* pm, float2 zk, float2 zm, float2 w,
+                                           float hp) {
   const float2 e = make_float2(zk.x + zm.x, zk.y - zm.y);  // Z[k] + conj Z[M-k]
   const float2 o = make_float2(zk.x - zm.x, zk.y + zm.y);  // Z[k] - conj Z[M-k]
   const float2 v = cmul(w, o);
   const float ax = e.x + v.y, ay = e.y - v.x;  // X[k]   = e - i v
   const float bx = e.x - v.y, by = e.y + v.x;  // X[M-k] = conj(e + i v)
-  prow[k] = power_of<PMODE>(fmaf(ax, ax, ay * ay), hp);
-  prow[kmirror] = power_of<PMODE>(fmaf(bx, bx, by * by), hp);
+  *pk = power_of<PMODE>(fmaf(ax, ax, ay * ay), hp);
+  *pm = power_of<PMODE>(fmaf(bx, bx, by * by), hp);
 }
 
 template <int N1, int N2, typename InT, int PMODE>
@@ -234,21 +234,26 @@ __global__ __launch_bounds__(256) void mel_forward_kernel(KArgs a) {
     // ---- pass 2: paired N2-point DFTs, real split, power -> P (aliases Y) --
     const bool has = f2 < nvalid;
     constexpr bool kTwPrefetch = M <= 256;  // registers allow it for small FFTs
+    // Unified split schedule: lanes with p != 0 pair bins p + N1*k2 (row p)
+    // with M - that (row N1 - p); lanes with p == 0 own the self-paired rows 0
+    // and N1/2 and walk the same N2 iterations with their rows permuted
+    // (k2 < CA: row 0's pairs, k2 >= CA: row N1/2's), plus one extra pair.
+    // One instruction stream for every lane: no divergent branches.
+    constexpr int CA = N2 / 2 + 1;        // row 0 pairs of the p == 0 lanes
+    constexpr int D2 = N1 / 2 - N1 * CA;  // bin offset of row N1/2's pairs there
+    constexpr int JX = N2 - CA;           // index of row N1/2's extra pair
+    const bool p0 = (p == 0);
+    const int off_lo = p;                 // bin = off + N1*k2 for k2 < CA
+    const int off_hi = p0 ? D2 : p;       // ... and for k2 >= CA
     float2 za[N2], zb[N2], wv[kTwPrefetch ? N2 + 1 : 1];
     auto tw_at = [&](int idx, int k) -> float2 {
       return kTwPrefetch ? wv[kTwPrefetch ? idx : 0] : a.tw_n[k];
     };
     if (has) {
       if constexpr (kTwPrefetch) {  // split twiddles load under the DFTs
-        if (p != 0) {
 #pragma unroll
-          for (int k2 = 0; k2 < N2; ++k2) wv[k2] = a.tw_n[p + N1 * k2];
-        } else {
-#pragma unroll
-          for (int k2 = 0; k2 <= N2 / 2; ++k2) wv[k2] = a.tw_n[N1 * k2];
-#pragma unroll
-          for (int k2 = 0; k2 <= (N2 - 1) / 2; ++k2) wv[N2 / 2 + 1 + k2] = a.tw_n[N1 / 2 + N1 * k2];
-        }
+        for (int k2 = 0; k2 < N2; ++k2) wv[k2] = a.tw_n[(k2 < CA ? off_lo : off_hi) + N1 * k2];
+        wv[N2] = a.tw_n[N1 / 2 + N1 * JX];
       }
       const int ka = p;
       const int kb = (p == 0) ? N1 / 2 : N1 - p;
@@ -266,26 +271,30 @@ __global__ __launch_bounds__(256) void mel_forward_kernel(KArgs a) {
     if (has) {
       float* prow = P + f2 * K;
       const float hp = a.half_power;
-      if (p != 0) {
-        // bins k = p + N1*k2 (za) and M - k = (N1 - p) + N1*(N2-1-k2) (zb)
+      // bin k = off + N1*k2 and its mirror M - k, as per-lane bases plus
+      // compile-time (non-negative) offsets
+      float* pk_lo = prow + off_lo;
+      float* pk_hi = prow + off_hi;
+      float* pm_lo = prow + (M - off_lo - N1 * (N2 - 1));
+      float* pm_hi = prow + (M - off_hi - N1 * (N2 - 1));
 #pragma unroll
-        for (int k2 = 0; k2 < N2; ++k2) {
-          const int k = p + N1 * k2;
-          split_pair<PMODE>(prow, k, M - k, za[k2], zb[N2 - 1 - k2], tw_at(k2, k), hp);
+      for (int k2 = 0; k2 < N2; ++k2) {
+        float2 zk, zm;
+        if (k2 < CA) {
+          zk = za[k2];
+          zm = p0 ? za[(N2 - k2) % N2] : zb[N2 - 1 - k2];
+        } else {
+          zk = p0 ? zb[k2 - CA] : za[k2];
+          zm = p0 ? zb[N2 - 1 - (k2 - CA)] : zb[N2 - 1 - k2];
         }
-      } else {
-        // k1 = 0: bins N1*k2 pair with N1*(N2-k2) inside za
-#pragma unroll
-        for (int k2 = 0; k2 <= N2 / 2; ++k2) {
-          const int k = N1 * k2;
-          split_pair<PMODE>(prow, k, M - k, za[k2], za[(N2 - k2) % N2], tw_at(k2, k), hp);
-        }
-        // k1 = N1/2: bins N1/2 + N1*k2 pair with N1/2 + N1*(N2-1-k2) inside zb
-#pragma unroll
-        for (int k2 = 0; k2 <= (N2 - 1) / 2; ++k2) {
-          const int k = N1 / 2 + N1 * k2;
-          split_pair<PMODE>(prow, k, M - k, zb[k2], zb[N2 - 1 - k2], tw_at(N2 / 2 + 1 + k2, k), hp);
-        }
+        const int k = (k2 < CA ? off_lo : off_hi) + N1 * k2;
+        float* pk = (k2 < CA ? pk_lo : pk_hi) + N1 * k2;
+        float* pm = (k2 < CA ? pm_lo : pm_hi) + N1 * (N2 - 1 - k2);
+        split_pair<PMODE>(pk, pm, zk, zm, tw_at(k2, k), hp);
+      }
+      if (p0) {
+        constexpr int k = N1 / 2 + N1 * JX;
+        split_pair<PMODE>(prow + k, prow + (M - k), zb[JX], zb[N2 - 1 - JX], tw_at(N2, k), hp);
       }
     }
     __syncthreads();
@@ -295,11 +304,12 @@ __global__ __launch_bounds__(256) void mel_forward_kernel(KArgs a) {
     {
       const WaveSweep ws = a.sweep[wave];
       const float* pp = P + min(lane, G - 1) * K + ws.k0;
+      // output is written once and never re-read here: streaming stores
       float* obase = a.out + static_cast<long long>(b) * a.n_mels * a.n_frames + t0 + lane;
       const bool store = lane < nvalid;
       CInt* empt = (CInt*)(a.empty_mels) + ws.empty_off;  // address-space cast
       for (int i = 0; i < ws.n_empty; ++i)
-        if (store) obase[static_cast<long long>(empt[i]) * a.n_frames] = 0.0f;
+        if (store) __builtin_nontemporal_store(0.0f, obase + static_cast<long long>(empt[i]) * a.n_frames);
       CStep* st = (CStep*)(a.steps) + ws.step_off;  // address-space cast
       float acc_a = 0.0f, acc_b = 0.0f;
       // steps come in chunks of 8: the next chunk's scalars load while this
@@ -328,9 +338,9 @@ __global__ __launch_bounds__(256) void mel_forward_kernel(KArgs a) {
           acc_a = fmaf(cwa[u], pv[u], acc_a);
           acc_b = fmaf(cwb[u], pv[u], acc_b);
           if (code & 3) {
-            if (store) obase[static_cast<long long>((code >> 8) & 0xff) * a.n_frames] = acc_a;
+            if (store) __builtin_nontemporal_store(acc_a, obase + static_cast<long long>((code >> 8) & 0xff) * a.n_frames);
             if ((code & 3) == 2) {
-              if (store) obase[static_cast<long long>((code >> 16) & 0xff) * a.n_frames] = acc_b;
+              if (store) __builtin_nontemporal_store(acc_b, obase + static_cast<long long>((code >> 16) & 0xff) * a.n_frames);
               acc_a = 0.0f;
             } else {
               acc_a = acc_b;
