@@ -60,6 +60,7 @@ def _load() -> ctypes.CDLL:
         "fm_last_error": (ctypes.c_char_p, []),
         "fm_plan_info_get": (I, [P, ctypes.POINTER(PlanInfo)]),
         "fm_plan_tables": (I, [P, P, P, P, P, P, P, P]),
+        "fm_plan_mel_blocks": (I, [P, P, P, P, P, P]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -135,6 +136,20 @@ class Plan:
                                  ptr(twm), ptr(twn)))
         return dict(window=win, first=first, len=ln, off=off, weights=w[:inf.nnz],
                     tw_m=twm[0::2] + 1j * twm[1::2], tw_n=twn[0::2] + 1j * twn[1::2])
+
+    def mel_blocks(self):
+        """The mel stage's block layout: (blocks[n,4] = kb, ksteps, w_off, mel0;
+        wave_beg[5]; weights)."""
+        import numpy as np
+        nb = ctypes.c_int32()
+        nw = ctypes.c_int64()
+        check(lib.fm_plan_mel_blocks(self.handle, None, None, None, ctypes.byref(nb), ctypes.byref(nw)))
+        blocks = np.zeros(max(nb.value, 1) * 4, np.int32)
+        wave_beg = np.zeros(5, np.int32)
+        w = np.zeros(max(nw.value, 1), np.float32)
+        ptr = lambda a: a.ctypes.data_as(ctypes.c_void_p)  # noqa: E731
+        check(lib.fm_plan_mel_blocks(self.handle, ptr(blocks), ptr(wave_beg), ptr(w), None, None))
+        return blocks[:4 * nb.value].reshape(-1, 4), wave_beg, w[:nw.value]
 
     def forward_ptr(self, in_ptr: int, in_dtype: int, batch: int, length: int, out_ptr: int,
                     stream: int = 0) -> None:

@@ -130,4 +130,23 @@ int fm_plan_tables(const fm_plan* plan, float* window, int32_t* mel_first, int32
   return FM_OK;
 }
 
+int fm_plan_mel_blocks(const fm_plan* plan, int32_t* blocks, int32_t* wave_beg, float* weights,
+                       int32_t* n_blocks, int64_t* n_weights) {
+  if (!plan) return fm::set_error(FM_E_INVAL, "plan must not be NULL");
+  const fm::Plan& p = plan->p;
+  if (blocks)
+    for (size_t j = 0; j < p.blocks.size(); ++j) {
+      blocks[4 * j + 0] = p.blocks[j].kb;
+      blocks[4 * j + 1] = p.blocks[j].ksteps;
+      blocks[4 * j + 2] = p.blocks[j].w_off;
+      blocks[4 * j + 3] = p.blocks[j].mel0;
+    }
+  if (wave_beg)
+    for (int w = 0; w <= fm::kMelWaves; ++w) wave_beg[w] = p.wave_beg[w];
+  if (weights) std::memcpy(weights, p.blk_w.data(), p.blk_w.size() * sizeof(float));
+  if (n_blocks) *n_blocks = static_cast<int32_t>(p.blocks.size());
+  if (n_weights) *n_weights = static_cast<int64_t>(p.blk_w.size());
+  return FM_OK;
+}
+
 }  // extern "C"

@@ -16,20 +16,34 @@ struct MelRow {
   int32_t first, len, off, pad_;
 };
 
-// One step of a wave's sweep over consecutive bins in the mel stage: the
-// weights of the bin in the (at most two) filters open at that bin, and the
-// filters that end at it.  code = n_end | (mel_a << 8) | (mel_b << 16): after
-// the bin, n_end (0..2) open filters end, the older one being mel_a.
-struct SweepStep {
-  float wa, wb;
-  int32_t code, pad_;
+// The mel projection runs on the matrix cores: filters in blocks of 16 (the
+// M side of a 16x16x4 f32 MFMA), each block against the contiguous run of
+// bins its filters touch, in steps of 4 bins (the K side), frames as the N
+// side.  A block's weights are stored dense, 64 per step, in the lane order
+// of the MFMA's A operand (lane l: filter mel0 + l%16, bin kb + 4*step + l/16),
+// zero where a filter has no weight.
+struct MelBlock {
+  int32_t kb;      // first bin of the run
+  int32_t ksteps;  // 4-bin steps, a multiple of kMelStepGroup (0 when every
+                   // filter of the block is empty)
+  int32_t w_off;   // offset of the block's weights (floats)
+  int32_t mel0;    // first filter of the block
 };
-
-// A wave's share of the mel stage: bins k0 .. k0 + nsteps - 1 (nsteps a
-// multiple of 8, tail steps zero), and the empty filters it writes as 0.
-struct WaveSweep {
-  int32_t k0, step_off, nsteps, empty_off, n_empty;
-};
+constexpr int kMelBlock = 16;
+constexpr int kMaxMelBlocks = 16;  // n_mels <= 256
+constexpr int kMelWaves = 4;       // waves of a workgroup
+// The kernel runs steps in groups of this many (blocks are zero-padded to
+// whole groups, so the table is a whole number of 256-float chunks, the unit
+// in which it is copied to LDS).
+constexpr int kMelStepGroup = 4;
+// Power-tile floats the mel stage may read past the tile (zeroed there).
+constexpr int kMelTileOverrun = 16;
+// Tiles of more than this many frames write their mel rows through a
+// per-wave LDS staging area (one contiguous store per row, rows long enough
+// to cover whole cache lines); narrower tiles store the MFMA results directly.
+constexpr int kMelStageMinFrames = 33;
+// Staging floats per wave: 16 filters x (64 frames + 1 pad).
+constexpr int kMelStageFloats = 16 * 65;
 
 // FFT factorisation of the complex transform of n_fft/2 points that carries
 // the real FFT (even samples as real part, odd samples as imaginary part).
@@ -50,10 +64,10 @@ struct Plan {
   int tile_override = 0; // FM_TILE_FRAMES, for sweeps (0: chosen per call)
   int threads = 256;
   int lds_bytes = 0;     // dynamic LDS of a tile of tile_max frames
-  int mel_split[5] = {0, 0, 0, 0, 0};  // mel rows of each of the 4 waves
-  WaveSweep sweep[4] = {};             // per-wave mel sweep
-  std::vector<SweepStep> steps;        // all waves' sweep steps
-  std::vector<int32_t> empty_mels;     // filters with no bin, by wave
+  // mel blocks in wave order: wave w takes blocks [wave_beg[w], wave_beg[w+1])
+  std::vector<MelBlock> blocks;
+  int wave_beg[kMelWaves + 1] = {};
+  std::vector<float> blk_w;            // block weights (see MelBlock)
   int nnz = 0, w_max = 0;
   // host tables (float32 after one rounding from float64)
   std::vector<float> window;  // [n_fft], unscaled
@@ -71,8 +85,8 @@ struct Plan {
   const void* d_tw_n = nullptr;   // float2[M]
   const void* d_rows = nullptr;   // MelRow[n_mels]
   const void* d_mel_w = nullptr;  // float[nnz]
-  const void* d_steps = nullptr;  // SweepStep[steps.size()]
-  const void* d_empty = nullptr;  // int32[empty_mels.size()]
+  const void* d_mel_tbl = nullptr;    // int32[8 + 4*n_blocks]: wave_beg, pad, blocks
+  const void* d_blk_w = nullptr;      // float[blk_w.size()]
 };
 
 // Thread-local error reporting.
@@ -85,9 +99,12 @@ int build_host_plan(Plan& p, int sample_rate, int n_fft, int win_length,
                     double power, int center, int pad_mode, int mel_scale,
                     int norm);
 
-// Dynamic LDS of a tile of `frames` frames: the exchange / power buffer,
-// then the staged mel weights and CSR rows.
+// LDS layout of a tile of `frames` frames: the FFT exchange buffer, which
+// later holds the power tile, its zeroed overrun floats, (from float
+// tile_weights_offset) the mel block weights and, for wide tiles, the 4
+// waves' output staging areas right after them.
 int tile_exchange_bytes(const Plan& p, int frames);
+int tile_weights_offset(const Plan& p, int frames);
 int tile_lds_bytes(const Plan& p, int frames);
 
 // Frames per signal for a plan (negative FM_E_* on invalid length).

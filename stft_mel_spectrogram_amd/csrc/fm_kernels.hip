@@ -16,7 +16,9 @@
 //              X[k] = (Z[k] + conj Z[M-k]) - i W_N^k (Z[k] - conj Z[M-k])
 //           (window pre-scaled by 1/2) and |X|^p need no further exchange.
 // The power tile P[f][k] (odd row stride n_fft/2+1) reuses the exchange
-// buffer.  The mel projection walks each filter's CSR run only.
+// buffer.  The mel projection is a block-sparse product on the matrix cores:
+// 16 filters x 16 frames per v_mfma_f32_16x16x4f32, over only the bins each
+// block of filters touches.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -45,23 +47,96 @@ struct KArgs {
   int pad_mode;
   float half_power;     // power / 2
   int vec_ok;           // interior tiles may use paired (2-sample) loads
-  const SweepStep* steps;  // mel sweep steps of all waves
-  const int* empty_mels;   // filters with no bin
-  WaveSweep sweep[4];      // each wave's share of the mel stage
+  const int* mel_tbl;   // wave_beg[5], 3 pad, then {kb, ksteps, w_off, mel0} per block
+  const float* blk_w;   // block weights, 64 per 4-bin step (MFMA A-operand order)
+  int w_chunks;         // block weights / 256 (copied to LDS in 1 KB chunks)
+  int w_lds;            // LDS float offset of the copied weights
 };
 
 // Tables read with wave-uniform indices are reached through the constant
 // address space so they load as scalars (SGPR operands of the FMAs).
-using CStep = const __attribute__((address_space(4))) SweepStep;
 using CInt = const __attribute__((address_space(4))) int;
+using CFloat = const __attribute__((address_space(4))) float;
 
-template <typename T>
-__device__ __forceinline__ float sample_to_float(T v);
-template <>
-__device__ __forceinline__ float sample_to_float<float>(float v) { return v; }
-template <>
-__device__ __forceinline__ float sample_to_float<int16_t>(int16_t v) {
-  return static_cast<float>(v) * (1.0f / 32768.0f);  // exact
+using f32x4 = float __attribute__((ext_vector_type(4)));
+
+// Mel projection of one wave's blocks on the matrix cores.  Per block of 16
+// filters and per 4-bin step, one v_mfma_f32_16x16x4f32 for each 16-frame
+// column group (NFB of them):
+//   A (16 filters x 4 bins)  weights, lane l: filter l%16, bin l/16;
+//   B (4 bins x 16 frames)   power tile, lane l: bin l/16, frame l%16;
+//   D (16 x 16)              lane l holds filters 4*(l/16) + r, r < 4, of
+//                            frame l%16.
+// Both operands come from LDS (the weights were copied there); blocks are
+// padded to whole groups of kMelStepGroup steps, so the step loop has no
+// tail.  Columns beyond the tile read its last frame and are not stored.
+// Output: with STAGE the 16 x 16*NFB result goes through the wave's LDS
+// staging area `stg` and each filter row leaves in one contiguous streaming
+// store (lane = frame); otherwise lanes store their D elements directly
+// (plain stores, so that L2 merges the 64-byte pieces of a row).
+template <int K, int NFB, bool STAGE>
+__device__ __forceinline__ void mel_blocks(const float* P, const float* WL, float* stg, int G,
+                                           int nvalid, int lane, float* obase, int n_frames,
+                                           int n_mels, CInt* blk, int bb, int be) {
+  constexpr int U = kMelStepGroup;
+  const int fr = lane & 15, kq = lane >> 4;
+  int roff[NFB];
+#pragma unroll
+  for (int f = 0; f < NFB; ++f) roff[f] = min(16 * f + fr, G - 1) * K + kq;
+  for (int bi = bb; bi < be; ++bi) {
+    const int kb = blk[4 * bi], ks = blk[4 * bi + 1], woff = blk[4 * bi + 2],
+              mel0 = blk[4 * bi + 3];
+    f32x4 acc[NFB];
+#pragma unroll
+    for (int f = 0; f < NFB; ++f) acc[f] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    const float* pb = P + kb;
+    const float* wl = WL + woff + lane;
+    for (int s0 = 0; s0 < ks; s0 += U, pb += 4 * U, wl += 64 * U) {
+      float av[U], bv[U][NFB];
+#pragma unroll
+      for (int u = 0; u < U; ++u) av[u] = wl[64 * u];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int f = 0; f < NFB; ++f) bv[u][f] = pb[roff[f] + 4 * u];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int f = 0; f < NFB; ++f)
+          acc[f] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[u], bv[u][f], acc[f], 0, 0, 0);
+    }
+    if constexpr (STAGE) {
+      constexpr int PITCH = 16 * NFB + 1;  // odd: conflict-free column writes
+#pragma unroll
+      for (int f = 0; f < NFB; ++f)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) stg[(4 * kq + r) * PITCH + 16 * f + fr] = acc[f][r];
+      // the rows are read back by other lanes of this wave: LDS operations
+      // of one wave complete in order, so waiting for the writes suffices
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+      __builtin_amdgcn_wave_barrier();
+      const int nrow = min(16, n_mels - mel0);
+      const bool st = lane < nvalid && lane < 16 * NFB;
+      for (int m = 0; m < nrow; ++m) {
+        const float v = stg[m * PITCH + lane];
+        // output is written once and never re-read here: streaming stores
+        if (st) __builtin_nontemporal_store(v, obase + static_cast<long long>(mel0 + m) * n_frames + lane);
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // reads done before the next block's writes
+      __builtin_amdgcn_wave_barrier();
+    } else {
+      const int mrow = mel0 + 4 * kq;
+#pragma unroll
+      for (int f = 0; f < NFB; ++f) {
+        const int frame = 16 * f + fr;
+        if (frame < nvalid) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (mrow + r < n_mels) obase[static_cast<long long>(mrow + r) * n_frames + frame] = acc[f][r];
+        }
+      }
+    }
+  }
 }
 
 // Source index of position i of the padded signal (i relative to sample 0),
@@ -124,8 +199,13 @@ __device__ __forceinline__ void split_pair(float* pk, float* pm, float2 zk, floa
   *pm = power_of<PMODE>(fmaf(bx, bx, by * by), hp);
 }
 
+// Two workgroups per compute unit (2 waves per SIMD, <= 256 registers each)
+// wherever two tiles fit the LDS; n_fft = 2048 tiles take the whole LDS.
+template <int N1, int N2>
+constexpr int kMinWavesPerSimd = (N1 * N2 <= 512) ? 2 : 1;
+
 template <int N1, int N2, typename InT, int PMODE>
-__global__ __launch_bounds__(256) void mel_forward_kernel(KArgs a) {
+__global__ __launch_bounds__(256, (kMinWavesPerSimd<N1, N2>)) void mel_forward_kernel(KArgs a) {
   constexpr int M = N1 * N2;
   constexpr int K = M + 1;        // one-sided bins; odd, so P rows are bank-skewed
   constexpr int NF = 2 * M;       // n_fft
@@ -147,7 +227,7 @@ __global__ __launch_bounds__(256) void mel_forward_kernel(KArgs a) {
   // pass-2 role: frame f2, pair p of first-pass outputs
   const int f2 = tid / NPAIR;
   const int p = tid - f2 * NPAIR;
-  // mel role: wave -> contiguous range of mel rows, lane -> frame
+  // mel role: wave -> its list of filter blocks
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
 
@@ -268,6 +348,13 @@ __global__ __launch_bounds__(256) void mel_forward_kernel(KArgs a) {
       Dft<N2>::run(zb);
     }
     __syncthreads();
+    // Every read of the exchange buffer is done: stream the mel weights into
+    // LDS behind the power tile (direct global -> LDS loads, 1 KB per wave
+    // instruction, lane l's 16 bytes at l*16), landing while the split runs.
+    for (int c = wave; c < a.w_chunks; c += 4)
+      __builtin_amdgcn_global_load_lds(a.blk_w + c * 256 + lane * 4, P + a.w_lds + c * 256, 16, 0, 0);
+    // the mel stage may read a few floats past the power tile: keep them 0
+    if (tid < kMelTileOverrun) P[G * K + tid] = 0.0f;
     if (has) {
       float* prow = P + f2 * K;
       const float hp = a.half_power;
@@ -297,63 +384,28 @@ __global__ __launch_bounds__(256) void mel_forward_kernel(KArgs a) {
         split_pair<PMODE>(prow + k, prow + (M - k), zb[JX], zb[N2 - 1 - JX], tw_at(N2, k), hp);
       }
     }
+    __builtin_amdgcn_s_waitcnt(0);  // the weight copies have landed in LDS
     __syncthreads();
 
-    // ---- mel projection: lane = frame; each wave sweeps the bins of its
-    //      filters once, with at most two filters open at a time ------------
+    // ---- mel projection on the matrix cores: each wave its filter blocks,
+    //      16-frame column groups across the tile ---------------------------
     {
-      const WaveSweep ws = a.sweep[wave];
-      const float* pp = P + min(lane, G - 1) * K + ws.k0;
-      // output is written once and never re-read here: streaming stores
-      float* obase = a.out + static_cast<long long>(b) * a.n_mels * a.n_frames + t0 + lane;
-      const bool store = lane < nvalid;
-      CInt* empt = (CInt*)(a.empty_mels) + ws.empty_off;  // address-space cast
-      for (int i = 0; i < ws.n_empty; ++i)
-        if (store) __builtin_nontemporal_store(0.0f, obase + static_cast<long long>(empt[i]) * a.n_frames);
-      CStep* st = (CStep*)(a.steps) + ws.step_off;  // address-space cast
-      float acc_a = 0.0f, acc_b = 0.0f;
-      // steps come in chunks of 8: the next chunk's scalars load while this
-      // one's power values and FMAs are in flight
-      float cwa[8], cwb[8];
-      int ccode[8];
-      auto load_chunk = [&](int s0, float (&wa)[8], float (&wb)[8], int (&code)[8]) {
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          wa[u] = st[s0 + u].wa;
-          wb[u] = st[s0 + u].wb;
-          code[u] = st[s0 + u].code;
-        }
-      };
-      if (ws.nsteps > 0) load_chunk(0, cwa, cwb, ccode);
-      for (int s0 = 0; s0 < ws.nsteps; s0 += 8, pp += 8) {
-        float pv[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) pv[u] = pp[u];
-        float nwa[8], nwb[8];
-        int ncode[8];
-        if (s0 + 8 < ws.nsteps) load_chunk(s0 + 8, nwa, nwb, ncode);
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int code = ccode[u];
-          acc_a = fmaf(cwa[u], pv[u], acc_a);
-          acc_b = fmaf(cwb[u], pv[u], acc_b);
-          if (code & 3) {
-            if (store) __builtin_nontemporal_store(acc_a, obase + static_cast<long long>((code >> 8) & 0xff) * a.n_frames);
-            if ((code & 3) == 2) {
-              if (store) __builtin_nontemporal_store(acc_b, obase + static_cast<long long>((code >> 16) & 0xff) * a.n_frames);
-              acc_a = 0.0f;
-            } else {
-              acc_a = acc_b;
-            }
-            acc_b = 0.0f;
-          }
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          cwa[u] = nwa[u];
-          cwb[u] = nwb[u];
-          ccode[u] = ncode[u];
-        }
+      CInt* tbl = (CInt*)(a.mel_tbl);  // address-space cast: scalar loads
+      const int bb = tbl[wave], be = tbl[wave + 1];
+      float* obase = a.out + static_cast<long long>(b) * a.n_mels * a.n_frames + t0;
+      const int nfb = (G + 15) >> 4;
+      CInt* blk = tbl + 8;
+      const float* WL = P + a.w_lds;
+      float* stg = P + a.w_lds + a.w_chunks * 256 + wave * kMelStageFloats;
+      static_assert(kMelStageMinFrames == 33, "staging is chosen for 3 and 4 column groups");
+      switch (nfb) {
+#define FM_MEL_CALL(NFB, STAGE) \
+  mel_blocks<K, NFB, STAGE>(P, WL, stg, G, nvalid, lane, obase, a.n_frames, a.n_mels, blk, bb, be)
+        case 1: FM_MEL_CALL(1, false); break;
+        case 2: FM_MEL_CALL(2, false); break;
+        case 3: FM_MEL_CALL(3, true); break;
+        default: FM_MEL_CALL(4, true); break;
+#undef FM_MEL_CALL
       }
     }
   }
@@ -395,16 +447,17 @@ int upload_plan(Plan& p) {
   e = hipDeviceGetAttribute(&p.n_cu, hipDeviceAttributeMultiprocessorCount, p.device);
   if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
   const int M = p.n_fft / 2;
-  // one block: win2 | tw_m | tw_n | rows | mel_w, each 256-byte aligned
+  // one block: win2 | tw_m | tw_n | rows | mel_w | mel blocks | block weights,
+  // each 256-byte aligned
   auto al = [](size_t n) { return (n + 255) / 256 * 256; };
   const size_t o_win = 0;
   const size_t o_twm = o_win + al(M * sizeof(float2));
   const size_t o_twn = o_twm + al(M * sizeof(float2));
   const size_t o_rows = o_twn + al(M * sizeof(float2));
   const size_t o_w = o_rows + al(p.n_mels * sizeof(MelRow));
-  const size_t o_st = o_w + al(static_cast<size_t>(p.nnz > 0 ? p.nnz : 1) * sizeof(float));
-  const size_t o_em = o_st + al(std::max<size_t>(p.steps.size(), 1) * sizeof(SweepStep));
-  const size_t total = o_em + al(std::max<size_t>(p.empty_mels.size(), 1) * sizeof(int32_t));
+  const size_t o_tbl = o_w + al(static_cast<size_t>(p.nnz > 0 ? p.nnz : 1) * sizeof(float));
+  const size_t o_bw = o_tbl + al((8 + 4 * p.blocks.size()) * sizeof(int32_t));
+  const size_t total = o_bw + al(std::max<size_t>(p.blk_w.size(), 1) * sizeof(float));
   std::vector<unsigned char> host(total, 0);
   float* win2 = reinterpret_cast<float*>(host.data() + o_win);
   for (int j = 0; j < p.n_fft; ++j) win2[j] = 0.5f * p.window[j];  // exact scaling
@@ -412,8 +465,15 @@ int upload_plan(Plan& p) {
   std::copy(p.tw_n.begin(), p.tw_n.end(), reinterpret_cast<float*>(host.data() + o_twn));
   std::copy(p.rows.begin(), p.rows.end(), reinterpret_cast<MelRow*>(host.data() + o_rows));
   std::copy(p.mel_w.begin(), p.mel_w.end(), reinterpret_cast<float*>(host.data() + o_w));
-  std::copy(p.steps.begin(), p.steps.end(), reinterpret_cast<SweepStep*>(host.data() + o_st));
-  std::copy(p.empty_mels.begin(), p.empty_mels.end(), reinterpret_cast<int32_t*>(host.data() + o_em));
+  int32_t* tbl = reinterpret_cast<int32_t*>(host.data() + o_tbl);
+  for (int w = 0; w <= kMelWaves; ++w) tbl[w] = p.wave_beg[w];
+  for (size_t j = 0; j < p.blocks.size(); ++j) {
+    tbl[8 + 4 * j + 0] = p.blocks[j].kb;
+    tbl[8 + 4 * j + 1] = p.blocks[j].ksteps;
+    tbl[8 + 4 * j + 2] = p.blocks[j].w_off;
+    tbl[8 + 4 * j + 3] = p.blocks[j].mel0;
+  }
+  std::copy(p.blk_w.begin(), p.blk_w.end(), reinterpret_cast<float*>(host.data() + o_bw));
   void* d = nullptr;
   e = hipMalloc(&d, total);
   if (e != hipSuccess) return set_error(FM_E_NOMEM, std::string("hipMalloc: ") + hipGetErrorString(e));
@@ -429,8 +489,8 @@ int upload_plan(Plan& p) {
   p.d_tw_n = base + o_twn;
   p.d_rows = base + o_rows;
   p.d_mel_w = base + o_w;
-  p.d_steps = base + o_st;
-  p.d_empty = base + o_em;
+  p.d_mel_tbl = base + o_tbl;
+  p.d_blk_w = base + o_bw;
   // Tiles above 64 KB of LDS need the per-kernel opt-in.
   for (int dt : {FM_F32, FM_I16}) {
     void* k = select_kernel(p, dt);
@@ -515,9 +575,10 @@ int launch_forward(const Plan& p, const void* in, int in_dtype, int64_t batch, i
   const size_t esz = (in_dtype == FM_I16) ? 2 : 4;
   const uintptr_t ia = reinterpret_cast<uintptr_t>(in);
   a.vec_ok = (ia % (2 * esz) == 0) && (length % 2 == 0) && (p.hop % 2 == 0) && (p.pad_left % 2 == 0);
-  a.steps = static_cast<const SweepStep*>(p.d_steps);
-  a.empty_mels = static_cast<const int*>(p.d_empty);
-  for (int w = 0; w < 4; ++w) a.sweep[w] = p.sweep[w];
+  a.mel_tbl = static_cast<const int*>(p.d_mel_tbl);
+  a.blk_w = static_cast<const float*>(p.d_blk_w);
+  a.w_chunks = static_cast<int>(p.blk_w.size() / 256);
+  a.w_lds = tile_weights_offset(p, G);
 
   void* k = select_kernel(p, in_dtype);
   if (!k) return set_error(FM_E_UNSUPPORTED, "no kernel for this n_fft");

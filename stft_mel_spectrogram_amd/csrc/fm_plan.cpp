@@ -82,18 +82,23 @@ std::string fmt(const char* what, double v) {
 }  // namespace
 
 int tile_exchange_bytes(const Plan& p, int frames) {
-  // complex exchange buffer Y[frames][n_fft/2]; the power tile
-  // P[frames][n_fft/2 + 1] aliases it.
-  const int M = p.n_fft / 2;
-  long y = static_cast<long>(frames) * M * 8;
-  long pw = static_cast<long>(std::max(frames, 1)) * (M + 1) * 4;
-  long b = std::max(y, pw);
-  return static_cast<int>((b + 15) / 16 * 16);
+  // complex exchange buffer Y[frames][n_fft/2]
+  const long y = static_cast<long>(std::max(frames, 1)) * (p.n_fft / 2) * 8;
+  return static_cast<int>((y + 15) / 16 * 16);
+}
+
+int tile_weights_offset(const Plan& p, int frames) {
+  // after the power tile P[frames][n_fft/2 + 1] and its zeroed overrun,
+  // 16-byte aligned
+  const long f = static_cast<long>(std::max(frames, 1)) * p.n_freqs + kMelTileOverrun;
+  return static_cast<int>((f + 3) / 4 * 4);
 }
 
 int tile_lds_bytes(const Plan& p, int frames) {
-  // the mel sweep reads up to 7 padding bins past a power row
-  return tile_exchange_bytes(p, frames) + 32;
+  const long stage = frames >= kMelStageMinFrames ? kMelWaves * kMelStageFloats : 0;
+  const long after_fft = (static_cast<long>(tile_weights_offset(p, frames)) +
+                          static_cast<long>(p.blk_w.size()) + stage) * 4;
+  return static_cast<int>(std::max<long>(tile_exchange_bytes(p, frames), after_fft));
 }
 
 int64_t out_frames(const Plan& p, int64_t length) {
@@ -209,86 +214,89 @@ int build_host_plan(Plan& p, int sample_rate, int n_fft, int win_length,
     p.tw_n[2 * j + 1] = static_cast<float>(-s);
   }
 
+  // ---- mel blocks ----------------------------------------------------------
+  // Blocks of 16 filters; each covers the union of its filters' bin runs,
+  // rounded up to whole groups of 4-bin steps and shifted left if it would
+  // run past the last bin.  When 4*steps exceeds n_freqs it starts at bin 0
+  // and reads at most 15 floats past a frame's row: the next frame's first
+  // bins (times zero weights), or, for the tile's last frame, floats the
+  // kernel zeroes.
+  {
+    const int K = p.n_freqs;
+    const int nb = (n_mels + kMelBlock - 1) / kMelBlock;
+    std::vector<MelBlock> blk(nb);
+    std::vector<std::vector<float>> bw(nb);
+    for (int j = 0; j < nb; ++j) {
+      const int m0 = j * kMelBlock, m1 = std::min(n_mels, m0 + kMelBlock);
+      int lo = K, hi = 0;
+      for (int m = m0; m < m1; ++m)
+        if (p.rows[m].len > 0) {
+          lo = std::min(lo, static_cast<int>(p.rows[m].first));
+          hi = std::max(hi, static_cast<int>(p.rows[m].first + p.rows[m].len));
+        }
+      MelBlock b{0, 0, 0, m0};
+      if (hi > lo) {
+        b.ksteps = ((hi - lo + 3) / 4 + kMelStepGroup - 1) / kMelStepGroup * kMelStepGroup;
+        b.kb = std::max(0, std::min(lo, K - 4 * b.ksteps));
+        bw[j].assign(static_cast<size_t>(b.ksteps) * 64, 0.0f);
+        for (int s = 0; s < b.ksteps; ++s)
+          for (int l = 0; l < 64; ++l) {
+            const int m = m0 + l % kMelBlock, k = b.kb + 4 * s + l / kMelBlock;
+            if (m >= n_mels) continue;
+            const MelRow& r = p.rows[m];
+            if (r.len > 0 && k >= r.first && k < r.first + r.len)
+              bw[j][static_cast<size_t>(s) * 64 + l] = p.mel_w[r.off + k - r.first];
+          }
+      }
+      blk[j] = b;
+    }
+    // Longest first onto the least loaded wave; a block costs its steps plus
+    // 2 for the address set-up and the stores.
+    std::vector<int> order(nb);
+    for (int j = 0; j < nb; ++j) order[j] = j;
+    std::stable_sort(order.begin(), order.end(),
+                     [&](int x, int y) { return blk[x].ksteps > blk[y].ksteps; });
+    long load[kMelWaves] = {};
+    std::vector<int> owner(nb);
+    for (int j : order) {
+      int w = 0;
+      for (int v = 1; v < kMelWaves; ++v)
+        if (load[v] < load[w]) w = v;
+      owner[j] = w;
+      load[w] += blk[j].ksteps + 2;
+    }
+    p.blocks.clear();
+    p.blk_w.clear();
+    for (int w = 0; w < kMelWaves; ++w) {
+      p.wave_beg[w] = static_cast<int>(p.blocks.size());
+      for (int j = 0; j < nb; ++j)
+        if (owner[j] == w) {
+          MelBlock b = blk[j];
+          b.w_off = static_cast<int32_t>(p.blk_w.size());
+          p.blk_w.insert(p.blk_w.end(), bw[j].begin(), bw[j].end());
+          p.blocks.push_back(b);
+        }
+    }
+    p.wave_beg[kMelWaves] = static_cast<int>(p.blocks.size());
+    static_assert(kMelTileOverrun >= 4 * kMelStepGroup - 1, "zeroed tail too short");
+    static_assert(kMelStepGroup * 64 % 256 == 0, "blocks must fill whole copy chunks");
+  }
   // ---- tile geometry -------------------------------------------------------
-  // At most 64 frames per workgroup tile (one per lane in the mel stage);
-  // the second FFT pass gives each thread one pair of n2-point transforms,
-  // and the complex exchange buffer must fit the 160 KB of LDS.
+  // At most 64 frames per workgroup tile (four 16-frame column groups of
+  // the mel stage's matrix products); the second FFT pass gives each thread
+  // one pair of n2-point transforms; the tile's LDS (the exchange buffer, or
+  // the power tile plus the mel weights) must fit the 160 KB of a CU.
   int tmax = 64;
   while (tmax > 1 && tmax * (fs.n1 / 2) > p.threads) --tmax;
   while (tmax > 1 && tile_lds_bytes(p, tmax) > 160 * 1024) --tmax;
+  if (tile_lds_bytes(p, tmax) > 160 * 1024)
+    return set_error(FM_E_UNSUPPORTED, "mel filterbank too large for the LDS of one tile");
   p.tile_max = tmax;
   p.lds_bytes = tile_lds_bytes(p, tmax);
   p.tile_override = 0;
   if (const char* e = std::getenv("FM_TILE_FRAMES")) {
     int v = std::atoi(e);
     if (v >= 1 && v <= tmax) p.tile_override = v;
-  }
-  // Mel rows split over the 4 waves of a workgroup with about equal work
-  // (weights plus a per-row overhead), in contiguous row ranges.
-  {
-    const int kWaves = 4, kRowCost = 3;
-    long total = 0;
-    for (int m = 0; m < n_mels; ++m) total += p.rows[m].len + kRowCost;
-    p.mel_split[0] = 0;
-    long acc = 0;
-    int w = 1;
-    for (int m = 0; m < n_mels && w < kWaves; ++m) {
-      acc += p.rows[m].len + kRowCost;
-      while (w < kWaves && acc * kWaves >= total * w) p.mel_split[w++] = m + 1;
-    }
-    while (w <= kWaves) p.mel_split[w++] = n_mels;
-  }
-  // Each wave sweeps the bins of its filters once.  Triangular filters are
-  // contiguous, start and end in filter order, and overlap pairwise, so at
-  // most two are open at any bin; a filter ends when the sweep passes its
-  // last bin.
-  p.steps.clear();
-  p.empty_mels.clear();
-  for (int w = 0; w < 4; ++w) {
-    WaveSweep ws{0, static_cast<int32_t>(p.steps.size()), 0,
-                 static_cast<int32_t>(p.empty_mels.size()), 0};
-    std::vector<int> live;
-    for (int m = p.mel_split[w]; m < p.mel_split[w + 1]; ++m) {
-      if (p.rows[m].len == 0) p.empty_mels.push_back(m);
-      else live.push_back(m);
-    }
-    ws.n_empty = static_cast<int32_t>(p.empty_mels.size()) - ws.empty_off;
-    if (!live.empty()) {
-      int k_lo = p.rows[live[0]].first, k_hi = 0;
-      for (int m : live) {
-        k_lo = std::min(k_lo, static_cast<int>(p.rows[m].first));
-        k_hi = std::max(k_hi, static_cast<int>(p.rows[m].first + p.rows[m].len - 1));
-      }
-      ws.k0 = k_lo;
-      std::vector<int> open;
-      size_t next = 0;
-      for (int k = k_lo; k <= k_hi; ++k) {
-        while (next < live.size() && p.rows[live[next]].first == k) open.push_back(live[next++]);
-        if (open.size() > 2)
-          return set_error(FM_E_UNSUPPORTED, "filterbank has more than two filters at one bin");
-        auto weight = [&](int m) {
-          const MelRow& r = p.rows[m];
-          return (k >= r.first && k < r.first + r.len) ? p.mel_w[r.off + k - r.first] : 0.0f;
-        };
-        SweepStep st{0.0f, 0.0f, 0, 0};
-        if (!open.empty()) st.wa = weight(open[0]);
-        if (open.size() > 1) st.wb = weight(open[1]);
-        int n_end = 0;
-        while (n_end < static_cast<int>(open.size()) &&
-               p.rows[open[n_end]].first + p.rows[open[n_end]].len - 1 == k) ++n_end;
-        for (size_t j = n_end; j < open.size(); ++j)
-          if (p.rows[open[j]].first + p.rows[open[j]].len - 1 == k)
-            return set_error(FM_E_UNSUPPORTED, "filters do not end in order");
-        if (n_end > 0) st.code = n_end | (open[0] << 8) | (n_end > 1 ? (open[1] << 16) : 0);
-        open.erase(open.begin(), open.begin() + n_end);
-        p.steps.push_back(st);
-      }
-      if (next != live.size() || !open.empty())
-        return set_error(FM_E_UNSUPPORTED, "filters do not start in order");
-    }
-    while ((p.steps.size() - ws.step_off) % 8) p.steps.push_back(SweepStep{0.0f, 0.0f, 0, 0});
-    ws.nsteps = static_cast<int32_t>(p.steps.size()) - ws.step_off;
-    p.sweep[w] = ws;
   }
   return FM_OK;
 }

@@ -125,7 +125,9 @@ def test_center_false_and_general_power_and_slaney():
                   dict(n_fft=1024, hop_length=256, n_mels=80, power=1.5),
                   dict(n_fft=400, hop_length=160, n_mels=40, mel_scale="slaney", norm="slaney"),
                   dict(n_fft=400, hop_length=160, n_mels=60, f_min=125.0, f_max=7000.0),
-                  dict(n_fft=400, win_length=320, hop_length=160, n_mels=60)):
+                  dict(n_fft=400, win_length=320, hop_length=160, n_mels=60),
+                  dict(n_fft=2048, hop_length=512, n_mels=8),        # rows wider than 64 bins
+                  dict(n_fft=400, hop_length=160, n_mels=256)):
         assert_parity(run_gpu(x, sample_rate=16000, **targs), oracle(x, sample_rate=16000, **targs),
                       str(targs))
 

@@ -92,6 +92,57 @@ def test_csr_statistics_of_the_workloads():
         assert [m for m in range(inf.n_mels) if t["len"][m] == 0] == empty, name
 
 
+@pytest.mark.parametrize("name,over", [("tiny", {}), ("whisper", {}), ("pow2", {}), ("large", {}),
+                                       ("large", dict(n_mels=8)), ("whisper", dict(n_mels=256)),
+                                       ("whisper", dict(n_mels=37)),
+                                       ("whisper", dict(mel_scale="slaney", norm="slaney"))])
+def test_mel_blocks_equal_the_csr_filterbank(name, over):
+    """The kernel's mel layout (16-filter blocks, dense 4-bin steps in the
+    matrix-core lane order, split over 4 waves) holds exactly the CSR
+    weights, stays inside the bins, and covers every filter once."""
+    cfg = dict(W.WORKLOADS[name])
+    cfg.update(over)
+    p = host_plan(cfg)
+    t = p.tables()
+    blocks, wave_beg, wts = p.mel_blocks()
+    K = cfg["n_fft"] // 2 + 1
+    M = cfg["n_mels"]
+    nb = (M + 15) // 16
+    assert len(blocks) == nb and wave_beg[0] == 0 and wave_beg[4] == nb
+    assert all(wave_beg[w] <= wave_beg[w + 1] for w in range(4))
+    assert sorted(blocks[:, 3]) == list(range(0, 16 * nb, 16))
+    dense = np.zeros((M, K))
+    for kb, ks, off, mel0 in blocks:
+        assert ks % 4 == 0
+        assert 0 <= kb and (kb + 4 * ks <= K or (kb == 0 and 4 * ks <= K + 15))
+        for s_ in range(ks):
+            for lane in range(64):
+                m, k = mel0 + lane % 16, kb + 4 * s_ + lane // 16
+                v = wts[off + 64 * s_ + lane]
+                if m >= M or k >= K:
+                    assert v == 0.0
+                elif v != 0.0:
+                    assert dense[m, k] == 0.0
+                    dense[m, k] = v
+    assert len(wts) == 64 * blocks[:, 1].sum() and len(wts) % 256 == 0   # whole 1 KB copy chunks
+    # a wave's blocks are consecutive in the table
+    for w in range(4):
+        for j in range(wave_beg[w], wave_beg[w + 1] - 1):
+            assert blocks[j + 1, 2] == blocks[j, 2] + 64 * blocks[j, 1]
+    csr = np.zeros((M, K))
+    for m in range(M):
+        a, ln, o = t["first"][m], t["len"][m], t["off"][m]
+        csr[m, a:a + ln] = t["weights"][o:o + ln]
+    assert np.array_equal(dense, csr)
+    # the tile's LDS holds the power tile, its overrun and the weights
+    inf = p.info()
+    G = inf.tile_frames
+    assert inf.lds_bytes >= 4 * (-(-(G * K + 16) // 4) * 4 + len(wts))
+    # the waves' shares of 4-bin steps are balanced to within one block
+    cost = [sum(blocks[j, 1] + 2 for j in range(wave_beg[w], wave_beg[w + 1])) for w in range(4)]
+    assert max(cost) - min(cost) <= max(blocks[:, 1]) + 2
+
+
 @pytest.mark.parametrize("n_fft", [400, 1024, 2048])
 def test_twiddles(n_fft):
     p = N.Plan(device=False, sample_rate=16000, n_fft=n_fft, hop_length=n_fft // 4, n_mels=40)
