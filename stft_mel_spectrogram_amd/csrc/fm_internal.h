@@ -45,6 +45,18 @@ constexpr int kMelStageMinFrames = 33;
 // Staging floats per wave: 16 filters x (64 frames + 1 pad).
 constexpr int kMelStageFloats = 16 * 65;
 
+// LDS frame strides of a tile, padded against bank conflicts: the exchange
+// buffer Y holds each frame's n_fft/2 complex values at a stride of
+// n_fft/2 + kExchangePad, the power tile P each frame's n_fft/2 + 1 bins at
+// a stride of n_fft/2 + 1 + kPowerPad (the pad floats are kept at zero).
+// A pad of 4 complex values keeps rows 16-byte aligned (paired 64-bit LDS
+// accesses) and spreads the frames of a wave over the 64 banks; the odd
+// power-tile stride needs none.
+constexpr int kExchangePad = 4;
+constexpr int kPowerPad = 0;
+constexpr int exchange_stride(int half) { return half + kExchangePad; }
+constexpr int power_stride(int half) { return half + 1 + kPowerPad; }
+
 // FFT factorisation of the complex transform of n_fft/2 points that carries
 // the real FFT (even samples as real part, odd samples as imaginary part).
 struct FftShape {

@@ -15,8 +15,8 @@
 //           Z[M - k] in the same thread, so the split into the real spectrum
 //              X[k] = (Z[k] + conj Z[M-k]) - i W_N^k (Z[k] - conj Z[M-k])
 //           (window pre-scaled by 1/2) and |X|^p need no further exchange.
-// The power tile P[f][k] (odd row stride n_fft/2+1) reuses the exchange
-// buffer.  The mel projection is a block-sparse product on the matrix cores:
+// The power tile P[f][k] (odd frame stride n_fft/2+1) reuses the exchange
+// buffer (frame stride n_fft/2 + 4 complex values).  The mel projection is a block-sparse product on the matrix cores:
 // 16 filters x 16 frames per v_mfma_f32_16x16x4f32, over only the bins each
 // block of filters touches.
 #include <hip/hip_runtime.h>
@@ -67,14 +67,15 @@ using f32x4 = float __attribute__((ext_vector_type(4)));
 //   B (4 bins x 16 frames)   power tile, lane l: bin l/16, frame l%16;
 //   D (16 x 16)              lane l holds filters 4*(l/16) + r, r < 4, of
 //                            frame l%16.
-// Both operands come from LDS (the weights were copied there); blocks are
+// KS is the power tile's frame stride.  Both operands come from LDS (the
+// weights were copied there); blocks are
 // padded to whole groups of kMelStepGroup steps, so the step loop has no
 // tail.  Columns beyond the tile read its last frame and are not stored.
 // Output: with STAGE the 16 x 16*NFB result goes through the wave's LDS
 // staging area `stg` and each filter row leaves in one contiguous streaming
 // store (lane = frame); otherwise lanes store their D elements directly
 // (plain stores, so that L2 merges the 64-byte pieces of a row).
-template <int K, int NFB, bool STAGE>
+template <int KS, int NFB, bool STAGE>
 __device__ __forceinline__ void mel_blocks(const float* P, const float* WL, float* stg, int G,
                                            int nvalid, int lane, float* obase, int n_frames,
                                            int n_mels, CInt* blk, int bb, int be) {
@@ -82,7 +83,7 @@ __device__ __forceinline__ void mel_blocks(const float* P, const float* WL, floa
   const int fr = lane & 15, kq = lane >> 4;
   int roff[NFB];
 #pragma unroll
-  for (int f = 0; f < NFB; ++f) roff[f] = min(16 * f + fr, G - 1) * K + kq;
+  for (int f = 0; f < NFB; ++f) roff[f] = min(16 * f + fr, G - 1) * KS + kq;
   for (int bi = bb; bi < be; ++bi) {
     const int kb = blk[4 * bi], ks = blk[4 * bi + 1], woff = blk[4 * bi + 2],
               mel0 = blk[4 * bi + 3];
@@ -207,7 +208,9 @@ constexpr int kMinWavesPerSimd = (N1 * N2 <= 512) ? 2 : 1;
 template <int N1, int N2, typename InT, int PMODE>
 __global__ __launch_bounds__(256, (kMinWavesPerSimd<N1, N2>)) void mel_forward_kernel(KArgs a) {
   constexpr int M = N1 * N2;
-  constexpr int K = M + 1;        // one-sided bins; odd, so P rows are bank-skewed
+  constexpr int K = M + 1;        // one-sided bins
+  constexpr int SY = exchange_stride(M);  // LDS frame strides (padded)
+  constexpr int SP = power_stride(M);
   constexpr int NF = 2 * M;       // n_fft
   constexpr int NPAIR = N1 / 2;   // pass-2 threads per frame
   constexpr int SLOTS = 256 / N2; // frames per pass-1 round (one thread per n2)
@@ -284,7 +287,7 @@ __global__ __launch_bounds__(256, (kMinWavesPerSimd<N1, N2>)) void mel_forward_k
           v[n1] = make_float2(s[n1].x * w.x, s[n1].y * w.y);
         }
         Dft<N1>::run(v);
-        float2* yrow = Y + f * M + n2;
+        float2* yrow = Y + f * SY + n2;
         yrow[0] = v[0];
 #pragma unroll
         for (int k1 = 1; k1 < N1; ++k1)
@@ -337,8 +340,8 @@ __global__ __launch_bounds__(256, (kMinWavesPerSimd<N1, N2>)) void mel_forward_k
       }
       const int ka = p;
       const int kb = (p == 0) ? N1 / 2 : N1 - p;
-      const float2* ra = Y + f2 * M + ka * N2;
-      const float2* rb = Y + f2 * M + kb * N2;
+      const float2* ra = Y + f2 * SY + ka * N2;
+      const float2* rb = Y + f2 * SY + kb * N2;
 #pragma unroll
       for (int j = 0; j < N2; ++j) {
         za[j] = ra[j];
@@ -354,9 +357,15 @@ __global__ __launch_bounds__(256, (kMinWavesPerSimd<N1, N2>)) void mel_forward_k
     for (int c = wave; c < a.w_chunks; c += 4)
       __builtin_amdgcn_global_load_lds(a.blk_w + c * 256 + lane * 4, P + a.w_lds + c * 256, 16, 0, 0);
     // the mel stage may read a few floats past the power tile: keep them 0
-    if (tid < kMelTileOverrun) P[G * K + tid] = 0.0f;
+    if (tid < kMelTileOverrun) P[G * SP + tid] = 0.0f;
     if (has) {
-      float* prow = P + f2 * K;
+      float* prow = P + f2 * SP;
+      if constexpr (SP > K) {
+        if (p == 0) {
+#pragma unroll
+          for (int j = K; j < SP; ++j) prow[j] = 0.0f;  // row pad
+        }
+      }
       const float hp = a.half_power;
       // bin k = off + N1*k2 and its mirror M - k, as per-lane bases plus
       // compile-time (non-negative) offsets
@@ -400,7 +409,7 @@ __global__ __launch_bounds__(256, (kMinWavesPerSimd<N1, N2>)) void mel_forward_k
       static_assert(kMelStageMinFrames == 33, "staging is chosen for 3 and 4 column groups");
       switch (nfb) {
 #define FM_MEL_CALL(NFB, STAGE) \
-  mel_blocks<K, NFB, STAGE>(P, WL, stg, G, nvalid, lane, obase, a.n_frames, a.n_mels, blk, bb, be)
+  mel_blocks<SP, NFB, STAGE>(P, WL, stg, G, nvalid, lane, obase, a.n_frames, a.n_mels, blk, bb, be)
         case 1: FM_MEL_CALL(1, false); break;
         case 2: FM_MEL_CALL(2, false); break;
         case 3: FM_MEL_CALL(3, true); break;

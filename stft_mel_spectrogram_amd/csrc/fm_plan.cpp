@@ -82,15 +82,15 @@ std::string fmt(const char* what, double v) {
 }  // namespace
 
 int tile_exchange_bytes(const Plan& p, int frames) {
-  // complex exchange buffer Y[frames][n_fft/2]
-  const long y = static_cast<long>(std::max(frames, 1)) * (p.n_fft / 2) * 8;
+  // complex exchange buffer Y[frames][exchange_stride]
+  const long y = static_cast<long>(std::max(frames, 1)) * exchange_stride(p.n_fft / 2) * 8;
   return static_cast<int>((y + 15) / 16 * 16);
 }
 
 int tile_weights_offset(const Plan& p, int frames) {
-  // after the power tile P[frames][n_fft/2 + 1] and its zeroed overrun,
+  // after the power tile P[frames][power_stride] and its zeroed overrun,
   // 16-byte aligned
-  const long f = static_cast<long>(std::max(frames, 1)) * p.n_freqs + kMelTileOverrun;
+  const long f = static_cast<long>(std::max(frames, 1)) * power_stride(p.n_fft / 2) + kMelTileOverrun;
   return static_cast<int>((f + 3) / 4 * 4);
 }
 
