@@ -11,8 +11,9 @@ Prints ONE JSON line (rank 0, N = 1):
   value        mel frames per second over the K timed steps (events around
                the whole timed region, torch's current stream);
   roofline     achieved HBM GB/s of the kernel: algorithmic bytes (input +
-               output) / mean per-launch duration from event pairs around
-               each launch on the launch stream, against 8 TB/s;
+               output) / the average launch duration over the timed region
+               (events on the launch stream around K back-to-back launches),
+               against 8 TB/s;
   cpu_baseline the f64 oracle timed on this host on a bounded sample.
 """
 from __future__ import annotations
@@ -41,6 +42,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default="whisper", choices=sorted(W.WORKLOADS))
     ap.add_argument("--sets", type=int, default=0, help="rotating buffer sets (0: enough for 512 MB)")
+    ap.add_argument("--out-dtype", default="f32", choices=["f32", "f16"],
+                    help="output element type (f16: the f32 result rounded at the store)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-copy-probe", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle sample")
@@ -134,18 +137,19 @@ def main():
     x_np = W.make_signal(cfg)
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    mel = MelSpectrogram(device=dev, **W.transform_args(cfg))
+    out_dt = torch.float16 if args.out_dtype == "f16" else torch.float32
+    mel = MelSpectrogram(device=dev, out_dtype=out_dt, **W.transform_args(cfg))
     B, L = x_np.shape
     T = mel.out_frames(L)
     in_bytes = x_np.nbytes
-    out_bytes = B * cfg["n_mels"] * T * 4
+    out_bytes = B * cfg["n_mels"] * T * (2 if args.out_dtype == "f16" else 4)
     algo_bytes = in_bytes + out_bytes
     frames = B * T
 
     sets = args.sets or max(2, int(np.ceil(2 * 256e6 / algo_bytes)) + 1)
     x0 = torch.from_numpy(x_np).to(dev)
     xs = [x0] + [x0.clone() for _ in range(sets - 1)]
-    ys = [torch.empty((B, cfg["n_mels"], T), dtype=torch.float32, device=dev) for _ in range(sets)]
+    ys = [torch.empty((B, cfg["n_mels"], T), dtype=out_dt, device=dev) for _ in range(sets)]
     stream = torch.cuda.current_stream(dev)
 
     for i in range(args.warmup):
@@ -218,7 +222,8 @@ def main():
     if os.path.exists(args.traffic_json):
         try:
             t = json.load(open(args.traffic_json))
-            if t.get("workload") == cfg["name"] and t.get("kernel_sources_sha256_16") == kernel_sources_hash():
+            if (t.get("workload") == cfg["name"] and t.get("out_dtype", "f32") == args.out_dtype
+                    and t.get("kernel_sources_sha256_16") == kernel_sources_hash()):
                 traffic = t.get("bytes_per_launch")
         except Exception:
             traffic = None
@@ -234,11 +239,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "i16->f32" if cfg["dtype"] == "i16" else "f32",
+        "dtype": "f32",   # arithmetic type of the path; input/output types are in config
         "data": "synthetic (seeded; see workloads.py)",
         "config": {"workload": f"{cfg['name']}: {B}x{L} {cfg['dtype']}, n_fft={cfg['n_fft']} "
-                               f"hop={cfg['hop_length']} {cfg['n_mels']} mels, power={cfg['power']}",
+                               f"hop={cfg['hop_length']} {cfg['n_mels']} mels, power={cfg['power']}, "
+                               f"{args.out_dtype} out",
                    "batch": B, "length": L, "n_frames": T, "buffer_sets": sets,
+                   "in_dtype": cfg["dtype"], "out_dtype": args.out_dtype,
                    "parallelism": "single GPU"},
         "hbm_gbps_step": algo_bytes / (ms_per_step * 1e-3) / 1e9,
         "kernel_ms_mean": kern_ms,

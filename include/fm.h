@@ -50,12 +50,54 @@ extern "C" {
 #define FM_NORM_NONE 0
 #define FM_NORM_SLANEY 1
 
-/* input sample type (README "Usage": float32, or int16 raw PCM scaled by
- * 1/32768).                                                                */
+/* sample types: input float32 or int16 raw PCM scaled by 1/32768 (README
+ * "Usage"); output float32 or float16 (README "Usage" out_dtype: the f32
+ * result rounded to nearest at the store, beyond 65504 it becomes inf).    */
 #define FM_F32 0
 #define FM_I16 1
+#define FM_F16 2
+
+/* normalized: STFT normalisation folded into the window (flashmel/filters.py
+ * make_window): none, divide by sqrt(sum of the squared window), or divide
+ * by sqrt(win_length).                                                     */
+#define FM_NORMALIZED_NONE 0
+#define FM_NORMALIZED_WINDOW 1
+#define FM_NORMALIZED_FRAME_LENGTH 2
 
 typedef struct fm_plan fm_plan;
+
+/*
+ * fm_args -- every argument of a plan (torchaudio MelSpectrogram's, README
+ * "Usage", plus the output type).  Fill it with fm_args_default, which sets
+ * torchaudio's defaults for n_fft = 400 at 16 kHz, then change fields.
+ *   sample_rate, n_fft, win_length, hop_length, n_mels, f_min, f_max, power,
+ *   center, pad_mode, mel_scale, norm: as for fm_plan_create below;
+ *   pad        >= 0 zero samples added on both sides of the signal before the
+ *              centre padding (which then reflects / repeats / wraps the
+ *              zero-extended signal); at most 2^28;
+ *   normalized FM_NORMALIZED_*;
+ *   out_dtype  FM_F32 or FM_F16: the element type fm_forward writes.
+ */
+typedef struct fm_args {
+  int sample_rate, n_fft, win_length, hop_length, n_mels;
+  double f_min, f_max, power;
+  int center, pad_mode, mel_scale, norm;
+  int pad, normalized, out_dtype;
+} fm_args;
+
+/* sample_rate 16000, n_fft 400, win_length 400, hop_length 200, n_mels 128,
+ * f_min 0, f_max 8000, power 2, center 1, reflect, HTK, no norm, pad 0, not
+ * normalized, f32 output.  FM_E_INVAL if args is NULL.                      */
+int fm_args_default(fm_args* args);
+
+/*
+ * fm_plan_create_args / fm_plan_create_args_host -- fm_plan_create and
+ * fm_plan_create_host with every argument in one struct (read, not kept).
+ * Same ownership, validation and errors; a plan made with out_dtype FM_F16
+ * writes float16 from fm_forward.
+ */
+int fm_plan_create_args(fm_plan** out, const fm_args* args);
+int fm_plan_create_args_host(fm_plan** out, const fm_args* args);
 
 /*
  * fm_plan_create -- build a plan on the CURRENT HIP device.
@@ -100,24 +142,26 @@ int fm_plan_create_host(fm_plan** out, int sample_rate, int n_fft,
  *
  *   in     device pointer to [batch, length] samples, row-major, contiguous,
  *          of type in_dtype (FM_F32: float, FM_I16: int16_t).
- *   out    device pointer to [batch, n_mels, n_frames] float32, row-major,
+ *   out    device pointer to [batch, n_mels, n_frames] elements of the plan's
+ *          out_dtype (float32 unless made with FM_F16: float16), row-major,
  *          contiguous (frames fastest), n_frames = fm_out_frames(plan,
- *          length).  Every element is written.
+ *          length), aligned to its element size.  Every element is written.
  *   batch  >= 0 (0 is a no-op); length >= 1, and with center + reflect
- *          padding length > n_fft/2 (a single reflection), otherwise
- *          FM_E_INVAL; without center length >= n_fft.
+ *          padding length + 2*pad > n_fft/2 (a single reflection), with
+ *          circular padding length + 2*pad >= n_fft/2, otherwise FM_E_INVAL;
+ *          without center length + 2*pad >= n_fft.
  *
  * One kernel launch; no allocation, no synchronisation.  Launch errors are
  * reported as FM_E_HIP.  The plan must live on the device that is current.
  */
 int fm_forward(const fm_plan* plan, const void* in, int in_dtype,
-               int64_t batch, int64_t length, float* out, void* stream);
+               int64_t batch, int64_t length, void* out, void* stream);
 
 /*
- * fm_out_frames -- frames per signal for a given length:
- *   center: 1 + floor(length / hop) for even n_fft (generally
- *           1 + floor((length + 2*(n_fft/2) - n_fft) / hop));
- *   else:   1 + floor((length - n_fft) / hop).
+ * fm_out_frames -- frames per signal for a given length (L = length + 2*pad):
+ *   center: 1 + floor(L / hop) for even n_fft (generally
+ *           1 + floor((L + 2*(n_fft/2) - n_fft) / hop));
+ *   else:   1 + floor((L - n_fft) / hop).
  * Returns a negative FM_E_* code if the length is invalid for the plan.
  */
 int64_t fm_out_frames(const fm_plan* plan, int64_t length);
@@ -135,6 +179,7 @@ const char* fm_last_error(void);
 
 typedef struct fm_plan_info {
   int n_fft, win_length, hop_length, n_mels, n_freqs; /* n_freqs = n_fft/2+1 */
+  int pad, normalized, out_dtype;
   int nnz;          /* nonzero filterbank weights (CSR length)              */
   int w_max;        /* widest filter (bins)                                 */
   int fft_n1, fft_n2; /* complex FFT of n_fft/2 = fft_n1 * fft_n2 points    */
@@ -148,8 +193,9 @@ int fm_plan_info_get(const fm_plan* plan, fm_plan_info* info);
 
 /*
  * fm_plan_tables -- copy the host tables of a plan.  Any pointer may be NULL
- * to skip that table.  Sizes: window[n_fft] (float32, unscaled; the device
- * copy is scaled by 1/2 for the real-FFT post-processing);
+ * to skip that table.  Sizes: window[n_fft] (float32, with the plan's
+ * normalisation; the device copy is further scaled by 1/2 for the real-FFT
+ * post-processing);
  * mel_first[n_mels], mel_len[n_mels], mel_off[n_mels] (int32; CSR rows,
  * len 0 for an empty filter); mel_w[nnz] (float32);
  * tw_m[2*(n_fft/2)] interleaved re,im of exp(-2*pi*i*j/(n_fft/2));

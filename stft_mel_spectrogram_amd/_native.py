@@ -24,6 +24,9 @@ FM_MEL = {"htk": 0, "slaney": 1}
 FM_NORM = {None: 0, "slaney": 1}
 FM_F32 = 0
 FM_I16 = 1
+FM_F16 = 2
+FM_NORMALIZED = {False: 0, None: 0, True: 1, "window": 1, "frame_length": 2}
+FM_OUT = {"f32": FM_F32, "f16": FM_F16}
 
 
 class FmError(RuntimeError):
@@ -36,8 +39,18 @@ class FmError(RuntimeError):
 
 class PlanInfo(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in (
-        "n_fft", "win_length", "hop_length", "n_mels", "n_freqs", "nnz", "w_max",
-        "fft_n1", "fft_n2", "tile_frames", "threads", "lds_bytes", "has_device")]
+        "n_fft", "win_length", "hop_length", "n_mels", "n_freqs", "pad", "normalized",
+        "out_dtype", "nnz", "w_max", "fft_n1", "fft_n2", "tile_frames", "threads", "lds_bytes",
+        "has_device")]
+
+
+class Args(ctypes.Structure):
+    """fm_args of include/fm.h."""
+    _fields_ = ([(n, ctypes.c_int) for n in ("sample_rate", "n_fft", "win_length", "hop_length",
+                                              "n_mels")] +
+                [(n, ctypes.c_double) for n in ("f_min", "f_max", "power")] +
+                [(n, ctypes.c_int) for n in ("center", "pad_mode", "mel_scale", "norm", "pad",
+                                              "normalized", "out_dtype")])
 
 
 def _load() -> ctypes.CDLL:
@@ -53,6 +66,9 @@ def _load() -> ctypes.CDLL:
     sigs = {
         "fm_plan_create": (I, create_args),
         "fm_plan_create_host": (I, create_args),
+        "fm_args_default": (I, [ctypes.POINTER(Args)]),
+        "fm_plan_create_args": (I, [ctypes.POINTER(P), ctypes.POINTER(Args)]),
+        "fm_plan_create_args_host": (I, [ctypes.POINTER(P), ctypes.POINTER(Args)]),
         "fm_forward": (I, [P, P, I, I64, I64, P, P]),
         "fm_out_frames": (I64, [P, I64]),
         "fm_plan_destroy": (I, [P]),
@@ -85,7 +101,8 @@ class Plan:
 
     def __init__(self, *, sample_rate=16000, n_fft=400, win_length=None, hop_length=None,
                  n_mels=128, f_min=0.0, f_max=None, power=2.0, center=True,
-                 pad_mode="reflect", mel_scale="htk", norm=None, device=True):
+                 pad_mode="reflect", mel_scale="htk", norm=None, pad=0, normalized=False,
+                 out_dtype="f32", device=True):
         win_length = n_fft if win_length is None else int(win_length)
         hop_length = win_length // 2 if hop_length is None else int(hop_length)
         f_max = float(sample_rate // 2) if f_max is None else float(f_max)
@@ -95,15 +112,28 @@ class Plan:
             raise ValueError(f"unknown mel_scale {mel_scale!r}")
         if norm not in FM_NORM:
             raise ValueError(f"unknown norm {norm!r}")
+        if not any(normalized is k or (isinstance(k, str) and normalized == k)
+                   for k in FM_NORMALIZED):
+            raise ValueError(f"unknown normalized {normalized!r}")
+        if out_dtype not in FM_OUT:
+            raise ValueError(f"out_dtype must be 'f32' or 'f16', got {out_dtype!r}")
+        a = Args()
+        check(lib.fm_args_default(ctypes.byref(a)))
+        a.sample_rate, a.n_fft, a.win_length, a.hop_length = (int(sample_rate), int(n_fft),
+                                                                win_length, hop_length)
+        a.n_mels, a.f_min, a.f_max, a.power = int(n_mels), float(f_min), f_max, float(power)
+        a.center, a.pad_mode = int(bool(center)), FM_PAD[pad_mode]
+        a.mel_scale, a.norm = FM_MEL[mel_scale], FM_NORM[norm]
+        a.pad = int(pad)
+        a.normalized = FM_NORMALIZED[normalized if not isinstance(normalized, bool) else bool(normalized)]
+        a.out_dtype = FM_OUT[out_dtype]
         self._h = ctypes.c_void_p()
-        fn = lib.fm_plan_create if device else lib.fm_plan_create_host
-        check(fn(ctypes.byref(self._h), int(sample_rate), int(n_fft), win_length, hop_length,
-                 int(n_mels), float(f_min), f_max, float(power), int(bool(center)),
-                 FM_PAD[pad_mode], FM_MEL[mel_scale], FM_NORM[norm]))
+        fn = lib.fm_plan_create_args if device else lib.fm_plan_create_args_host
+        check(fn(ctypes.byref(self._h), ctypes.byref(a)))
         self.args = dict(sample_rate=sample_rate, n_fft=n_fft, win_length=win_length,
                          hop_length=hop_length, n_mels=n_mels, f_min=f_min, f_max=f_max,
                          power=power, center=center, pad_mode=pad_mode, mel_scale=mel_scale,
-                         norm=norm)
+                         norm=norm, pad=pad, normalized=normalized, out_dtype=out_dtype)
 
     @property
     def handle(self) -> ctypes.c_void_p:

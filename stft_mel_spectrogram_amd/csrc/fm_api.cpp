@@ -26,15 +26,13 @@ const char* last_error_cstr() { return g_last_error.c_str(); }
 
 namespace {
 
-int create(fm_plan** out, bool with_device, int sample_rate, int n_fft, int win_length,
-           int hop_length, int n_mels, double f_min, double f_max, double power, int center,
-           int pad_mode, int mel_scale, int norm) {
+int create(fm_plan** out, bool with_device, const fm_args* a) {
   if (!out) return fm::set_error(FM_E_INVAL, "out must not be NULL");
   *out = nullptr;
+  if (!a) return fm::set_error(FM_E_INVAL, "args must not be NULL");
   fm_plan* h = new (std::nothrow) fm_plan();
   if (!h) return fm::set_error(FM_E_NOMEM, "host allocation failed");
-  int st = fm::build_host_plan(h->p, sample_rate, n_fft, win_length, hop_length, n_mels, f_min,
-                               f_max, power, center, pad_mode, mel_scale, norm);
+  int st = fm::build_host_plan(h->p, *a);
   if (st == FM_OK && with_device) st = fm::upload_plan(h->p);
   if (st != FM_OK) {
     fm::free_plan_device(h->p);
@@ -45,26 +43,60 @@ int create(fm_plan** out, bool with_device, int sample_rate, int n_fft, int win_
   return FM_OK;
 }
 
+fm_args positional(int sample_rate, int n_fft, int win_length, int hop_length, int n_mels,
+                   double f_min, double f_max, double power, int center, int pad_mode,
+                   int mel_scale, int norm) {
+  fm_args a;
+  fm::default_args(&a);
+  a.sample_rate = sample_rate;
+  a.n_fft = n_fft;
+  a.win_length = win_length;
+  a.hop_length = hop_length;
+  a.n_mels = n_mels;
+  a.f_min = f_min;
+  a.f_max = f_max;
+  a.power = power;
+  a.center = center;
+  a.pad_mode = pad_mode;
+  a.mel_scale = mel_scale;
+  a.norm = norm;
+  return a;
+}
+
 }  // namespace
 
 extern "C" {
 
+int fm_args_default(fm_args* args) {
+  if (!args) return fm::set_error(FM_E_INVAL, "args must not be NULL");
+  fm::default_args(args);
+  return FM_OK;
+}
+
+int fm_plan_create_args(fm_plan** out, const fm_args* args) { return create(out, true, args); }
+
+int fm_plan_create_args_host(fm_plan** out, const fm_args* args) {
+  return create(out, false, args);
+}
+
 int fm_plan_create(fm_plan** out, int sample_rate, int n_fft, int win_length, int hop_length,
                    int n_mels, double f_min, double f_max, double power, int center, int pad_mode,
                    int mel_scale, int norm) {
-  return create(out, true, sample_rate, n_fft, win_length, hop_length, n_mels, f_min, f_max,
-                power, center, pad_mode, mel_scale, norm);
+  const fm_args a = positional(sample_rate, n_fft, win_length, hop_length, n_mels, f_min, f_max,
+                              power, center, pad_mode, mel_scale, norm);
+  return create(out, true, &a);
 }
 
 int fm_plan_create_host(fm_plan** out, int sample_rate, int n_fft, int win_length,
                         int hop_length, int n_mels, double f_min, double f_max, double power,
                         int center, int pad_mode, int mel_scale, int norm) {
-  return create(out, false, sample_rate, n_fft, win_length, hop_length, n_mels, f_min, f_max,
-                power, center, pad_mode, mel_scale, norm);
+  const fm_args a = positional(sample_rate, n_fft, win_length, hop_length, n_mels, f_min, f_max,
+                              power, center, pad_mode, mel_scale, norm);
+  return create(out, false, &a);
 }
 
 int fm_forward(const fm_plan* plan, const void* in, int in_dtype, int64_t batch, int64_t length,
-               float* out, void* stream) {
+               void* out, void* stream) {
   if (!plan) return fm::set_error(FM_E_INVAL, "plan must not be NULL");
   return fm::launch_forward(plan->p, in, in_dtype, batch, length, out, stream);
 }
@@ -103,6 +135,9 @@ int fm_plan_info_get(const fm_plan* plan, fm_plan_info* info) {
   info->hop_length = p.hop;
   info->n_mels = p.n_mels;
   info->n_freqs = p.n_freqs;
+  info->pad = p.zpad;
+  info->normalized = p.normalized;
+  info->out_dtype = p.out_dtype;
   info->nnz = p.nnz;
   info->w_max = p.w_max;
   info->fft_n1 = p.fft.n1;

@@ -68,6 +68,9 @@ struct Plan {
   int sample_rate = 0, n_fft = 0, win_length = 0, hop = 0, n_mels = 0;
   double f_min = 0, f_max = 0, power = 2.0;
   int center = 1, pad_mode = FM_PAD_REFLECT, mel_scale = FM_MEL_HTK, norm = FM_NORM_NONE;
+  int zpad = 0;                          // zero samples added on both sides
+  int normalized = FM_NORMALIZED_NONE;
+  int out_dtype = FM_F32;
   // derived
   int n_freqs = 0;     // n_fft/2 + 1
   int pad_left = 0;    // samples of centre padding on each side
@@ -106,10 +109,8 @@ int set_error(int code, const std::string& msg);
 const char* last_error_cstr();
 
 // Builds every host table and the tile geometry; touches no GPU.
-int build_host_plan(Plan& p, int sample_rate, int n_fft, int win_length,
-                    int hop_length, int n_mels, double f_min, double f_max,
-                    double power, int center, int pad_mode, int mel_scale,
-                    int norm);
+int build_host_plan(Plan& p, const fm_args& a);
+void default_args(fm_args* a);
 
 // LDS layout of a tile of `frames` frames: the FFT exchange buffer, which
 // later holds the power tile, its zeroed overrun floats, (from float
@@ -126,6 +127,6 @@ int64_t out_frames(const Plan& p, int64_t length);
 int upload_plan(Plan& p);
 void free_plan_device(Plan& p);
 int launch_forward(const Plan& p, const void* in, int in_dtype, int64_t batch,
-                   int64_t length, float* out, void* stream);
+                   int64_t length, void* out, void* stream);
 
 }  // namespace fm

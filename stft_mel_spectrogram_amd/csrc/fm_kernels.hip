@@ -33,14 +33,16 @@ namespace {
 
 struct KArgs {
   const void* in;
-  float* out;
+  void* out;            // [B, n_mels, n_frames] float or _Float16
   const float2* win2;   // [M]  0.5*(w[2m], w[2m+1])
   const float2* tw_m;   // [M]  exp(-2 pi i j / M)
   const float2* tw_n;   // [M]  exp(-2 pi i k / N)
   long long length;     // samples per signal
   int n_frames;         // frames per signal
   int hop;
-  int pad;              // left padding (n_fft/2 with centring, else 0)
+  int pad;              // first frame's offset before sample 0: centre padding
+                        // (n_fft/2, or 0) + zero padding
+  int zpad;             // zero samples added on both sides of the signal
   int n_mels;
   int tile;             // frames per workgroup tile (<= 64)
   int tiles_per_signal;
@@ -51,6 +53,7 @@ struct KArgs {
   const float* blk_w;   // block weights, 64 per 4-bin step (MFMA A-operand order)
   int w_chunks;         // block weights / 256 (copied to LDS in 1 KB chunks)
   int w_lds;            // LDS float offset of the copied weights
+  int out_f16;          // 1: the output is float16
 };
 
 // Tables read with wave-uniform indices are reached through the constant
@@ -71,13 +74,14 @@ using f32x4 = float __attribute__((ext_vector_type(4)));
 // weights were copied there); blocks are
 // padded to whole groups of kMelStepGroup steps, so the step loop has no
 // tail.  Columns beyond the tile read its last frame and are not stored.
-// Output: with STAGE the 16 x 16*NFB result goes through the wave's LDS
-// staging area `stg` and each filter row leaves in one contiguous streaming
-// store (lane = frame); otherwise lanes store their D elements directly
-// (plain stores, so that L2 merges the 64-byte pieces of a row).
-template <int KS, int NFB, bool STAGE>
+// Output (element type OT: float, or _Float16 rounded to nearest): with
+// STAGE the 16 x 16*NFB result goes through the wave's LDS staging area
+// `stg` and each filter row leaves in one contiguous streaming store (lane =
+// frame); otherwise lanes store their D elements directly (plain stores, so
+// that L2 merges the pieces of a row).
+template <int KS, int NFB, bool STAGE, typename OT>
 __device__ __forceinline__ void mel_blocks(const float* P, const float* WL, float* stg, int G,
-                                           int nvalid, int lane, float* obase, int n_frames,
+                                           int nvalid, int lane, OT* obase, int n_frames,
                                            int n_mels, CInt* blk, int bb, int be) {
   constexpr int U = kMelStepGroup;
   const int fr = lane & 15, kq = lane >> 4;
@@ -121,7 +125,7 @@ __device__ __forceinline__ void mel_blocks(const float* P, const float* WL, floa
       for (int m = 0; m < nrow; ++m) {
         const float v = stg[m * PITCH + lane];
         // output is written once and never re-read here: streaming stores
-        if (st) __builtin_nontemporal_store(v, obase + static_cast<long long>(mel0 + m) * n_frames + lane);
+        if (st) __builtin_nontemporal_store(static_cast<OT>(v), obase + static_cast<long long>(mel0 + m) * n_frames + lane);
       }
       __builtin_amdgcn_s_waitcnt(0xC07F);  // reads done before the next block's writes
       __builtin_amdgcn_wave_barrier();
@@ -133,17 +137,17 @@ __device__ __forceinline__ void mel_blocks(const float* P, const float* WL, floa
         if (frame < nvalid) {
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            if (mrow + r < n_mels) obase[static_cast<long long>(mrow + r) * n_frames + frame] = acc[f][r];
+            if (mrow + r < n_mels) obase[static_cast<long long>(mrow + r) * n_frames + frame] = static_cast<OT>(acc[f][r]);
         }
       }
     }
   }
 }
 
-// Source index of position i of the padded signal (i relative to sample 0),
-// or -1 for a constant-zero position.  The host guarantees that frames
-// reach at most one signal length beyond either end, so one reflection or
-// wrap suffices; all indices fit in 32 bits.
+// Source index of position i of the centre-padded signal (i relative to
+// sample 0 of a signal of L samples), or -1 for a constant-zero position.
+// The host guarantees that frames reach at most one signal length beyond
+// either end, so one reflection or wrap suffices; all indices fit in 32 bits.
 __device__ __forceinline__ int padded_index(int i, int L, int mode) {
   if (static_cast<unsigned>(i) < static_cast<unsigned>(L)) return i;
   switch (mode) {
@@ -165,11 +169,16 @@ __device__ __forceinline__ float2 load_pair_raw(const int16_t* x, int i) {
   const short2 v = *reinterpret_cast<const short2*>(x + i);
   return make_float2(static_cast<float>(v.x), static_cast<float>(v.y));
 }
+// Sample at position i (relative to x[0]) of the signal first extended by
+// zpad zeros on both sides, then centre-padded in `mode` (the centre padding
+// reflects, repeats or wraps the zero-extended signal).
 template <typename T>
-__device__ __forceinline__ float padded_sample_raw(const T* x, int i, int L, int mode) {
-  const int j = padded_index(i, L, mode);
-  if constexpr (std::is_same<T, int16_t>::value) return j < 0 ? 0.0f : static_cast<float>(x[j]);
-  else return j < 0 ? 0.0f : x[j];
+__device__ __forceinline__ float padded_sample_raw(const T* x, int i, int L, int zpad, int mode) {
+  const int e = padded_index(i + zpad, L + 2 * zpad, mode);
+  const int j = e - zpad;
+  if (e < 0 || static_cast<unsigned>(j) >= static_cast<unsigned>(L)) return 0.0f;
+  if constexpr (std::is_same<T, int16_t>::value) return static_cast<float>(x[j]);
+  else return x[j];
 }
 template <typename T>
 constexpr float kSampleScale = std::is_same<T, int16_t>::value ? (1.0f / 32768.0f) : 1.0f;
@@ -268,8 +277,8 @@ __global__ __launch_bounds__(256, (kMinWavesPerSimd<N1, N2>)) void mel_forward_k
 #pragma unroll
           for (int n1 = 0; n1 < N1; ++n1) {
             const int i = base + 2 * (N2 * n1 + n2);
-            s[n1] = make_float2(padded_sample_raw(x, i, L, a.pad_mode),
-                                padded_sample_raw(x, i + 1, L, a.pad_mode));
+            s[n1] = make_float2(padded_sample_raw(x, i, L, a.zpad, a.pad_mode),
+                                padded_sample_raw(x, i + 1, L, a.zpad, a.pad_mode));
           }
         }
       };
@@ -401,15 +410,22 @@ __global__ __launch_bounds__(256, (kMinWavesPerSimd<N1, N2>)) void mel_forward_k
     {
       CInt* tbl = (CInt*)(a.mel_tbl);  // address-space cast: scalar loads
       const int bb = tbl[wave], be = tbl[wave + 1];
-      float* obase = a.out + static_cast<long long>(b) * a.n_mels * a.n_frames + t0;
+      const long long obase = static_cast<long long>(b) * a.n_mels * a.n_frames + t0;  // element offset
       const int nfb = (G + 15) >> 4;
       CInt* blk = tbl + 8;
       const float* WL = P + a.w_lds;
       float* stg = P + a.w_lds + a.w_chunks * 256 + wave * kMelStageFloats;
       static_assert(kMelStageMinFrames == 33, "staging is chosen for 3 and 4 column groups");
       switch (nfb) {
-#define FM_MEL_CALL(NFB, STAGE) \
-  mel_blocks<SP, NFB, STAGE>(P, WL, stg, G, nvalid, lane, obase, a.n_frames, a.n_mels, blk, bb, be)
+#define FM_MEL_CALL(NFB, STAGE)                                                                \
+  if (a.out_f16)                                                                              \
+    mel_blocks<SP, NFB, STAGE, _Float16>(P, WL, stg, G, nvalid, lane,                          \
+                                         static_cast<_Float16*>(a.out) + obase, a.n_frames,   \
+                                         a.n_mels, blk, bb, be);                              \
+  else                                                                                        \
+    mel_blocks<SP, NFB, STAGE, float>(P, WL, stg, G, nvalid, lane,                            \
+                                      static_cast<float*>(a.out) + obase, a.n_frames, a.n_mels, \
+                                      blk, bb, be)
         case 1: FM_MEL_CALL(1, false); break;
         case 2: FM_MEL_CALL(2, false); break;
         case 3: FM_MEL_CALL(3, true); break;
@@ -547,7 +563,7 @@ int choose_tile(const Plan& p, int64_t batch, int64_t T) {
 }  // namespace
 
 int launch_forward(const Plan& p, const void* in, int in_dtype, int64_t batch, int64_t length,
-                   float* out, void* stream) {
+                   void* out, void* stream) {
   if (!p.has_device) return set_error(FM_E_NODEVICE, "plan was built without device tables");
   if (in_dtype != FM_F32 && in_dtype != FM_I16) return set_error(FM_E_INVAL, "in_dtype must be FM_F32 or FM_I16");
   if (batch < 0) return set_error(FM_E_INVAL, "batch must be >= 0");
@@ -575,7 +591,8 @@ int launch_forward(const Plan& p, const void* in, int in_dtype, int64_t batch, i
   a.length = length;
   a.n_frames = static_cast<int>(T);
   a.hop = p.hop;
-  a.pad = p.pad_left;
+  a.pad = p.pad_left + p.zpad;
+  a.zpad = p.zpad;
   a.n_mels = p.n_mels;
   a.tile = G;
   a.tiles_per_signal = static_cast<int>(tiles);
@@ -583,11 +600,13 @@ int launch_forward(const Plan& p, const void* in, int in_dtype, int64_t batch, i
   a.half_power = static_cast<float>(p.power * 0.5);
   const size_t esz = (in_dtype == FM_I16) ? 2 : 4;
   const uintptr_t ia = reinterpret_cast<uintptr_t>(in);
-  a.vec_ok = (ia % (2 * esz) == 0) && (length % 2 == 0) && (p.hop % 2 == 0) && (p.pad_left % 2 == 0);
+  a.vec_ok = (ia % (2 * esz) == 0) && (length % 2 == 0) && (p.hop % 2 == 0) &&
+             ((p.pad_left + p.zpad) % 2 == 0);
   a.mel_tbl = static_cast<const int*>(p.d_mel_tbl);
   a.blk_w = static_cast<const float*>(p.d_blk_w);
   a.w_chunks = static_cast<int>(p.blk_w.size() / 256);
   a.w_lds = tile_weights_offset(p, G);
+  a.out_f16 = p.out_dtype == FM_F16 ? 1 : 0;
 
   void* k = select_kernel(p, in_dtype);
   if (!k) return set_error(FM_E_UNSUPPORTED, "no kernel for this n_fft");

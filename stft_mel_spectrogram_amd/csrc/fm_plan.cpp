@@ -103,24 +103,45 @@ int tile_lds_bytes(const Plan& p, int frames) {
 
 int64_t out_frames(const Plan& p, int64_t length) {
   if (length < 1) return set_error(FM_E_INVAL, "length must be >= 1");
+  const int64_t le = length + 2 * static_cast<int64_t>(p.zpad);  // zero-extended signal
   if (p.center) {
-    if (p.pad_mode == FM_PAD_REFLECT && length <= p.pad_left)
+    if (p.pad_mode == FM_PAD_REFLECT && le <= p.pad_left)
       return set_error(FM_E_INVAL,
-                       "reflect padding needs length > n_fft/2 (one reflection)");
-    if (p.pad_mode == FM_PAD_CIRCULAR && length < p.pad_left)
-      return set_error(FM_E_INVAL, "circular padding needs length >= n_fft/2 (one wrap)");
-    int64_t lp = length + 2 * static_cast<int64_t>(p.pad_left);
+                       "reflect padding needs length + 2*pad > n_fft/2 (one reflection)");
+    if (p.pad_mode == FM_PAD_CIRCULAR && le < p.pad_left)
+      return set_error(FM_E_INVAL, "circular padding needs length + 2*pad >= n_fft/2 (one wrap)");
+    int64_t lp = le + 2 * static_cast<int64_t>(p.pad_left);
     if (lp < p.n_fft) return set_error(FM_E_INVAL, "signal shorter than one frame");
     return 1 + (lp - p.n_fft) / p.hop;
   }
-  if (length < p.n_fft) return set_error(FM_E_INVAL, "length < n_fft without centring");
-  return 1 + (length - p.n_fft) / p.hop;
+  if (le < p.n_fft) return set_error(FM_E_INVAL, "length + 2*pad < n_fft without centring");
+  return 1 + (le - p.n_fft) / p.hop;
 }
 
-int build_host_plan(Plan& p, int sample_rate, int n_fft, int win_length,
-                    int hop_length, int n_mels, double f_min, double f_max,
-                    double power, int center, int pad_mode, int mel_scale,
-                    int norm) {
+void default_args(fm_args* a) {
+  *a = fm_args{};
+  a->sample_rate = 16000;
+  a->n_fft = 400;
+  a->win_length = 400;
+  a->hop_length = 200;
+  a->n_mels = 128;
+  a->f_min = 0.0;
+  a->f_max = 8000.0;
+  a->power = 2.0;
+  a->center = 1;
+  a->pad_mode = FM_PAD_REFLECT;
+  a->mel_scale = FM_MEL_HTK;
+  a->norm = FM_NORM_NONE;
+  a->pad = 0;
+  a->normalized = FM_NORMALIZED_NONE;
+  a->out_dtype = FM_F32;
+}
+
+int build_host_plan(Plan& p, const fm_args& a) {
+  const int sample_rate = a.sample_rate, n_fft = a.n_fft, win_length = a.win_length;
+  const int hop_length = a.hop_length, n_mels = a.n_mels, center = a.center;
+  const int pad_mode = a.pad_mode, mel_scale = a.mel_scale, norm = a.norm;
+  const double f_min = a.f_min, f_max = a.f_max, power = a.power;
   // ---- validation (all host-side integer / float checks) ------------------
   if (sample_rate <= 0) return set_error(FM_E_INVAL, fmt("sample_rate must be > 0", sample_rate));
   if (n_fft <= 0) return set_error(FM_E_INVAL, fmt("n_fft must be > 0", n_fft));
@@ -141,6 +162,11 @@ int build_host_plan(Plan& p, int sample_rate, int n_fft, int win_length,
     return set_error(FM_E_INVAL, fmt("unknown mel_scale", mel_scale));
   if (norm != FM_NORM_NONE && norm != FM_NORM_SLANEY)
     return set_error(FM_E_INVAL, fmt("unknown norm", norm));
+  if (a.pad < 0 || a.pad > (1 << 28)) return set_error(FM_E_INVAL, fmt("need 0 <= pad <= 2^28", a.pad));
+  if (a.normalized < FM_NORMALIZED_NONE || a.normalized > FM_NORMALIZED_FRAME_LENGTH)
+    return set_error(FM_E_INVAL, fmt("unknown normalized", a.normalized));
+  if (a.out_dtype != FM_F32 && a.out_dtype != FM_F16)
+    return set_error(FM_E_INVAL, fmt("out_dtype must be FM_F32 or FM_F16", a.out_dtype));
   if (n_mels > 256) return set_error(FM_E_UNSUPPORTED, fmt("n_mels > 256 is not supported", n_mels));
   FftShape fs;
   if (!fft_shape_for(n_fft, &fs))
@@ -150,19 +176,28 @@ int build_host_plan(Plan& p, int sample_rate, int n_fft, int win_length,
   p.hop = hop_length; p.n_mels = n_mels; p.f_min = f_min; p.f_max = f_max;
   p.power = power; p.center = center; p.pad_mode = pad_mode;
   p.mel_scale = mel_scale; p.norm = norm;
+  p.zpad = a.pad; p.normalized = a.normalized; p.out_dtype = a.out_dtype;
   p.n_freqs = n_fft / 2 + 1;
   p.pad_left = center ? n_fft / 2 : 0;
   p.fft = fs;
   const int M = n_fft / 2;
 
-  // ---- window: periodic Hann of win_length, centred in n_fft --------------
+  // ---- window: periodic Hann of win_length, centred in n_fft, with the
+  //      STFT normalisation folded in (flashmel/filters.py make_window) -----
   p.window.assign(n_fft, 0.0f);
   const int left = (n_fft - win_length) / 2;
+  std::vector<double> wd(win_length);
+  double sum_sq = 0.0;
   for (int n = 0; n < win_length; ++n) {
     double c, s;
     cos_sin_2pi(n, win_length, &c, &s);
-    p.window[left + n] = static_cast<float>(0.5 - 0.5 * c);
+    wd[n] = 0.5 - 0.5 * c;
+    sum_sq += wd[n] * wd[n];
   }
+  double wscale = 1.0;
+  if (a.normalized == FM_NORMALIZED_WINDOW) wscale = 1.0 / std::sqrt(sum_sq);
+  if (a.normalized == FM_NORMALIZED_FRAME_LENGTH) wscale = 1.0 / std::sqrt(static_cast<double>(win_length));
+  for (int n = 0; n < win_length; ++n) p.window[left + n] = static_cast<float>(wd[n] * wscale);
 
   // ---- mel filterbank: triangles on the mel scale, CSR rows ---------------
   std::vector<double> fpts(n_mels + 2);

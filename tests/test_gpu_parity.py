@@ -132,6 +132,77 @@ def test_center_false_and_general_power_and_slaney():
                       str(targs))
 
 
+@pytest.mark.parametrize("pad", [1, 3, 160, 999])
+@pytest.mark.parametrize("pad_mode", ["reflect", "constant", "replicate", "circular"])
+def test_zero_pad_argument(pad, pad_mode):
+    """`pad` zeros on both sides, then centre padding of the zero-extended
+    signal (odd pads take the unpaired-load path)."""
+    x = np.random.default_rng(pad).standard_normal((2, 4321)).astype(np.float32)
+    targs = dict(sample_rate=16000, n_fft=400, hop_length=160, n_mels=64, pad=pad, pad_mode=pad_mode)
+    assert_parity(run_gpu(x, **targs), oracle(x, **targs), f"pad={pad} {pad_mode}")
+
+
+def test_zero_pad_short_signal_and_no_centring():
+    x = np.random.default_rng(11).standard_normal((3, 150)).astype(np.float32)
+    for targs in (dict(n_fft=400, hop_length=160, n_mels=40, pad=60),     # 150 < 200 < 270
+                  dict(n_fft=400, hop_length=100, n_mels=40, pad=200, center=False),
+                  dict(n_fft=1024, hop_length=256, n_mels=80, pad=700)):
+        assert_parity(run_gpu(x, sample_rate=16000, **targs), oracle(x, sample_rate=16000, **targs),
+                      str(targs))
+
+
+@pytest.mark.parametrize("normalized", [True, "frame_length"])
+@pytest.mark.parametrize("n_fft,win", [(400, 400), (400, 320), (1024, 1000)])
+def test_normalized_window(normalized, n_fft, win):
+    x = np.random.default_rng(win).standard_normal((2, 8000)).astype(np.float32)
+    targs = dict(sample_rate=16000, n_fft=n_fft, win_length=win, hop_length=n_fft // 4, n_mels=64,
+                 normalized=normalized)
+    assert_parity(run_gpu(x, **targs), oracle(x, **targs), f"normalized={normalized} {n_fft}/{win}")
+
+
+TOL16 = 1e-2
+
+
+def assert_parity_f16(got, ref64, what=""):
+    """fp16 output: against the f64 oracle rounded to fp16, |gpu - ref16| <=
+    1e-2 * (1 + |ref16|); values beyond the fp16 range may come out as inf."""
+    assert got.dtype == np.float16 and got.shape == ref64.shape, what
+    ref16 = ref64.astype(np.float16).astype(np.float64)
+    g = got.astype(np.float64)
+    big = np.abs(ref64) >= 65504.0 * (1 - TOL16)
+    assert np.all(np.isfinite(g[~big])), what
+    assert np.all(np.isinf(g[big]) | (np.abs(g[big] - ref16[big]) <= TOL16 * (1 + np.abs(ref16[big])))), what
+    err = np.abs(g[~big] - ref16[~big])
+    ratio = float(np.max(err / (TOL16 * (1 + np.abs(ref16[~big]))))) if err.size else 0.0
+    print(f"[parity f16] {what}: max err/bound {ratio:.3g}, {int(big.sum())} values past fp16 range",
+          flush=True)
+    assert ratio <= 1.0, what
+
+
+@pytest.mark.parametrize("name,over,scale", [("whisper", dict(batch=2, length=48_000), 1.0),
+                                             ("int16", dict(batch=2, length=48_000), 1.0),
+                                             ("pow2", dict(batch=3), 1.0),
+                                             ("tiny", dict(), 80.0),
+                                             ("large", dict(batch=2), 1.0)])
+def test_f16_output(name, over, scale):
+    cfg = W.workload(name, **over)
+    x = W.make_signal(cfg)
+    if scale != 1.0:
+        x = (x * scale).astype(x.dtype)       # pushes some powers past 65504
+    targs = W.transform_args(cfg)
+    got = run_gpu(x, out_dtype=torch.float16, **targs)
+    assert_parity_f16(got, oracle(x, **targs), f"f16 {name} x{scale}")
+
+
+def test_f16_full_whisper_sampled_rows():
+    cfg = W.workload("whisper")
+    x = W.make_signal(cfg)
+    targs = W.transform_args(cfg)
+    got = run_gpu(x, out_dtype=torch.float16, **targs)
+    assert got.shape == (8, 128, 3001)
+    assert_parity_f16(got[[0, 7]], oracle(x[[0, 7]], **targs), "f16 full whisper rows 0, 7")
+
+
 def test_int16_odd_length_and_misaligned_input():
     from stft_mel_spectrogram_amd import MelSpectrogram
     _require_gpu()

@@ -54,6 +54,59 @@ def test_window_matches_oracle(name):
     np.testing.assert_allclose(t["window"], ref, rtol=1.2e-7, atol=1e-30)
 
 
+@pytest.mark.parametrize("normalized", [True, "window", "frame_length"])
+@pytest.mark.parametrize("win", [400, 320, 257])
+def test_window_normalisation_matches_oracle(normalized, win):
+    p = N.Plan(device=False, n_fft=400, win_length=win, hop_length=100, n_mels=40,
+               normalized=normalized)
+    np.testing.assert_allclose(p.tables()["window"], O.make_window(400, win, normalized),
+                               rtol=1.2e-7, atol=1e-30)
+    assert p.info().normalized == (2 if normalized == "frame_length" else 1)
+
+
+def test_args_defaults_are_torchaudios():
+    a = N.Args()
+    assert N.lib.fm_args_default(ctypes.byref(a)) == N.FM_OK
+    got = {f: getattr(a, f) for f, _ in N.Args._fields_}
+    assert got == dict(sample_rate=16000, n_fft=400, win_length=400, hop_length=200, n_mels=128,
+                       f_min=0.0, f_max=8000.0, power=2.0, center=1, pad_mode=0, mel_scale=0,
+                       norm=0, pad=0, normalized=0, out_dtype=N.FM_F32)
+    assert N.lib.fm_args_default(None) == N.FM_E_INVAL
+
+
+@pytest.mark.parametrize("pad", [1, 7, 200, 5000])
+def test_out_frames_with_zero_pad(pad):
+    for L in (1, 150, 201, 1000, 48_000):
+        for center in (True, False):
+            p = N.Plan(device=False, n_fft=400, hop_length=160, n_mels=40, pad=pad, center=center,
+                       pad_mode="constant")
+            lp = L + 2 * pad
+            if not center and lp < 400:
+                with pytest.raises(N.FmError):
+                    p.out_frames(L)
+                continue
+            assert p.out_frames(L) == O.frame_count(L, 400, 160, center=center, pad=pad), (L, pad)
+    # reflect needs the zero-extended signal to exceed n_fft/2
+    r = N.Plan(device=False, n_fft=400, hop_length=160, n_mels=40, pad=30)
+    assert r.out_frames(141) == O.frame_count(141, 400, 160, center=True, pad=30)
+    with pytest.raises(N.FmError):
+        r.out_frames(140)
+
+
+def test_raw_args_validation():
+    a = N.Args()
+    N.lib.fm_args_default(ctypes.byref(a))
+    h = ctypes.c_void_p()
+    for field, bad in (("pad", -1), ("pad", (1 << 28) + 1), ("normalized", 3), ("out_dtype", N.FM_I16),
+                       ("out_dtype", 7)):
+        b = N.Args.from_buffer_copy(a)
+        setattr(b, field, bad)
+        assert N.lib.fm_plan_create_args_host(ctypes.byref(h), ctypes.byref(b)) == N.FM_E_INVAL, field
+    assert N.lib.fm_plan_create_args_host(ctypes.byref(h), None) == N.FM_E_INVAL
+    assert N.lib.fm_plan_create_args_host(ctypes.byref(h), ctypes.byref(a)) == N.FM_OK
+    N.lib.fm_plan_destroy(h)
+
+
 def test_window_shorter_than_nfft_is_centred():
     p = N.Plan(device=False, sample_rate=16000, n_fft=400, win_length=300, hop_length=100, n_mels=40)
     np.testing.assert_allclose(p.tables()["window"], O.make_window(400, 300, False), rtol=1.2e-7, atol=1e-30)
