@@ -221,10 +221,10 @@ def main():
     traffic = None
     if os.path.exists(args.traffic_json):
         try:
-            t = json.load(open(args.traffic_json))
-            if (t.get("workload") == cfg["name"] and t.get("out_dtype", "f32") == args.out_dtype
-                    and t.get("kernel_sources_sha256_16") == kernel_sources_hash()):
-                traffic = t.get("bytes_per_launch")
+            for t in json.load(open(args.traffic_json)).get("entries", []):
+                if (t.get("workload") == cfg["name"] and t.get("out_dtype", "f32") == args.out_dtype
+                        and t.get("kernel_sources_sha256_16") == kernel_sources_hash()):
+                    traffic = t.get("bytes_per_launch")
         except Exception:
             traffic = None
 
