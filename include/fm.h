@@ -103,8 +103,9 @@ int fm_plan_create_args_host(fm_plan** out, const fm_args* args);
  * fm_plan_create -- build a plan on the CURRENT HIP device.
  *
  * Arguments are torchaudio MelSpectrogram's (README "Usage"):
- *   sample_rate > 0; n_fft in {400, 1024, 2048} (others: FM_E_UNSUPPORTED;
- *   README "Usage" allows 400 and powers of two 64..16384);
+ *   sample_rate > 0; n_fft 400 or a power of two from 64 to 4096 (others:
+ *   FM_E_UNSUPPORTED; README "Usage" allows 400 and powers of two
+ *   64..16384);
  *   0 < win_length <= n_fft (a shorter window is zero-padded centred,
  *   flashmel/filters.py make_window); hop_length > 0;
  *   1 <= n_mels <= 256 (README "Usage");

@@ -1,24 +1,32 @@
 """Ahead-of-time build of the HIP library libfm.so for gfx950.
 
 ``python -m stft_mel_spectrogram_amd.build`` (or ``build()``) compiles every
-source under ``csrc/`` with hipcc into ``stft_mel_spectrogram_amd/libfm.so``,
-in place, so the shared object ships with the source tree.  It always
-recompiles.
+source under ``csrc/`` with hipcc (one translation unit per FFT shape, in
+parallel) and links ``stft_mel_spectrogram_amd/libfm.so`` in place, so the
+shared object ships with the source tree.  It always recompiles.
 """
 from __future__ import annotations
 
+import glob
 import os
 import shutil
 import subprocess
 import sys
 import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfm.so")
-SOURCES = ["fm_api.cpp", "fm_plan.cpp", "fm_kernels.hip"]
+SOURCES = ["fm_api.cpp", "fm_plan.cpp", "fm_launch.hip"]
+
+
+def sources() -> list:
+    """Host/ABI sources plus one fm_shape_<n1>x<n2>.hip per built FFT shape."""
+    shapes = sorted(os.path.basename(f) for f in glob.glob(os.path.join(CSRC, "fm_shape_*.hip")))
+    return SOURCES + shapes
 
 # Packed-FP32 VALU forms are switched off for all device code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
@@ -29,26 +37,41 @@ def hipcc() -> str:
     return exe
 
 
-def build(verbose: bool = False, arch: str = "gfx950") -> str:
+def build(verbose: bool = False, arch: str = "gfx950", jobs: int = 0) -> str:
     """Compile libfm.so for `arch`; returns its path.  Raises on failure."""
+    common = [f"--offload-arch={arch}", "-O3", "-std=c++17", "-fPIC", "-Wall",
+              "-Wno-unused-command-line-argument", *DEVICE_FLAGS, "-I", INCLUDE, "-I", CSRC]
+    tmpdir = tempfile.mkdtemp(prefix=".libfm-build-", dir=PKG)
     fd, tmp = tempfile.mkstemp(suffix=".so", prefix=".libfm-", dir=PKG)
     os.close(fd)
-    cmd = [hipcc(), f"--offload-arch={arch}", "-O3", "-std=c++17", "-fPIC", "-shared",
-           "-Wall", "-Wno-unused-command-line-argument", *DEVICE_FLAGS,
-           "-I", INCLUDE, "-I", CSRC,
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
     try:
+        def compile_one(src):
+            obj = os.path.join(tmpdir, os.path.splitext(src)[0] + ".o")
+            cmd = [hipcc(), *common, "-c", os.path.join(CSRC, src), "-o", obj]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            r = subprocess.run(cmd, capture_output=True, text=True)
+            if r.returncode != 0:
+                raise RuntimeError(f"hipcc failed on {src} ({r.returncode}):\n{r.stderr[-8000:]}")
+            if verbose and r.stderr.strip():
+                print(r.stderr[-4000:], file=sys.stderr)
+            return obj
+
+        srcs = sources()
+        n = jobs or min(len(srcs), max(1, min(os.cpu_count() or 1, 16)))
+        with ThreadPoolExecutor(max_workers=n) as ex:
+            objs = list(ex.map(compile_one, srcs))
+        cmd = [hipcc(), f"--offload-arch={arch}", "-shared", "-fPIC", *objs, "-o", tmp]
+        if verbose:
+            print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
-            raise RuntimeError(f"hipcc failed ({r.returncode}):\n{r.stderr[-8000:]}")
-        if verbose and r.stderr.strip():
-            print(r.stderr[-4000:], file=sys.stderr)
+            raise RuntimeError(f"hipcc link failed ({r.returncode}):\n{r.stderr[-8000:]}")
         os.replace(tmp, LIB)
     finally:
         if os.path.exists(tmp):
             os.unlink(tmp)
+        shutil.rmtree(tmpdir, ignore_errors=True)
     return LIB
 
 

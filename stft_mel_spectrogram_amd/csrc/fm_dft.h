@@ -182,5 +182,6 @@ template <> struct Dft<8> : DftComposite<8, 2> {};
 template <> struct Dft<16> : DftComposite<16, 4> {};
 template <> struct Dft<25> : DftComposite<25, 5> {};
 template <> struct Dft<32> : DftComposite<32, 4> {};
+template <> struct Dft<64> : DftComposite<64, 8> {};
 
 }  // namespace fm

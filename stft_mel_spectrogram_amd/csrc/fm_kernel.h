@@ -1,4 +1,6 @@
-// Fused mel-spectrogram forward kernel for gfx950 (MI355X), and its launcher.
+// Fused mel-spectrogram forward kernel for gfx950 (MI355X): device code.
+// Each fm_shape_<n1>x<n2>.hip instantiates it for one FFT shape;
+// fm_launch.hip uploads plans and launches it.
 //
 // One workgroup owns a tile of consecutive frames of one signal and runs the
 // whole chain the flashmel 0.1.0 page describes (README "How it works"):
@@ -19,6 +21,8 @@
 // buffer (frame stride n_fft/2 + 4 complex values).  The mel projection is a block-sparse product on the matrix cores:
 // 16 filters x 16 frames per v_mfma_f32_16x16x4f32, over only the bins each
 // block of filters touches.
+#pragma once
+
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -29,8 +33,7 @@
 
 namespace fm {
 
-namespace {
-
+// Kernel arguments (one struct, passed by value).
 struct KArgs {
   const void* in;
   void* out;            // [B, n_mels, n_frames] float or _Float16
@@ -55,6 +58,8 @@ struct KArgs {
   int w_lds;            // LDS float offset of the copied weights
   int out_f16;          // 1: the output is float16
 };
+
+namespace {
 
 // Tables read with wave-uniform indices are reached through the constant
 // address space so they load as scalars (SGPR operands of the FMAs).
@@ -436,187 +441,27 @@ __global__ __launch_bounds__(256, (kMinWavesPerSimd<N1, N2>)) void mel_forward_k
   }
 }
 
-template <int N1, int N2, typename InT>
-void* kernel_for_power(int pmode) {
-  if (pmode == 0) return reinterpret_cast<void*>(&mel_forward_kernel<N1, N2, InT, 0>);
-  if (pmode == 1) return reinterpret_cast<void*>(&mel_forward_kernel<N1, N2, InT, 1>);
-  return reinterpret_cast<void*>(&mel_forward_kernel<N1, N2, InT, 2>);
-}
+}  // namespace
 
+// Kernel entry of one FFT shape for an input type and power mode
+// (0: p = 2, 1: p = 1, 2: general p); instantiated in fm_shape_<N1>x<N2>.hip.
 template <int N1, int N2>
 void* kernel_for(int in_dtype, int pmode) {
-  if (in_dtype == FM_I16) return kernel_for_power<N1, N2, int16_t>(pmode);
-  return kernel_for_power<N1, N2, float>(pmode);
+  auto pick = [](auto in_tag, int pm) -> void* {
+    using InT = decltype(in_tag);
+    if (pm == 0) return reinterpret_cast<void*>(&mel_forward_kernel<N1, N2, InT, 0>);
+    if (pm == 1) return reinterpret_cast<void*>(&mel_forward_kernel<N1, N2, InT, 1>);
+    return reinterpret_cast<void*>(&mel_forward_kernel<N1, N2, InT, 2>);
+  };
+  if (in_dtype == FM_I16) return pick(int16_t{}, pmode);
+  return pick(float{}, pmode);
 }
 
-int power_mode(const Plan& p) { return p.power == 2.0 ? 0 : (p.power == 1.0 ? 1 : 2); }
-
-void* select_kernel(const Plan& p, int in_dtype) {
-  const int pm = power_mode(p);
-  if (p.fft.n1 == 8 && p.fft.n2 == 25) return kernel_for<8, 25>(in_dtype, pm);
-  if (p.fft.n1 == 32 && p.fft.n2 == 16) return kernel_for<32, 16>(in_dtype, pm);
-  if (p.fft.n1 == 32 && p.fft.n2 == 32) return kernel_for<32, 32>(in_dtype, pm);
-  return nullptr;
-}
-
-int hip_fail(hipError_t e, const char* what) {
-  std::string msg = std::string(what) + ": " + hipGetErrorString(e);
-  return set_error(FM_E_HIP, msg);
-}
-
-}  // namespace
-
-int upload_plan(Plan& p) {
-  hipError_t e = hipGetDevice(&p.device);
-  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-  e = hipDeviceGetAttribute(&p.n_cu, hipDeviceAttributeMultiprocessorCount, p.device);
-  if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
-  const int M = p.n_fft / 2;
-  // one block: win2 | tw_m | tw_n | rows | mel_w | mel blocks | block weights,
-  // each 256-byte aligned
-  auto al = [](size_t n) { return (n + 255) / 256 * 256; };
-  const size_t o_win = 0;
-  const size_t o_twm = o_win + al(M * sizeof(float2));
-  const size_t o_twn = o_twm + al(M * sizeof(float2));
-  const size_t o_rows = o_twn + al(M * sizeof(float2));
-  const size_t o_w = o_rows + al(p.n_mels * sizeof(MelRow));
-  const size_t o_tbl = o_w + al(static_cast<size_t>(p.nnz > 0 ? p.nnz : 1) * sizeof(float));
-  const size_t o_bw = o_tbl + al((8 + 4 * p.blocks.size()) * sizeof(int32_t));
-  const size_t total = o_bw + al(std::max<size_t>(p.blk_w.size(), 1) * sizeof(float));
-  std::vector<unsigned char> host(total, 0);
-  float* win2 = reinterpret_cast<float*>(host.data() + o_win);
-  for (int j = 0; j < p.n_fft; ++j) win2[j] = 0.5f * p.window[j];  // exact scaling
-  std::copy(p.tw_m.begin(), p.tw_m.end(), reinterpret_cast<float*>(host.data() + o_twm));
-  std::copy(p.tw_n.begin(), p.tw_n.end(), reinterpret_cast<float*>(host.data() + o_twn));
-  std::copy(p.rows.begin(), p.rows.end(), reinterpret_cast<MelRow*>(host.data() + o_rows));
-  std::copy(p.mel_w.begin(), p.mel_w.end(), reinterpret_cast<float*>(host.data() + o_w));
-  int32_t* tbl = reinterpret_cast<int32_t*>(host.data() + o_tbl);
-  for (int w = 0; w <= kMelWaves; ++w) tbl[w] = p.wave_beg[w];
-  for (size_t j = 0; j < p.blocks.size(); ++j) {
-    tbl[8 + 4 * j + 0] = p.blocks[j].kb;
-    tbl[8 + 4 * j + 1] = p.blocks[j].ksteps;
-    tbl[8 + 4 * j + 2] = p.blocks[j].w_off;
-    tbl[8 + 4 * j + 3] = p.blocks[j].mel0;
-  }
-  std::copy(p.blk_w.begin(), p.blk_w.end(), reinterpret_cast<float*>(host.data() + o_bw));
-  void* d = nullptr;
-  e = hipMalloc(&d, total);
-  if (e != hipSuccess) return set_error(FM_E_NOMEM, std::string("hipMalloc: ") + hipGetErrorString(e));
-  e = hipMemcpy(d, host.data(), total, hipMemcpyHostToDevice);
-  if (e != hipSuccess) {
-    (void)hipFree(d);
-    return hip_fail(e, "hipMemcpy (plan tables)");
-  }
-  unsigned char* base = static_cast<unsigned char*>(d);
-  p.d_block = d;
-  p.d_win2 = base + o_win;
-  p.d_tw_m = base + o_twm;
-  p.d_tw_n = base + o_twn;
-  p.d_rows = base + o_rows;
-  p.d_mel_w = base + o_w;
-  p.d_mel_tbl = base + o_tbl;
-  p.d_blk_w = base + o_bw;
-  // Tiles above 64 KB of LDS need the per-kernel opt-in.
-  for (int dt : {FM_F32, FM_I16}) {
-    void* k = select_kernel(p, dt);
-    if (!k) return set_error(FM_E_UNSUPPORTED, "no kernel for this n_fft");
-    e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, p.lds_bytes);
-    if (e != hipSuccess) return hip_fail(e, "hipFuncSetAttribute");
-  }
-  p.has_device = true;
-  return FM_OK;
-}
-
-void free_plan_device(Plan& p) {
-  if (p.d_block) {
-    int cur = -1;
-    (void)hipGetDevice(&cur);
-    if (cur != p.device) (void)hipSetDevice(p.device);
-    (void)hipFree(p.d_block);
-    if (cur != p.device && cur >= 0) (void)hipSetDevice(cur);
-  }
-  p.d_block = nullptr;
-  p.has_device = false;
-}
-
-namespace {
-
-// Frames per tile for this call: the largest tile whose busiest compute
-// unit holds the fewest frames (all tiles resident at once when they fit).
-int choose_tile(const Plan& p, int64_t batch, int64_t T) {
-  if (p.tile_override > 0) return p.tile_override;
-  const int ncu = p.n_cu > 0 ? p.n_cu : 256;
-  int best = p.tile_max;
-  int64_t best_cost = INT64_MAX;
-  for (int g = p.tile_max; g >= 1 && g * 2 >= p.tile_max; --g) {
-    const int64_t tiles = batch * ((T + g - 1) / g);
-    const int64_t per_cu = (tiles + ncu - 1) / ncu;
-    const int64_t cost = per_cu * g;
-    if (cost < best_cost) {
-      best_cost = cost;
-      best = g;
-    }
-  }
-  return best;
-}
-
-}  // namespace
-
-int launch_forward(const Plan& p, const void* in, int in_dtype, int64_t batch, int64_t length,
-                   void* out, void* stream) {
-  if (!p.has_device) return set_error(FM_E_NODEVICE, "plan was built without device tables");
-  if (in_dtype != FM_F32 && in_dtype != FM_I16) return set_error(FM_E_INVAL, "in_dtype must be FM_F32 or FM_I16");
-  if (batch < 0) return set_error(FM_E_INVAL, "batch must be >= 0");
-  const int64_t T = out_frames(p, length);
-  if (T < 0) return static_cast<int>(T);
-  if (batch == 0) return FM_OK;
-  if (!in || !out) return set_error(FM_E_INVAL, "null input or output pointer");
-  int cur = -1;
-  hipError_t e = hipGetDevice(&cur);
-  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-  if (cur != p.device) return set_error(FM_E_INVAL, "plan belongs to another device than the current one");
-  const int G = choose_tile(p, batch, T);
-  const int64_t tiles = (T + G - 1) / G;
-  if (length > (1 << 29) || tiles * batch > INT32_MAX)
-    return set_error(FM_E_INVAL, "problem too large for one launch (length <= 2^29, tiles < 2^31)");
-  const int lds = tile_lds_bytes(p, G);
-  const int64_t n_tiles = tiles * batch;
-
-  KArgs a;
-  a.in = in;
-  a.out = out;
-  a.win2 = static_cast<const float2*>(p.d_win2);
-  a.tw_m = static_cast<const float2*>(p.d_tw_m);
-  a.tw_n = static_cast<const float2*>(p.d_tw_n);
-  a.length = length;
-  a.n_frames = static_cast<int>(T);
-  a.hop = p.hop;
-  a.pad = p.pad_left + p.zpad;
-  a.zpad = p.zpad;
-  a.n_mels = p.n_mels;
-  a.tile = G;
-  a.tiles_per_signal = static_cast<int>(tiles);
-  a.pad_mode = p.pad_mode;
-  a.half_power = static_cast<float>(p.power * 0.5);
-  const size_t esz = (in_dtype == FM_I16) ? 2 : 4;
-  const uintptr_t ia = reinterpret_cast<uintptr_t>(in);
-  a.vec_ok = (ia % (2 * esz) == 0) && (length % 2 == 0) && (p.hop % 2 == 0) &&
-             ((p.pad_left + p.zpad) % 2 == 0);
-  a.mel_tbl = static_cast<const int*>(p.d_mel_tbl);
-  a.blk_w = static_cast<const float*>(p.d_blk_w);
-  a.w_chunks = static_cast<int>(p.blk_w.size() / 256);
-  a.w_lds = tile_weights_offset(p, G);
-  a.out_f16 = p.out_dtype == FM_F16 ? 1 : 0;
-
-  void* k = select_kernel(p, in_dtype);
-  if (!k) return set_error(FM_E_UNSUPPORTED, "no kernel for this n_fft");
-  void* args[] = {&a};
-  e = hipLaunchKernel(k, dim3(static_cast<unsigned>(n_tiles)), dim3(p.threads), args,
-                      static_cast<size_t>(lds), static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "kernel launch");
-  e = hipGetLastError();
-  if (e != hipSuccess) return hip_fail(e, "kernel launch");
-  return FM_OK;
-}
+// Shapes built into the library (n_fft/2 = N1 * N2).
+#define FM_FOR_EACH_SHAPE(X) \
+  X(8, 4) X(8, 8) X(8, 16) X(8, 25) X(16, 16) X(32, 16) X(32, 32) X(64, 32)
+#define FM_DECLARE_SHAPE(A, B) extern template void* kernel_for<A, B>(int, int);
+FM_FOR_EACH_SHAPE(FM_DECLARE_SHAPE)
+#undef FM_DECLARE_SHAPE
 
 }  // namespace fm

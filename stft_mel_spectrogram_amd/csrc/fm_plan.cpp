@@ -66,9 +66,14 @@ double mel_to_hz(double m, int scale) {
 // n2 transforms of n1 points, the second n1 transforms of n2 points.
 bool fft_shape_for(int n_fft, FftShape* s) {
   switch (n_fft) {
+    case 64: *s = {8, 4}; return true;      // 32 = 8 * 4
+    case 128: *s = {8, 8}; return true;     // 64 = 8 * 8
+    case 256: *s = {8, 16}; return true;    // 128 = 8 * 16
     case 400: *s = {8, 25}; return true;    // 200 = 8 * 25 (radix 2*4, 5*5)
+    case 512: *s = {16, 16}; return true;   // 256 = 16 * 16
     case 1024: *s = {32, 16}; return true;  // 512 = 32 * 16 (radix 4*8, 4*4)
     case 2048: *s = {32, 32}; return true;  // 1024 = 32 * 32
+    case 4096: *s = {64, 32}; return true;  // 2048 = 64 * 32 (radix 8*8, 4*8)
     default: return false;
   }
 }
@@ -170,7 +175,7 @@ int build_host_plan(Plan& p, const fm_args& a) {
   if (n_mels > 256) return set_error(FM_E_UNSUPPORTED, fmt("n_mels > 256 is not supported", n_mels));
   FftShape fs;
   if (!fft_shape_for(n_fft, &fs))
-    return set_error(FM_E_UNSUPPORTED, fmt("n_fft not built (supported: 400, 1024, 2048)", n_fft));
+    return set_error(FM_E_UNSUPPORTED, fmt("n_fft not built (supported: 400 and powers of two 64..4096)", n_fft));
 
   p.sample_rate = sample_rate; p.n_fft = n_fft; p.win_length = win_length;
   p.hop = hop_length; p.n_mels = n_mels; p.f_min = f_min; p.f_max = f_max;

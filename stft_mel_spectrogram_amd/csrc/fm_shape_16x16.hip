@@ -1,0 +1,6 @@
+// Kernels for n_fft = 512: complex FFT of 256 = 16 x 16 points.
+#include "fm_kernel.h"
+
+namespace fm {
+template void* kernel_for<16, 16>(int, int);
+}  // namespace fm

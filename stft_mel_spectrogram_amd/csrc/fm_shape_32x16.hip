@@ -1,0 +1,6 @@
+// Kernels for n_fft = 1024: complex FFT of 512 = 32 x 16 points.
+#include "fm_kernel.h"
+
+namespace fm {
+template void* kernel_for<32, 16>(int, int);
+}  // namespace fm

@@ -1,0 +1,6 @@
+// Kernels for n_fft = 2048: complex FFT of 1024 = 32 x 32 points.
+#include "fm_kernel.h"
+
+namespace fm {
+template void* kernel_for<32, 32>(int, int);
+}  // namespace fm

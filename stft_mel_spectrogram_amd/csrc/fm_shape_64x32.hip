@@ -1,0 +1,6 @@
+// Kernels for n_fft = 4096: complex FFT of 2048 = 64 x 32 points.
+#include "fm_kernel.h"
+
+namespace fm {
+template void* kernel_for<64, 32>(int, int);
+}  // namespace fm

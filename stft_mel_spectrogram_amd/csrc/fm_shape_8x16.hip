@@ -1,0 +1,6 @@
+// Kernels for n_fft = 256: complex FFT of 128 = 8 x 16 points.
+#include "fm_kernel.h"
+
+namespace fm {
+template void* kernel_for<8, 16>(int, int);
+}  // namespace fm

@@ -1,0 +1,6 @@
+// Kernels for n_fft = 64: complex FFT of 32 = 8 x 4 points.
+#include "fm_kernel.h"
+
+namespace fm {
+template void* kernel_for<8, 4>(int, int);
+}  // namespace fm

@@ -1,0 +1,6 @@
+// Kernels for n_fft = 128: complex FFT of 64 = 8 x 8 points.
+#include "fm_kernel.h"
+
+namespace fm {
+template void* kernel_for<8, 8>(int, int);
+}  // namespace fm

@@ -112,6 +112,29 @@ def test_ragged_large_fft(n_fft, hop):
     assert_parity(run_gpu(x, **targs), oracle(x, **targs), f"{n_fft}/{hop}")
 
 
+OTHER_FFT = [(64, 16, 40), (64, 20, 8), (128, 32, 40), (256, 64, 64), (256, 100, 128),
+             (512, 128, 80), (512, 100, 256), (4096, 1024, 128), (4096, 512, 40)]
+
+
+@pytest.mark.parametrize("n_fft,hop,mels", OTHER_FFT)
+def test_other_fft_sizes(n_fft, hop, mels):
+    """Powers of two 64..4096 besides 1024/2048 (ragged signal lengths)."""
+    x = np.random.default_rng(n_fft + hop).standard_normal((2, 9001)).astype(np.float32)
+    targs = dict(sample_rate=16000, n_fft=n_fft, hop_length=hop, n_mels=mels)
+    assert_parity(run_gpu(x, **targs), oracle(x, **targs), f"n_fft={n_fft} hop={hop} mels={mels}")
+
+
+def test_other_fft_sizes_mixed_arguments():
+    q = np.random.default_rng(21).integers(-32768, 32768, size=(3, 7777)).astype(np.int16)
+    for targs in (dict(n_fft=64, hop_length=32, n_mels=24, power=1.0, center=False),
+                  dict(n_fft=256, win_length=200, hop_length=80, n_mels=64, pad_mode="constant"),
+                  dict(n_fft=512, hop_length=160, n_mels=96, power=1.5, normalized=True),
+                  dict(n_fft=128, hop_length=64, n_mels=32, mel_scale="slaney", norm="slaney"),
+                  dict(n_fft=4096, win_length=3000, hop_length=700, n_mels=64, pad=123)):
+        assert_parity(run_gpu(q, sample_rate=22050, **targs), oracle(q, sample_rate=22050, **targs),
+                      f"i16 {targs}")
+
+
 @pytest.mark.parametrize("pad_mode", ["constant", "replicate", "circular"])
 def test_other_pad_modes(pad_mode):
     x = np.random.default_rng(3).standard_normal((2, 5000)).astype(np.float32)

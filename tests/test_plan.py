@@ -147,6 +147,9 @@ def test_csr_statistics_of_the_workloads():
 
 @pytest.mark.parametrize("name,over", [("tiny", {}), ("whisper", {}), ("pow2", {}), ("large", {}),
                                        ("large", dict(n_mels=8)), ("whisper", dict(n_mels=256)),
+                                       ("tiny", dict(n_fft=64, win_length=64, hop_length=16, n_mels=40)),
+                                       ("tiny", dict(n_fft=512, win_length=512, hop_length=128)),
+                                       ("large", dict(n_fft=4096, win_length=4096, hop_length=1024)),
                                        ("whisper", dict(n_mels=37)),
                                        ("whisper", dict(mel_scale="slaney", norm="slaney"))])
 def test_mel_blocks_equal_the_csr_filterbank(name, over):
@@ -196,7 +199,7 @@ def test_mel_blocks_equal_the_csr_filterbank(name, over):
     assert max(cost) - min(cost) <= max(blocks[:, 1]) + 2
 
 
-@pytest.mark.parametrize("n_fft", [400, 1024, 2048])
+@pytest.mark.parametrize("n_fft", [64, 128, 256, 400, 512, 1024, 2048, 4096])
 def test_twiddles(n_fft):
     p = N.Plan(device=False, sample_rate=16000, n_fft=n_fft, hop_length=n_fft // 4, n_mels=40)
     t = p.tables()
@@ -210,7 +213,8 @@ def test_twiddles(n_fft):
 
 @pytest.mark.parametrize("L", [201, 202, 1000, 16000, 480000, 220500])
 def test_out_frames_closed_form(L):
-    for n_fft, hop in ((400, 160), (1024, 256), (2048, 512)):
+    for n_fft, hop in ((64, 16), (256, 64), (400, 160), (512, 100), (1024, 256), (2048, 512),
+                       (4096, 1024)):
         if L <= n_fft // 2:
             continue
         p = N.Plan(device=False, n_fft=n_fft, hop_length=hop, n_mels=40)
@@ -221,15 +225,21 @@ def test_out_frames_closed_form(L):
 
 
 def test_geometry_fits_the_hardware():
-    for name in ("tiny", "whisper", "pow2", "large"):
-        inf = host_plan(W.WORKLOADS[name]).info()
+    plans = [host_plan(W.WORKLOADS[name]) for name in ("tiny", "whisper", "pow2", "large")]
+    plans += [N.Plan(device=False, n_fft=n, hop_length=n // 4, n_mels=m)
+              for n in (64, 128, 256, 512, 4096) for m in (8, 128, 256)]
+    for p in plans:
+        inf = p.info()
         assert inf.lds_bytes <= 160 * 1024
+        assert 1 <= inf.tile_frames <= 64
         assert inf.tile_frames * inf.fft_n1 // 2 <= inf.threads
+        assert inf.fft_n1 * inf.fft_n2 == inf.n_fft // 2
         assert inf.has_device == 0
 
 
 BAD = [
-    (dict(n_fft=512), N.FM_E_UNSUPPORTED),
+    (dict(n_fft=8192, hop_length=2048, f_max=8000.0), N.FM_E_UNSUPPORTED),
+    (dict(n_fft=300), N.FM_E_UNSUPPORTED),
     (dict(n_mels=257), N.FM_E_UNSUPPORTED),
     (dict(f_min=8000.0, f_max=8000.0), N.FM_E_INVAL),
     (dict(f_max=8001.0), N.FM_E_INVAL),
