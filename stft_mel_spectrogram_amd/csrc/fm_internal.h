@@ -38,6 +38,13 @@ constexpr int kMelWaves = 4;       // waves of a workgroup
 constexpr int kMelStepGroup = 4;
 // Power-tile floats the mel stage may read past the tile (zeroed there).
 constexpr int kMelTileOverrun = 16;
+// FFTs of n_fft/2 >= this many points keep the mel weights in global memory
+// (L2) instead of LDS: their weights (about n_fft/2 x 64 bytes) would force
+// the tile below the geometric maximum.  The kernel then loads the weights
+// in chunks of kMelGlobalChunk steps and the table carries one chunk of zero
+// slack at its end.
+constexpr int kMelGlobalWeightsFrom = 2048;
+constexpr int kMelGlobalChunk = 32;
 // Tiles of more than this many frames write their mel rows through a
 // per-wave LDS staging area (one contiguous store per row, rows long enough
 // to cover whole cache lines); narrower tiles store the MFMA results directly.
@@ -83,6 +90,7 @@ struct Plan {
   std::vector<MelBlock> blocks;
   int wave_beg[kMelWaves + 1] = {};
   std::vector<float> blk_w;            // block weights (see MelBlock)
+  bool w_in_lds = true;                // weights staged in LDS (else read from L2)
   int nnz = 0, w_max = 0;
   // host tables (float32 after one rounding from float64)
   std::vector<float> window;  // [n_fft], unscaled

@@ -54,7 +54,8 @@ struct KArgs {
   int vec_ok;           // interior tiles may use paired (2-sample) loads
   const int* mel_tbl;   // wave_beg[5], 3 pad, then {kb, ksteps, w_off, mel0} per block
   const float* blk_w;   // block weights, 64 per 4-bin step (MFMA A-operand order)
-  int w_chunks;         // block weights / 256 (copied to LDS in 1 KB chunks)
+  int w_chunks;         // block weights / 256 (copied to LDS in 1 KB chunks;
+                        // 0 when the shape reads them from global memory)
   int w_lds;            // LDS float offset of the copied weights
   int out_f16;          // 1: the output is float16
 };
@@ -84,7 +85,9 @@ using f32x4 = float __attribute__((ext_vector_type(4)));
 // `stg` and each filter row leaves in one contiguous streaming store (lane =
 // frame); otherwise lanes store their D elements directly (plain stores, so
 // that L2 merges the pieces of a row).
-template <int KS, int NFB, bool STAGE, typename OT>
+// GW: the weights WL are in global memory (large FFTs); they are loaded
+// kMelGlobalChunk steps at a time, then consumed group by group.
+template <int KS, int NFB, bool STAGE, bool GW, typename OT>
 __device__ __forceinline__ void mel_blocks(const float* P, const float* WL, float* stg, int G,
                                            int nvalid, int lane, OT* obase, int n_frames,
                                            int n_mels, CInt* blk, int bb, int be) {
@@ -101,19 +104,35 @@ __device__ __forceinline__ void mel_blocks(const float* P, const float* WL, floa
     for (int f = 0; f < NFB; ++f) acc[f] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     const float* pb = P + kb;
     const float* wl = WL + woff + lane;
-    for (int s0 = 0; s0 < ks; s0 += U, pb += 4 * U, wl += 64 * U) {
-      float av[U], bv[U][NFB];
-#pragma unroll
-      for (int u = 0; u < U; ++u) av[u] = wl[64 * u];
+    auto group = [&](const float* av, const float* pg) {
+      float bv[U][NFB];
 #pragma unroll
       for (int u = 0; u < U; ++u)
 #pragma unroll
-        for (int f = 0; f < NFB; ++f) bv[u][f] = pb[roff[f] + 4 * u];
+        for (int f = 0; f < NFB; ++f) bv[u][f] = pg[roff[f] + 4 * u];
 #pragma unroll
       for (int u = 0; u < U; ++u)
 #pragma unroll
         for (int f = 0; f < NFB; ++f)
           acc[f] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[u], bv[u][f], acc[f], 0, 0, 0);
+    };
+    if constexpr (GW) {
+      constexpr int CH = kMelGlobalChunk;
+      for (int s0 = 0; s0 < ks; s0 += CH, pb += 4 * CH, wl += 64 * CH) {
+        float av[CH];  // one chunk of weights in flight at once (slack covers the tail)
+#pragma unroll
+        for (int j = 0; j < CH; ++j) av[j] = wl[64 * j];
+#pragma unroll
+        for (int g = 0; g < CH / U; ++g)
+          if (s0 + U * g < ks) group(av + U * g, pb + 4 * U * g);
+      }
+    } else {
+      for (int s0 = 0; s0 < ks; s0 += U, pb += 4 * U, wl += 64 * U) {
+        float av[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) av[u] = wl[64 * u];
+        group(av, pb);
+      }
     }
     if constexpr (STAGE) {
       constexpr int PITCH = 16 * NFB + 1;  // odd: conflict-free column writes
@@ -418,17 +437,18 @@ __global__ __launch_bounds__(256, (kMinWavesPerSimd<N1, N2>)) void mel_forward_k
       const long long obase = static_cast<long long>(b) * a.n_mels * a.n_frames + t0;  // element offset
       const int nfb = (G + 15) >> 4;
       CInt* blk = tbl + 8;
-      const float* WL = P + a.w_lds;
+      constexpr bool GW = M >= kMelGlobalWeightsFrom;
+      const float* WL = GW ? a.blk_w : P + a.w_lds;
       float* stg = P + a.w_lds + a.w_chunks * 256 + wave * kMelStageFloats;
       static_assert(kMelStageMinFrames == 33, "staging is chosen for 3 and 4 column groups");
       switch (nfb) {
 #define FM_MEL_CALL(NFB, STAGE)                                                                \
   if (a.out_f16)                                                                              \
-    mel_blocks<SP, NFB, STAGE, _Float16>(P, WL, stg, G, nvalid, lane,                          \
+    mel_blocks<SP, NFB, STAGE, GW, _Float16>(P, WL, stg, G, nvalid, lane,                      \
                                          static_cast<_Float16*>(a.out) + obase, a.n_frames,   \
                                          a.n_mels, blk, bb, be);                              \
   else                                                                                        \
-    mel_blocks<SP, NFB, STAGE, float>(P, WL, stg, G, nvalid, lane,                            \
+    mel_blocks<SP, NFB, STAGE, GW, float>(P, WL, stg, G, nvalid, lane,                        \
                                       static_cast<float*>(a.out) + obase, a.n_frames, a.n_mels, \
                                       blk, bb, be)
         case 1: FM_MEL_CALL(1, false); break;

@@ -169,7 +169,7 @@ int launch_forward(const Plan& p, const void* in, int in_dtype, int64_t batch, i
              ((p.pad_left + p.zpad) % 2 == 0);
   a.mel_tbl = static_cast<const int*>(p.d_mel_tbl);
   a.blk_w = static_cast<const float*>(p.d_blk_w);
-  a.w_chunks = static_cast<int>(p.blk_w.size() / 256);
+  a.w_chunks = p.w_in_lds ? static_cast<int>(p.blk_w.size() / 256) : 0;
   a.w_lds = tile_weights_offset(p, G);
   a.out_f16 = p.out_dtype == FM_F16 ? 1 : 0;
 

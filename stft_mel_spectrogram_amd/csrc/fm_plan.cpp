@@ -101,8 +101,8 @@ int tile_weights_offset(const Plan& p, int frames) {
 
 int tile_lds_bytes(const Plan& p, int frames) {
   const long stage = frames >= kMelStageMinFrames ? kMelWaves * kMelStageFloats : 0;
-  const long after_fft = (static_cast<long>(tile_weights_offset(p, frames)) +
-                          static_cast<long>(p.blk_w.size()) + stage) * 4;
+  const long weights = p.w_in_lds ? static_cast<long>(p.blk_w.size()) : 0;
+  const long after_fft = (static_cast<long>(tile_weights_offset(p, frames)) + weights + stage) * 4;
   return static_cast<int>(std::max<long>(tile_exchange_bytes(p, frames), after_fft));
 }
 
@@ -318,6 +318,9 @@ int build_host_plan(Plan& p, const fm_args& a) {
         }
     }
     p.wave_beg[kMelWaves] = static_cast<int>(p.blocks.size());
+    p.w_in_lds = M < kMelGlobalWeightsFrom;
+    if (!p.w_in_lds)  // read-ahead slack of the chunked global loads
+      p.blk_w.resize(p.blk_w.size() + static_cast<size_t>(kMelGlobalChunk) * 64, 0.0f);
     static_assert(kMelTileOverrun >= 4 * kMelStepGroup - 1, "zeroed tail too short");
     static_assert(kMelStepGroup * 64 % 256 == 0, "blocks must fill whole copy chunks");
   }

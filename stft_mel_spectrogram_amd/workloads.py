@@ -38,6 +38,23 @@ WORKLOADS = {
     "large": dict(batch=64, length=220500, dtype="f32", signal="chirp", sigma=0.1, seed=5,
                   sample_rate=22050, n_fft=2048, win_length=2048, hop_length=512,
                   n_mels=128, f_min=0.0, f_max=11025.0, power=1.0),
+    # measurement and parity cases for the other FFT sizes (not in the pages'
+    # benchmark table; shapes of common speech and music front ends)
+    "asr512": dict(batch=8, length=480000, dtype="f32", signal="sines", sigma=0.1, seed=6,
+                   sample_rate=16000, n_fft=512, win_length=400, hop_length=160,
+                   n_mels=80, f_min=0.0, f_max=8000.0, power=2.0),
+    "music4096": dict(batch=4, length=1323000, dtype="f32", signal="chirp", sigma=0.1, seed=7,
+                      sample_rate=44100, n_fft=4096, win_length=4096, hop_length=1024,
+                      n_mels=128, f_min=0.0, f_max=22050.0, power=2.0),
+    "fft256": dict(batch=8, length=480000, dtype="f32", signal="noise", sigma=0.1, seed=8,
+                   sample_rate=16000, n_fft=256, win_length=256, hop_length=64,
+                   n_mels=64, f_min=0.0, f_max=8000.0, power=2.0),
+    "fft128": dict(batch=8, length=480000, dtype="f32", signal="noise", sigma=0.1, seed=9,
+                   sample_rate=16000, n_fft=128, win_length=128, hop_length=32,
+                   n_mels=40, f_min=0.0, f_max=8000.0, power=2.0),
+    "fft64": dict(batch=8, length=480000, dtype="f32", signal="noise", sigma=0.1, seed=10,
+                  sample_rate=16000, n_fft=64, win_length=64, hop_length=16,
+                  n_mels=24, f_min=0.0, f_max=8000.0, power=2.0),
 }
 
 # The arguments that define the transform (everything but the input recipe).

@@ -124,6 +124,19 @@ def test_other_fft_sizes(n_fft, hop, mels):
     assert_parity(run_gpu(x, **targs), oracle(x, **targs), f"n_fft={n_fft} hop={hop} mels={mels}")
 
 
+@pytest.mark.parametrize("name", ["asr512", "music4096", "fft256", "fft128", "fft64"])
+def test_parity_full_other_fft_workloads(name):
+    """Full-size measurement workloads of the other FFT sizes: every output
+    finite and non-negative; first and last signals against the oracle."""
+    cfg = W.workload(name)
+    x = W.make_signal(cfg)
+    targs = W.transform_args(cfg)
+    got = run_gpu(x, **targs)
+    assert np.all(np.isfinite(got)) and np.all(got >= 0)
+    rows = [0, cfg["batch"] - 1]
+    assert_parity(got[rows], oracle(x[rows], **targs), f"full {name} (rows {rows})")
+
+
 def test_other_fft_sizes_mixed_arguments():
     q = np.random.default_rng(21).integers(-32768, 32768, size=(3, 7777)).astype(np.int16)
     for targs in (dict(n_fft=64, hop_length=32, n_mels=24, power=1.0, center=False),

@@ -180,7 +180,9 @@ def test_mel_blocks_equal_the_csr_filterbank(name, over):
                 elif v != 0.0:
                     assert dense[m, k] == 0.0
                     dense[m, k] = v
-    assert len(wts) == 64 * blocks[:, 1].sum() and len(wts) % 256 == 0   # whole 1 KB copy chunks
+    slack = 32 * 64 if K - 1 >= 2048 else 0     # large FFTs read weights from L2 in 32-step chunks
+    assert len(wts) == 64 * blocks[:, 1].sum() + slack and len(wts) % 256 == 0
+    assert np.all(wts[len(wts) - slack:] == 0.0)
     # a wave's blocks are consecutive in the table
     for w in range(4):
         for j in range(wave_beg[w], wave_beg[w + 1] - 1):
@@ -193,7 +195,7 @@ def test_mel_blocks_equal_the_csr_filterbank(name, over):
     # the tile's LDS holds the power tile, its overrun and the weights
     inf = p.info()
     G = inf.tile_frames
-    assert inf.lds_bytes >= 4 * (-(-(G * K + 16) // 4) * 4 + len(wts))
+    assert inf.lds_bytes >= 4 * (-(-(G * K + 16) // 4) * 4 + (len(wts) if not slack else 0))
     # the waves' shares of 4-bin steps are balanced to within one block
     cost = [sum(blocks[j, 1] + 2 for j in range(wave_beg[w], wave_beg[w + 1])) for w in range(4)]
     assert max(cost) - min(cost) <= max(blocks[:, 1]) + 2
