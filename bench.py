@@ -103,11 +103,18 @@ def copy_probe(torch, dev, nbytes: int, reps: int = 50) -> dict:
 
 
 def kernel_sources_hash() -> str:
+    """sha256[:16] of the library sources with comments and whitespace
+    removed, so that only a change of code invalidates measured counters."""
     import glob
     import hashlib
+    import re
     m = hashlib.sha256()
     for f in sorted(glob.glob(os.path.join(ROOT, "stft_mel_spectrogram_amd", "csrc", "*"))):
-        m.update(open(f, "rb").read())
+        src = open(f, encoding="utf-8", errors="replace").read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)       # block comments
+        src = re.sub(r"//[^\n]*", " ", src)                       # line comments
+        m.update(os.path.basename(f).encode())
+        m.update(" ".join(src.split()).encode())
     return m.hexdigest()[:16]
 
 

@@ -131,7 +131,7 @@ int tile_lds_bytes(const Plan& p, int frames);
 // Frames per signal for a plan (negative FM_E_* on invalid length).
 int64_t out_frames(const Plan& p, int64_t length);
 
-// Device side (fm_kernels.hip).
+// Device side (fm_launch.hip).
 int upload_plan(Plan& p);
 void free_plan_device(Plan& p);
 int launch_forward(const Plan& p, const void* in, int in_dtype, int64_t batch,
