@@ -204,6 +204,19 @@ __device__ __forceinline__ float padded_sample_raw(const T* x, int i, int L, int
   if constexpr (std::is_same<T, int16_t>::value) return static_cast<float>(x[j]);
   else return x[j];
 }
+// Two consecutive samples from the LDS copy of a tile (int16 unscaled).
+template <typename T>
+__device__ __forceinline__ float2 lds_pair_raw(const unsigned char* p);
+template <>
+__device__ __forceinline__ float2 lds_pair_raw<float>(const unsigned char* p) {
+  return *reinterpret_cast<const float2*>(p);
+}
+template <>
+__device__ __forceinline__ float2 lds_pair_raw<int16_t>(const unsigned char* p) {
+  const short2 v = *reinterpret_cast<const short2*>(p);
+  return make_float2(static_cast<float>(v.x), static_cast<float>(v.y));
+}
+
 template <typename T>
 constexpr float kSampleScale = std::is_same<T, int16_t>::value ? (1.0f / 32768.0f) : 1.0f;
 
@@ -238,7 +251,13 @@ __device__ __forceinline__ void split_pair(float* pk, float* pm, float2 zk, floa
 template <int N1, int N2>
 constexpr int kMinWavesPerSimd = (N1 * N2 <= 512) ? 2 : 1;
 
-template <int N1, int N2, typename InT, int PMODE>
+// Shapes whose pass-1 threads hold all their samples in registers (N1 <= 8)
+// and load two or more frames each can copy a tile's samples into LDS first
+// (COPY variant, chosen per call); the others only gather.
+template <int N1, int N2>
+constexpr bool kCopyCapable = (N1 <= 8) && (N2 >= 8);
+
+template <int N1, int N2, typename InT, int PMODE, bool COPY>
 __global__ __launch_bounds__(256, (kMinWavesPerSimd<N1, N2>)) void mel_forward_kernel(KArgs a) {
   constexpr int M = N1 * N2;
   constexpr int K = M + 1;        // one-sided bins
@@ -278,7 +297,8 @@ __global__ __launch_bounds__(256, (kMinWavesPerSimd<N1, N2>)) void mel_forward_k
     const InT* x = static_cast<const InT*>(a.in) + static_cast<long long>(b) * L;
 
     // ---- pass 1: window + N1-point DFTs, twiddle, exchange through LDS ----
-    if (slot < SLOTS) {
+    const bool p1 = slot < SLOTS;  // threads with a pass-1 role
+    {
       float2 win[kHoist ? N1 : 1], twv[kHoist ? N1 : 1];
       if constexpr (kHoist) {
 #pragma unroll
@@ -327,17 +347,60 @@ __global__ __launch_bounds__(256, (kMinWavesPerSimd<N1, N2>)) void mel_forward_k
           yrow[k1 * N2] = cmul(v[k1], kHoist ? twv[kHoist ? k1 : 0] : a.tw_m[n2 * k1]);
       };
       if constexpr (kHoist) {
-        // every frame of this thread is fetched before any is computed, so
-        // the whole tile's loads are in flight at once
+        // Every frame of this thread is loaded before any is computed.  A
+        // tile whose samples lie inside the signal first copies its whole
+        // contiguous span into LDS with 16-byte direct loads (a few wide
+        // instructions per wave instead of one 8-byte gather per sample
+        // pair, and each sample read once instead of n_fft/hop times); the
+        // copy aliases the exchange buffer, so every thread takes its
+        // samples into registers before the first Y store.  Edge tiles
+        // gather through the padding index map.
         constexpr int RMAX = (64 + SLOTS - 1) / SLOTS;
+        constexpr int ES = static_cast<int>(sizeof(InT));
         float2 sb[RMAX][N1];
+        const int base0 = t0 * a.hop - a.pad;  // first sample of the tile
+        const int span = (nvalid - 1) * a.hop + NF;
+        const uintptr_t xa = reinterpret_cast<uintptr_t>(x);
+        const uintptr_t b_lo = xa + static_cast<uintptr_t>(static_cast<long long>(base0) * ES);
+        const uintptr_t g_lo = b_lo & ~static_cast<uintptr_t>(15);
+        const uintptr_t g_hi = (b_lo + static_cast<uintptr_t>(span) * ES + 15) & ~static_cast<uintptr_t>(15);
+        const bool copy = COPY && base0 >= 0 && base0 + span <= L && g_lo >= xa &&
+                          g_hi <= xa + static_cast<uintptr_t>(L) * ES && (b_lo % (2 * ES)) == 0 &&
+                          (a.hop % 2) == 0;  // wave-uniform: depends on the tile only
+        if (copy) {
+          const int n16 = static_cast<int>((g_hi - g_lo) >> 4);
+          for (int c = wave; c * 64 < n16; c += 4) {
+            const int q = c * 64 + lane;
+            if (q < n16)
+              __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(g_lo + static_cast<uintptr_t>(q) * 16),
+                                               lds + c * 1024, 16, 0, 0);
+          }
+          __builtin_amdgcn_s_waitcnt(0);  // the copies have landed
+          __syncthreads();
+          const unsigned char* r0 = lds + (b_lo - g_lo);
+          if (p1) {
 #pragma unroll
-        for (int r = 0; r < RMAX; ++r)
-          if (slot + SLOTS * r < nvalid) fetch(slot + SLOTS * r, sb[r]);
+            for (int r = 0; r < RMAX; ++r) {
+              const int f = slot + SLOTS * r;
+              if (f < nvalid) {
 #pragma unroll
-        for (int r = 0; r < RMAX; ++r)
-          if (slot + SLOTS * r < nvalid) compute(slot + SLOTS * r, sb[r]);
-      } else {
+                for (int n1 = 0; n1 < N1; ++n1)
+                  sb[r][n1] = lds_pair_raw<InT>(r0 + (f * a.hop + 2 * (N2 * n1 + n2)) * ES);
+              }
+            }
+          }
+          __syncthreads();  // the copy is consumed: Y may overwrite it
+        } else if (p1) {
+#pragma unroll
+          for (int r = 0; r < RMAX; ++r)
+            if (slot + SLOTS * r < nvalid) fetch(slot + SLOTS * r, sb[r]);
+        }
+        if (p1) {
+#pragma unroll
+          for (int r = 0; r < RMAX; ++r)
+            if (slot + SLOTS * r < nvalid) compute(slot + SLOTS * r, sb[r]);
+        }
+      } else if (p1) {
         for (int f = slot; f < nvalid; f += SLOTS) {
           float2 s0[N1];
           fetch(f, s0);
@@ -463,24 +526,32 @@ __global__ __launch_bounds__(256, (kMinWavesPerSimd<N1, N2>)) void mel_forward_k
 
 }  // namespace
 
-// Kernel entry of one FFT shape for an input type and power mode
-// (0: p = 2, 1: p = 1, 2: general p); instantiated in fm_shape_<N1>x<N2>.hip.
+// Kernel entry of one FFT shape for an input type, a power mode (0: p = 2,
+// 1: p = 1, 2: general p) and the tile-copy variant (only for shapes that
+// support it); instantiated in fm_shape_<N1>x<N2>.hip.
 template <int N1, int N2>
-void* kernel_for(int in_dtype, int pmode) {
-  auto pick = [](auto in_tag, int pm) -> void* {
+void* kernel_for(int in_dtype, int pmode, bool copy) {
+  auto pick = [](auto in_tag, auto copy_tag, int pm) -> void* {
     using InT = decltype(in_tag);
-    if (pm == 0) return reinterpret_cast<void*>(&mel_forward_kernel<N1, N2, InT, 0>);
-    if (pm == 1) return reinterpret_cast<void*>(&mel_forward_kernel<N1, N2, InT, 1>);
-    return reinterpret_cast<void*>(&mel_forward_kernel<N1, N2, InT, 2>);
+    constexpr bool C = decltype(copy_tag)::value;
+    if (pm == 0) return reinterpret_cast<void*>(&mel_forward_kernel<N1, N2, InT, 0, C>);
+    if (pm == 1) return reinterpret_cast<void*>(&mel_forward_kernel<N1, N2, InT, 1, C>);
+    return reinterpret_cast<void*>(&mel_forward_kernel<N1, N2, InT, 2, C>);
   };
-  if (in_dtype == FM_I16) return pick(int16_t{}, pmode);
-  return pick(float{}, pmode);
+  using Yes = std::integral_constant<bool, kCopyCapable<N1, N2>>;
+  using No = std::false_type;
+  if (copy && kCopyCapable<N1, N2>) {
+    if (in_dtype == FM_I16) return pick(int16_t{}, Yes{}, pmode);
+    return pick(float{}, Yes{}, pmode);
+  }
+  if (in_dtype == FM_I16) return pick(int16_t{}, No{}, pmode);
+  return pick(float{}, No{}, pmode);
 }
 
 // Shapes built into the library (n_fft/2 = N1 * N2).
 #define FM_FOR_EACH_SHAPE(X) \
   X(8, 4) X(8, 8) X(8, 16) X(8, 25) X(16, 16) X(32, 16) X(32, 32) X(64, 32)
-#define FM_DECLARE_SHAPE(A, B) extern template void* kernel_for<A, B>(int, int);
+#define FM_DECLARE_SHAPE(A, B) extern template void* kernel_for<A, B>(int, int, bool);
 FM_FOR_EACH_SHAPE(FM_DECLARE_SHAPE)
 #undef FM_DECLARE_SHAPE
 

@@ -15,10 +15,19 @@ namespace {
 
 int power_mode(const Plan& p) { return p.power == 2.0 ? 0 : (p.power == 1.0 ? 1 : 2); }
 
-void* select_kernel(const Plan& p, int in_dtype) {
+// Whole-tile sample copy (the COPY kernel variant) for this plan.  The
+// exchange buffer (G x (n_fft/2 + 4) complex) holds a tile's span ((G-1) hop
+// + n_fft samples + 32 bytes of alignment) whenever hop <= n_fft.  The copy
+// must land before any frame is computed, whereas the per-frame gather lets
+// early frames compute while later ones load; measured, the copy pays where
+// frames overlap at least 4 times (each sample gathered 4+ times): n_fft
+// 128/256 at hop n_fft/4 run 6-9% faster, n_fft 400 at hop 160 2% slower.
+bool use_tile_copy(const Plan& p) { return 4 * p.hop <= p.n_fft; }
+
+void* select_kernel(const Plan& p, int in_dtype, bool copy) {
   const int pm = power_mode(p);
 #define FM_SELECT_SHAPE(A, B) \
-  if (p.fft.n1 == A && p.fft.n2 == B) return kernel_for<A, B>(in_dtype, pm);
+  if (p.fft.n1 == A && p.fft.n2 == B) return kernel_for<A, B>(in_dtype, pm, copy);
   FM_FOR_EACH_SHAPE(FM_SELECT_SHAPE)
 #undef FM_SELECT_SHAPE
   return nullptr;
@@ -83,7 +92,7 @@ int upload_plan(Plan& p) {
   p.d_blk_w = base + o_bw;
   // Tiles above 64 KB of LDS need the per-kernel opt-in.
   for (int dt : {FM_F32, FM_I16}) {
-    void* k = select_kernel(p, dt);
+    void* k = select_kernel(p, dt, use_tile_copy(p));
     if (!k) return set_error(FM_E_UNSUPPORTED, "no kernel for this n_fft");
     e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, p.lds_bytes);
     if (e != hipSuccess) return hip_fail(e, "hipFuncSetAttribute");
@@ -173,7 +182,7 @@ int launch_forward(const Plan& p, const void* in, int in_dtype, int64_t batch, i
   a.w_lds = tile_weights_offset(p, G);
   a.out_f16 = p.out_dtype == FM_F16 ? 1 : 0;
 
-  void* k = select_kernel(p, in_dtype);
+  void* k = select_kernel(p, in_dtype, use_tile_copy(p));
   if (!k) return set_error(FM_E_UNSUPPORTED, "no kernel for this n_fft");
   void* args[] = {&a};
   e = hipLaunchKernel(k, dim3(static_cast<unsigned>(n_tiles)), dim3(p.threads), args,

@@ -2,5 +2,5 @@
 #include "fm_kernel.h"
 
 namespace fm {
-template void* kernel_for<8, 16>(int, int);
+template void* kernel_for<8, 16>(int, int, bool);
 }  // namespace fm

@@ -2,5 +2,5 @@
 #include "fm_kernel.h"
 
 namespace fm {
-template void* kernel_for<8, 25>(int, int);
+template void* kernel_for<8, 25>(int, int, bool);
 }  // namespace fm
