@@ -102,6 +102,7 @@ struct Plan {
   bool has_device = false;
   int device = -1;
   int n_cu = 0;                // compute units of that device
+  std::vector<int> wg_per_cu;  // [tile frames] resident workgroups per CU
   void* d_block = nullptr;     // one allocation holding every table
   const void* d_win2 = nullptr;   // float2[M] : 0.5*(w[2m], w[2m+1])
   const void* d_tw_m = nullptr;   // float2[M]

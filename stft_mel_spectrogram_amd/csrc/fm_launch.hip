@@ -97,6 +97,15 @@ int upload_plan(Plan& p) {
     e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, p.lds_bytes);
     if (e != hipSuccess) return hip_fail(e, "hipFuncSetAttribute");
   }
+  // Resident workgroups per CU for each tile size (registers and LDS).
+  p.wg_per_cu.assign(p.tile_max + 1, 1);
+  if (void* k = select_kernel(p, FM_F32, use_tile_copy(p))) {
+    for (int g = 1; g <= p.tile_max; ++g) {
+      int n = 0;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k, p.threads, tile_lds_bytes(p, g)) == hipSuccess)
+        p.wg_per_cu[g] = std::max(1, n);
+    }
+  }
   p.has_device = true;
   return FM_OK;
 }
@@ -115,17 +124,24 @@ void free_plan_device(Plan& p) {
 
 namespace {
 
-// Frames per tile for this call: the largest tile whose busiest compute
-// unit holds the fewest frames (all tiles resident at once when they fit).
+// Frames per tile for this call.  Rounds of resident workgroups times the
+// time of one workgroup, which grows with its pass-1 rounds (frames per
+// thread) on top of a fixed part (pass 2, split, mel) worth about 3 of them;
+// ties go to smaller tiles (more compute units busy for small calls).
+// Measured: n_fft 2048 x 64 signals picks 16 frames (7 rounds of 1 per CU:
+// 127 us) where "fewest frames on the busiest CU" picked 12 (9 rounds:
+// 160 us); whisper shape 47 and n_fft 1024 x 8 signals 8 are unchanged.
 int choose_tile(const Plan& p, int64_t batch, int64_t T) {
   if (p.tile_override > 0) return p.tile_override;
   const int ncu = p.n_cu > 0 ? p.n_cu : 256;
+  const int slots = std::max(1, p.threads / p.fft.n2);  // frames per pass-1 round
   int best = p.tile_max;
   int64_t best_cost = INT64_MAX;
-  for (int g = p.tile_max; g >= 1 && g * 2 >= p.tile_max; --g) {
+  for (int g = (p.tile_max + 1) / 2; g <= p.tile_max; ++g) {
     const int64_t tiles = batch * ((T + g - 1) / g);
-    const int64_t per_cu = (tiles + ncu - 1) / ncu;
-    const int64_t cost = per_cu * g;
+    const int occ = (g < static_cast<int>(p.wg_per_cu.size()) && p.wg_per_cu[g] > 0) ? p.wg_per_cu[g] : 1;
+    const int64_t rounds = (tiles + static_cast<int64_t>(ncu) * occ - 1) / (static_cast<int64_t>(ncu) * occ);
+    const int64_t cost = rounds * ((g + slots - 1) / slots + 3);
     if (cost < best_cost) {
       best_cost = cost;
       best = g;
