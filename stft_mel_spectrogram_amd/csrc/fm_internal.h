@@ -45,6 +45,15 @@ constexpr int kMelTileOverrun = 16;
 // slack at its end.
 constexpr int kMelGlobalWeightsFrom = 2048;
 constexpr int kMelGlobalChunk = 32;
+
+// Pass-1 tables (the window pairs and the twiddles exp(-2 pi i n2 k1 / M),
+// 16*M bytes) of shapes that cannot hold them in registers (N1 > 8) are
+// either read from global memory per frame or copied into LDS behind the
+// exchange buffer at the start.  Measured: the copy pays for N1 = 16
+// (n_fft 512: two pass-1 rounds per thread at 2 workgroups per CU, 22.0 ->
+// 20.4 us on asr512) and costs for N1 = 32 (n_fft 1024/2048: the copy's wait
+// lands on a single round per thread: 13.6 -> 14.8 us, 124 -> 135 us).
+constexpr bool tables_in_lds(int n1, int m) { return n1 == 16 && m < kMelGlobalWeightsFrom; }
 // Tiles of more than this many frames write their mel rows through a
 // per-wave LDS staging area (one contiguous store per row, rows long enough
 // to cover whole cache lines); narrower tiles store the MFMA results directly.
@@ -121,12 +130,14 @@ const char* last_error_cstr();
 int build_host_plan(Plan& p, const fm_args& a);
 void default_args(fm_args* a);
 
-// LDS layout of a tile of `frames` frames: the FFT exchange buffer, which
-// later holds the power tile, its zeroed overrun floats, (from float
+// LDS layout of a tile of `frames` frames: the FFT exchange buffer (during
+// pass 1 followed by the pass-1 tables where tables_in_lds), which later
+// holds the power tile, its zeroed overrun floats, (from float
 // tile_weights_offset) the mel block weights and, for wide tiles, the 4
 // waves' output staging areas right after them.
 int tile_exchange_bytes(const Plan& p, int frames);
 int tile_weights_offset(const Plan& p, int frames);
+int tile_tables_offset(const Plan& p, int frames);  // bytes; pass-1 tables in LDS
 int tile_lds_bytes(const Plan& p, int frames);
 
 // Frames per signal for a plan (negative FM_E_* on invalid length).

@@ -58,6 +58,7 @@ struct KArgs {
                         // 0 when the shape reads them from global memory)
   int w_lds;            // LDS float offset of the copied weights
   int out_f16;          // 1: the output is float16
+  int tab_lds;          // LDS byte offset of the pass-1 tables (tables_in_lds)
 };
 
 namespace {
@@ -268,9 +269,13 @@ __global__ __launch_bounds__(256, (kMinWavesPerSimd<N1, N2>)) void mel_forward_k
   constexpr int SLOTS = 256 / N2; // frames per pass-1 round (one thread per n2)
   constexpr bool kHoist = N1 <= 8;   // window and twiddles in registers,
                                      // next frame's samples prefetched
+  constexpr bool kTabLds = tables_in_lds(N1, M);  // else: tables in LDS, or global
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   float2* Y = reinterpret_cast<float2*>(lds);  // Y[f][k1][n2]
   float* P = reinterpret_cast<float*>(lds);    // P[f][k], aliases Y
+  // pass-1 tables copied behind Y (kTabLds): window pairs, then twiddles
+  const float2* tab_win = reinterpret_cast<const float2*>(lds + a.tab_lds);
+  const float2* tab_tw = tab_win + M;
 
   const int tid = threadIdx.x;
   const int G = a.tile;
@@ -334,7 +339,7 @@ __global__ __launch_bounds__(256, (kMinWavesPerSimd<N1, N2>)) void mel_forward_k
           if constexpr (kHoist) {
             w = win[kHoist ? n1 : 0];  // already scaled for int16
           } else {
-            w = a.win2[N2 * n1 + n2];
+            w = kTabLds ? tab_win[N2 * n1 + n2] : a.win2[N2 * n1 + n2];
             w = make_float2(w.x * kSampleScale<InT>, w.y * kSampleScale<InT>);
           }
           v[n1] = make_float2(s[n1].x * w.x, s[n1].y * w.y);
@@ -344,7 +349,8 @@ __global__ __launch_bounds__(256, (kMinWavesPerSimd<N1, N2>)) void mel_forward_k
         yrow[0] = v[0];
 #pragma unroll
         for (int k1 = 1; k1 < N1; ++k1)
-          yrow[k1 * N2] = cmul(v[k1], kHoist ? twv[kHoist ? k1 : 0] : a.tw_m[n2 * k1]);
+          yrow[k1 * N2] = cmul(v[k1], kHoist ? twv[kHoist ? k1 : 0]
+                                             : (kTabLds ? tab_tw[n2 * k1] : a.tw_m[n2 * k1]));
       };
       if constexpr (kHoist) {
         // Every frame of this thread is loaded before any is computed.  A
@@ -399,6 +405,21 @@ __global__ __launch_bounds__(256, (kMinWavesPerSimd<N1, N2>)) void mel_forward_k
 #pragma unroll
           for (int r = 0; r < RMAX; ++r)
             if (slot + SLOTS * r < nvalid) compute(slot + SLOTS * r, sb[r]);
+        }
+      } else if constexpr (kTabLds) {
+        // the tables land in LDS while the first frame's samples load
+        for (int c = wave; c < M / 64; c += 4)
+          __builtin_amdgcn_global_load_lds(reinterpret_cast<const float*>(a.win2) + c * 256 + lane * 4,
+                                           lds + a.tab_lds + c * 1024, 16, 0, 0);
+        float2 s0[N1];
+        if (p1 && slot < nvalid) fetch(slot, s0);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (p1) {
+          for (int f = slot; f < nvalid; f += SLOTS) {
+            if (f != slot) fetch(f, s0);
+            compute(f, s0);
+          }
         }
       } else if (p1) {
         for (int f = slot; f < nvalid; f += SLOTS) {

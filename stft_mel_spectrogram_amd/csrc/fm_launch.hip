@@ -57,6 +57,9 @@ int upload_plan(Plan& p) {
   const size_t o_tbl = o_w + al(static_cast<size_t>(p.nnz > 0 ? p.nnz : 1) * sizeof(float));
   const size_t o_bw = o_tbl + al((8 + 4 * p.blocks.size()) * sizeof(int32_t));
   const size_t total = o_bw + al(std::max<size_t>(p.blk_w.size(), 1) * sizeof(float));
+  // the kernels copy win2 and tw_m as one block of 16*M bytes
+  if (o_twm != o_win + static_cast<size_t>(M) * sizeof(float2) && tables_in_lds(p.fft.n1, M))
+    return set_error(FM_E_HIP, "internal: pass-1 tables are not contiguous");
   std::vector<unsigned char> host(total, 0);
   float* win2 = reinterpret_cast<float*>(host.data() + o_win);
   for (int j = 0; j < p.n_fft; ++j) win2[j] = 0.5f * p.window[j];  // exact scaling
@@ -197,6 +200,7 @@ int launch_forward(const Plan& p, const void* in, int in_dtype, int64_t batch, i
   a.w_chunks = p.w_in_lds ? static_cast<int>(p.blk_w.size() / 256) : 0;
   a.w_lds = tile_weights_offset(p, G);
   a.out_f16 = p.out_dtype == FM_F16 ? 1 : 0;
+  a.tab_lds = tile_tables_offset(p, G);
 
   void* k = select_kernel(p, in_dtype, use_tile_copy(p));
   if (!k) return set_error(FM_E_UNSUPPORTED, "no kernel for this n_fft");
