@@ -267,6 +267,22 @@ def test_tile_copy_path(n_fft, dtype):
     assert_parity(y.cpu().numpy(), ref, f"copy {dtype} {n_fft} misaligned")
 
 
+@pytest.mark.parametrize("n_fft,tiles", [(400, [1, 7, 16, 17, 32, 33, 48, 49, 64]),
+                                         (128, [5, 64]), (1024, [1, 9, 16]), (4096, [3, 8])])
+def test_forced_tile_sizes(monkeypatch, n_fft, tiles):
+    """Every tile width the kernel has: 1..4 sixteen-frame column groups in
+    the mel stage, direct stores (<= 32 frames) and staged row stores (>= 33),
+    ragged last tiles; f32 and f16 output (FM_TILE_FRAMES forces the size)."""
+    x = np.random.default_rng(n_fft).standard_normal((2, 12_345)).astype(np.float32)
+    targs = dict(sample_rate=16000, n_fft=n_fft, hop_length=n_fft // 3, n_mels=72)
+    ref = oracle(x, **targs)
+    for g in tiles:
+        monkeypatch.setenv("FM_TILE_FRAMES", str(g))
+        assert_parity(run_gpu(x, **targs), ref, f"n_fft={n_fft} tile={g}")
+        assert_parity_f16(run_gpu(x, out_dtype=torch.float16, **targs), ref, f"f16 n_fft={n_fft} tile={g}")
+    monkeypatch.delenv("FM_TILE_FRAMES")
+
+
 def test_int16_odd_length_and_misaligned_input():
     from stft_mel_spectrogram_amd import MelSpectrogram
     _require_gpu()
