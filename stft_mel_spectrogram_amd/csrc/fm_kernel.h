@@ -267,9 +267,10 @@ __global__ __launch_bounds__(256, (kMinWavesPerSimd<N1, N2>)) void mel_forward_k
   constexpr int NF = 2 * M;       // n_fft
   constexpr int NPAIR = N1 / 2;   // pass-2 threads per frame
   constexpr int SLOTS = 256 / N2; // frames per pass-1 round (one thread per n2)
-  constexpr bool kHoist = N1 <= 8;   // window and twiddles in registers,
-                                     // next frame's samples prefetched
-  constexpr bool kTabLds = tables_in_lds(N1, M);  // else: tables in LDS, or global
+  constexpr bool kHoist = N1 <= 8;   // window and twiddles in registers, all of
+                                     // a thread's samples loaded before compute
+  constexpr bool kTabLds = tables_in_lds(N1, M);  // !kHoist: pass-1 tables copied into
+                                                  // LDS (else read per frame from L2)
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   float2* Y = reinterpret_cast<float2*>(lds);  // Y[f][k1][n2]
   float* P = reinterpret_cast<float*>(lds);    // P[f][k], aliases Y

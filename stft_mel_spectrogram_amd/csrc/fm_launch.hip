@@ -207,8 +207,8 @@ int launch_forward(const Plan& p, const void* in, int in_dtype, int64_t batch, i
   void* args[] = {&a};
   e = hipLaunchKernel(k, dim3(static_cast<unsigned>(n_tiles)), dim3(p.threads), args,
                       static_cast<size_t>(lds), static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "kernel launch");
-  e = hipGetLastError();
+  // (the launch's own status only: hipGetLastError would also report, and
+  // clear, an unrelated earlier failure on the caller's thread)
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
   return FM_OK;
 }
