@@ -321,6 +321,65 @@ def test_every_output_written_and_deterministic():
         assert torch.all(out1[:, m] == 0)
 
 
+def test_maximum_length_sampled_frames():
+    """length = 2^29 (the largest one launch takes; 2 GB of f32): frames at
+    both ends and inside against the oracle on excerpts (a prefix for the
+    first frames, a hop-aligned suffix for the last, exact slices inside);
+    one sample more is rejected."""
+    from stft_mel_spectrogram_amd import MelSpectrogram
+    from stft_mel_spectrogram_amd._native import FmError
+    _require_gpu()
+    n, hop, nfft = 1 << 29, 160, 400
+    targs = dict(sample_rate=16000, n_fft=nfft, hop_length=hop, n_mels=80)
+    rng = np.random.default_rng(29)
+    x = (rng.standard_normal(n, dtype=np.float32) * np.float32(0.1))
+    mel = MelSpectrogram(**targs)
+    xd = torch.from_numpy(x).cuda()
+    y = mel(xd)
+    torch.cuda.synchronize()
+    T = y.shape[-1]
+    assert T == 1 + n // hop
+    # first frames: the oracle on a prefix (centre padding reflects inside it)
+    pre = 20 * hop
+    ref = oracle(x[:pre], **targs)
+    assert_parity(y[:, :10].cpu().numpy(), ref[:, :10], "max length: first frames")
+    # last frames: a suffix starting on the frame grid
+    start = (n // hop - 20) * hop
+    ref = oracle(x[start:], **targs)
+    assert_parity(y[:, -5:].cpu().numpy(), ref[:, -5:], "max length: last frames")
+    # interior frames: exactly their samples, no centring
+    for t in (T // 3, T // 2, T - 40):
+        a0 = t * hop - nfft // 2
+        ref = oracle(x[a0:a0 + nfft], center=False, **targs)
+        assert_parity(y[:, t:t + 1].cpu().numpy(), ref, f"max length: frame {t}")
+    del y
+    with pytest.raises(FmError):
+        mel.plan.forward_ptr(xd.data_ptr(), 0, 1, n + 1, xd.data_ptr())
+
+
+def test_one_plan_on_two_streams():
+    """A plan is immutable: two streams may run it at the same time."""
+    from stft_mel_spectrogram_amd import MelSpectrogram
+    _require_gpu()
+    cfg = W.workload("whisper", batch=4, length=64_000)
+    mel = MelSpectrogram(**W.transform_args(cfg))
+    xa = torch.from_numpy(W.make_signal(cfg)).cuda()
+    xb = torch.from_numpy(W.make_signal(W.workload("whisper", batch=4, length=64_000, seed=9))).cuda()
+    ref_a, ref_b = mel(xa).clone(), mel(xb).clone()
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    for _ in range(5):
+        with torch.cuda.stream(s1):
+            ya = mel(xa)
+        with torch.cuda.stream(s2):
+            yb = mel(xb)
+        outs.append((ya, yb))
+    torch.cuda.synchronize()
+    for ya, yb in outs:
+        assert torch.equal(ya, ref_a) and torch.equal(yb, ref_b)
+
+
 def test_leading_dims_and_empty_batch():
     from stft_mel_spectrogram_amd import MelSpectrogram
     _require_gpu()
