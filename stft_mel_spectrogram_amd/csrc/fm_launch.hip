@@ -103,7 +103,7 @@ int upload_plan(Plan& p) {
   // Resident workgroups per CU for each tile size (registers and LDS).
   p.wg_per_cu.assign(p.tile_max + 1, 1);
   if (void* k = select_kernel(p, FM_F32, use_tile_copy(p))) {
-    for (int g = 1; g <= p.tile_max; ++g) {
+    for (int g = (p.tile_max + 1) / 2; g <= p.tile_max; ++g) {
       int n = 0;
       if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k, p.threads, tile_lds_bytes(p, g)) == hipSuccess)
         p.wg_per_cu[g] = std::max(1, n);
@@ -133,7 +133,11 @@ namespace {
 // ties go to smaller tiles (more compute units busy for small calls).
 // Measured: n_fft 2048 x 64 signals picks 16 frames (7 rounds of 1 per CU:
 // 127 us) where "fewest frames on the busiest CU" picked 12 (9 rounds:
-// 160 us); whisper shape 47 and n_fft 1024 x 8 signals 8 are unchanged.
+// 160 us); the whisper shape keeps 47.  Calls with fewer tiles than CUs
+// then shrink the tile while every tile still gets a CU of its own
+// (1 x 16000 samples: 1-frame tiles, 8.2 us, against 10.0 us with 32-frame
+// tiles; below that point, in calls of several rounds, the model above does
+// not rank small tiles reliably and they measured slower).
 int choose_tile(const Plan& p, int64_t batch, int64_t T) {
   if (p.tile_override > 0) return p.tile_override;
   const int ncu = p.n_cu > 0 ? p.n_cu : 256;
@@ -149,6 +153,10 @@ int choose_tile(const Plan& p, int64_t batch, int64_t T) {
       best_cost = cost;
       best = g;
     }
+  }
+  // A call that leaves CUs idle takes smaller tiles, down to one per CU.
+  if (batch * ((T + best - 1) / best) < ncu) {
+    while (best > 1 && batch * ((T + best - 2) / (best - 1)) <= ncu) --best;
   }
   return best;
 }
