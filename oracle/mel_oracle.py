@@ -21,8 +21,9 @@ maps for padding, a dense O(N^2) DFT whose angles are reduced on integers
 evaluated directly from their corner frequencies.  Library calls are used
 only as single steps (a matmul, a log10).
 
-Readings taken where the page leaves a step open are listed in the design doc
-("Readings of the pages").
+Where the page leaves a step open (it delegates the definitions to
+torchaudio), the reading taken is stated in the docstring of the function
+that implements that step.
 """
 from __future__ import annotations
 
