@@ -18,9 +18,9 @@
 //              X[k] = (Z[k] + conj Z[M-k]) - i W_N^k (Z[k] - conj Z[M-k])
 //           (window pre-scaled by 1/2) and |X|^p need no further exchange.
 // The power tile P[f][k] (odd frame stride n_fft/2+1) reuses the exchange
-// buffer (frame stride n_fft/2 + 4 complex values).  The mel projection is a block-sparse product on the matrix cores:
-// 16 filters x 16 frames per v_mfma_f32_16x16x4f32, over only the bins each
-// block of filters touches.
+// buffer (frame stride n_fft/2 + 4 complex values).  The mel projection is
+// a block-sparse product on the matrix cores: 16 filters x 16 frames per
+// v_mfma_f32_16x16x4f32, over only the bins each block of filters touches.
 #pragma once
 
 #include <hip/hip_runtime.h>

@@ -3,12 +3,16 @@
 // Everything the kernel reads besides the signal is built here once per plan,
 // in float64, and rounded once to float32:
 //   * the STFT window: periodic Hann of win_length, zero-padded centred to
-//     n_fft (flashmel 0.1.0 page, flashmel/filters.py make_window);
+//     n_fft, with the window / frame-length normalisation folded in
+//     (flashmel 0.1.0 page, flashmel/filters.py make_window);
 //   * the triangular mel filterbank in CSR form -- per mel the first bin of
 //     its contiguous support, the run length and the weights -- with empty
 //     filters kept as zero-length rows (flashmel/filters.py pack_fbank keeps
 //     per-mel start/width rows; README "How it works": the projection loop
 //     runs over each filter's actual width);
+//   * from the CSR rows, the blocks the kernel's matrix-core projection
+//     uses: 16 filters each over their common run of bins, dense in 4-bin
+//     steps in the MFMA operand order, shared out over the waves;
 //   * the twiddle tables of the complex FFT of n_fft/2 points that carries
 //     the real FFT, and of the real-FFT post-processing step;
 //   * the tile geometry of the kernel launch.
