@@ -9,6 +9,7 @@ from __future__ import annotations
 
 import glob
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -30,6 +31,27 @@ def sources() -> list:
 
 # Packed-FP32 VALU forms are switched off for all device code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Kernels must not use scratch (private) memory: on the MI355X a launch of a
+# kernel with any scratch costs about 20 us (2.4 us without), more than the
+# whole forward pass, so a register spill is a build error.  The compiler's
+# resource remarks report the scratch size of every kernel.
+RESOURCE_FLAGS = ["-Rpass-analysis=kernel-resource-usage"]
+_REMARK_NAME = re.compile(r"remark:\s+Function Name: (\S+)")
+_REMARK_SCRATCH = re.compile(r"remark:\s+ScratchSize \[bytes/lane\]: (\d+)")
+
+
+def scratch_users(stderr: str) -> list:
+    """(kernel, bytes per lane) for every kernel whose remarks report scratch."""
+    out, name = [], None
+    for line in stderr.splitlines():
+        m = _REMARK_NAME.search(line)
+        if m:
+            name = m.group(1)
+            continue
+        m = _REMARK_SCRATCH.search(line)
+        if m and int(m.group(1)) > 0:
+            out.append((name, int(m.group(1))))
+    return out
 
 
 def hipcc() -> str:
@@ -47,14 +69,20 @@ def build(verbose: bool = False, arch: str = "gfx950", jobs: int = 0) -> str:
     try:
         def compile_one(src):
             obj = os.path.join(tmpdir, os.path.splitext(src)[0] + ".o")
-            cmd = [hipcc(), *common, "-c", os.path.join(CSRC, src), "-o", obj]
+            extra = RESOURCE_FLAGS if src.endswith(".hip") else []
+            cmd = [hipcc(), *common, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
             if verbose:
                 print(" ".join(cmd), flush=True)
             r = subprocess.run(cmd, capture_output=True, text=True)
             if r.returncode != 0:
                 raise RuntimeError(f"hipcc failed on {src} ({r.returncode}):\n{r.stderr[-8000:]}")
+            spills = scratch_users(r.stderr)
+            if spills:
+                raise RuntimeError(f"{src}: kernels use scratch memory (register spills), "
+                                   f"which costs ~20 us per launch: {spills}")
             if verbose and r.stderr.strip():
-                print(r.stderr[-4000:], file=sys.stderr)
+                print("\n".join(l for l in r.stderr.splitlines() if "kernel-resource-usage" not in l)[-4000:],
+                      file=sys.stderr)
             return obj
 
         srcs = sources()

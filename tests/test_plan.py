@@ -293,3 +293,22 @@ def test_forward_on_host_plan_and_bad_lengths():
     r = N.Plan(device=False, n_fft=400, hop_length=160, n_mels=80, center=False)
     with pytest.raises(N.FmError):
         r.out_frames(399)
+
+
+def test_build_rejects_kernels_that_use_scratch():
+    """The build fails on any kernel whose resource remarks report scratch
+    (a launch of such a kernel costs about 20 us on the MI355X); the parser
+    picks out exactly the kernels with a non-zero scratch size."""
+    from stft_mel_spectrogram_amd.build import RESOURCE_FLAGS, scratch_users
+    assert "-Rpass-analysis=kernel-resource-usage" in RESOURCE_FLAGS
+    remarks = "\n".join([
+        "k.hip:10:1: remark: Function Name: _Z4kern1v [-Rpass-analysis=kernel-resource-usage]",
+        "k.hip:10:1: remark:     VGPRs: 128 [-Rpass-analysis=kernel-resource-usage]",
+        "k.hip:10:1: remark:     ScratchSize [bytes/lane]: 0 [-Rpass-analysis=kernel-resource-usage]",
+        "k.hip:20:1: remark: Function Name: _Z4kern2v [-Rpass-analysis=kernel-resource-usage]",
+        "k.hip:20:1: remark:     ScratchSize [bytes/lane]: 12 [-Rpass-analysis=kernel-resource-usage]",
+        "k.hip:30:1: remark: Function Name: _Z4kern3v [-Rpass-analysis=kernel-resource-usage]",
+        "k.hip:30:1: remark:     ScratchSize [bytes/lane]: 8 [-Rpass-analysis=kernel-resource-usage]",
+    ])
+    assert scratch_users(remarks) == [("_Z4kern2v", 12), ("_Z4kern3v", 8)]
+    assert scratch_users("") == []
