@@ -51,9 +51,13 @@ constexpr int kMelGlobalChunk = 32;
 // either read from global memory per frame or copied into LDS behind the
 // exchange buffer at the start.  Measured: the copy pays for N1 = 16
 // (n_fft 512: two pass-1 rounds per thread at 2 workgroups per CU, 22.0 ->
-// 20.4 us on asr512) and costs for N1 = 32 (n_fft 1024/2048: the copy's wait
-// lands on a single round per thread: 13.6 -> 14.8 us, 124 -> 135 us).
-constexpr bool tables_in_lds(int n1, int m) { return n1 == 16 && m < kMelGlobalWeightsFrom; }
+// 20.4 us on asr512) and for n_fft 2048 with 8-wave workgroups (every
+// thread's 63 table reads per frame from L2 otherwise; 64 x 220500 samples:
+// 127.7 -> 112.8 us, while either change alone gains nothing); it costs for
+// n_fft 1024 (one round per thread: 13.6 -> 14.8 us).
+constexpr bool tables_in_lds(int n1, int m) {
+  return (n1 == 16 || (n1 == 32 && m == 1024)) && m < kMelGlobalWeightsFrom;
+}
 // Tiles of more than this many frames write their mel rows through a
 // per-wave LDS staging area (one contiguous store per row, rows long enough
 // to cover whole cache lines); narrower tiles store the MFMA results directly.
@@ -72,6 +76,11 @@ constexpr int kExchangePad = 4;
 constexpr int kPowerPad = 0;
 constexpr int exchange_stride(int half) { return half + kExchangePad; }
 constexpr int power_stride(int half) { return half + 1 + kPowerPad; }
+
+// Threads per workgroup of an FFT shape.  n_fft = 2048 (32 x 32) tiles fill
+// the LDS of a CU on their own; 8 waves instead of 4 give the CU two waves
+// per SIMD and each pass-1 thread a single frame.
+constexpr int threads_for(int n1, int n2) { return (n1 == 32 && n2 == 32) ? 512 : 256; }
 
 // FFT factorisation of the complex transform of n_fft/2 points that carries
 // the real FFT (even samples as real part, odd samples as imaginary part).

@@ -247,10 +247,14 @@ __device__ __forceinline__ void split_pair(float* pk, float* pm, float2 zk, floa
   *pm = power_of<PMODE>(fmaf(bx, bx, by * by), hp);
 }
 
-// Two workgroups per compute unit (2 waves per SIMD, <= 256 registers each)
-// wherever two tiles fit the LDS; n_fft = 2048 tiles take the whole LDS.
+// Two waves per SIMD (<= 256 registers each): two workgroups per compute
+// unit wherever two tiles fit the LDS, or one workgroup of 8 waves
+// (n_fft = 2048, whose tile takes the whole LDS); n_fft = 4096 runs one wave
+// per SIMD.
 template <int N1, int N2>
-constexpr int kMinWavesPerSimd = (N1 * N2 <= 512) ? 2 : 1;
+constexpr int kMinWavesPerSimd = (N1 * N2 <= 1024) ? 2 : 1;
+template <int N1, int N2>
+constexpr int kThreads = threads_for(N1, N2);
 
 // Shapes whose pass-1 threads hold all their samples in registers (N1 <= 8)
 // and load two or more frames each can copy a tile's samples into LDS first
@@ -259,14 +263,16 @@ template <int N1, int N2>
 constexpr bool kCopyCapable = (N1 <= 8) && (N2 >= 8);
 
 template <int N1, int N2, typename InT, int PMODE, bool COPY>
-__global__ __launch_bounds__(256, (kMinWavesPerSimd<N1, N2>)) void mel_forward_kernel(KArgs a) {
+__global__ __launch_bounds__((kThreads<N1, N2>), (kMinWavesPerSimd<N1, N2>)) void mel_forward_kernel(KArgs a) {
   constexpr int M = N1 * N2;
   constexpr int K = M + 1;        // one-sided bins
   constexpr int SY = exchange_stride(M);  // LDS frame strides (padded)
   constexpr int SP = power_stride(M);
   constexpr int NF = 2 * M;       // n_fft
   constexpr int NPAIR = N1 / 2;   // pass-2 threads per frame
-  constexpr int SLOTS = 256 / N2; // frames per pass-1 round (one thread per n2)
+  constexpr int NT = kThreads<N1, N2>;  // threads of the workgroup
+  constexpr int NW = NT / 64;           // waves
+  constexpr int SLOTS = NT / N2;  // frames per pass-1 round (one thread per n2)
   constexpr bool kHoist = N1 <= 8;   // window and twiddles in registers, all of
                                      // a thread's samples loaded before compute
   constexpr bool kTabLds = tables_in_lds(N1, M);  // !kHoist: pass-1 tables copied into
@@ -376,7 +382,7 @@ __global__ __launch_bounds__(256, (kMinWavesPerSimd<N1, N2>)) void mel_forward_k
                           (a.hop % 2) == 0;  // wave-uniform: depends on the tile only
         if (copy) {
           const int n16 = static_cast<int>((g_hi - g_lo) >> 4);
-          for (int c = wave; c * 64 < n16; c += 4) {
+          for (int c = wave; c * 64 < n16; c += NW) {
             const int q = c * 64 + lane;
             if (q < n16)
               __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(g_lo + static_cast<uintptr_t>(q) * 16),
@@ -409,7 +415,7 @@ __global__ __launch_bounds__(256, (kMinWavesPerSimd<N1, N2>)) void mel_forward_k
         }
       } else if constexpr (kTabLds) {
         // the tables land in LDS while the first frame's samples load
-        for (int c = wave; c < M / 64; c += 4)
+        for (int c = wave; c < M / 64; c += NW)
           __builtin_amdgcn_global_load_lds(reinterpret_cast<const float*>(a.win2) + c * 256 + lane * 4,
                                            lds + a.tab_lds + c * 1024, 16, 0, 0);
         float2 s0[N1];
@@ -472,7 +478,7 @@ __global__ __launch_bounds__(256, (kMinWavesPerSimd<N1, N2>)) void mel_forward_k
     // Every read of the exchange buffer is done: stream the mel weights into
     // LDS behind the power tile (direct global -> LDS loads, 1 KB per wave
     // instruction, lane l's 16 bytes at l*16), landing while the split runs.
-    for (int c = wave; c < a.w_chunks; c += 4)
+    for (int c = wave; c < a.w_chunks; c += NW)
       __builtin_amdgcn_global_load_lds(a.blk_w + c * 256 + lane * 4, P + a.w_lds + c * 256, 16, 0, 0);
     // the mel stage may read a few floats past the power tile: keep them 0
     if (tid < kMelTileOverrun) P[G * SP + tid] = 0.0f;
@@ -518,7 +524,8 @@ __global__ __launch_bounds__(256, (kMinWavesPerSimd<N1, N2>)) void mel_forward_k
     //      16-frame column groups across the tile ---------------------------
     {
       CInt* tbl = (CInt*)(a.mel_tbl);  // address-space cast: scalar loads
-      const int bb = tbl[wave], be = tbl[wave + 1];
+      // (the blocks are shared out over the first kMelWaves waves)
+      const int bb = wave < kMelWaves ? tbl[wave] : 0, be = wave < kMelWaves ? tbl[wave + 1] : 0;
       const long long obase = static_cast<long long>(b) * a.n_mels * a.n_frames + t0;  // element offset
       const int nfb = (G + 15) >> 4;
       CInt* blk = tbl + 8;

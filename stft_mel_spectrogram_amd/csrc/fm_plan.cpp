@@ -193,6 +193,7 @@ int build_host_plan(Plan& p, const fm_args& a) {
   p.n_freqs = n_fft / 2 + 1;
   p.pad_left = center ? n_fft / 2 : 0;
   p.fft = fs;
+  p.threads = threads_for(fs.n1, fs.n2);
   const int M = n_fft / 2;
 
   // ---- window: periodic Hann of win_length, centred in n_fft, with the
