@@ -327,3 +327,109 @@ def mel_spectrogram(x, *, sample_rate: int = 16000, n_fft: int = 400,
         outs.append(np.swapaxes(P @ fb, -1, -2))             # [b, n_mels, T]
     out = np.concatenate(outs, axis=0)
     return out.reshape(lead + out.shape[-2:])
+
+
+# ---------------------------------------------------------------------------
+# Backward: vector-Jacobian product with respect to the input signal
+# ---------------------------------------------------------------------------
+
+
+def power_gradient(X: np.ndarray, dP: np.ndarray, power: float) -> np.ndarray:
+    """Gradient of sum(dP * |X|**power) with respect to (Re X, Im X), packed
+    as the complex number dRe + i*dIm.
+
+    d|X|^p / dRe = p*|X|^(p-2)*Re X (and likewise for Im), so the gradient is
+    p*dP*|X|^(p-2)*X; for power 2 that is 2*dP*X.  Reading (the page is
+    silent on it): where X = 0 and power != 2 the gradient is taken as 0, the
+    value torch's abs() backward gives there (sgn(0) = 0).
+    """
+    if power == 2.0:
+        return 2.0 * dP * X
+    mag = np.abs(X)
+    safe = np.where(mag > 0.0, mag, 1.0)
+    return np.where(mag > 0.0, power * dP * safe ** (power - 2.0) * X, 0.0)
+
+
+def dft_onesided_adjoint(dX: np.ndarray, n_fft: int) -> np.ndarray:
+    """Adjoint of dft_onesided as a real-linear map: given the gradient
+    dX = dRe + i*dIm of the K one-sided bins, the gradient of each real frame
+    sample is  sum_k dRe[k]*cos(theta_nk) - dIm[k]*sin(theta_nk),
+    since Re X[k] = sum_n f[n] cos(theta_nk) and Im X[k] = -sum_n f[n] sin(theta_nk).
+    """
+    c, s = _dft_basis(n_fft)
+    return dX.real @ c.T - dX.imag @ s.T
+
+
+def pad_signal_adjoint(g: np.ndarray, length: int, left: int, right: int, mode: str) -> np.ndarray:
+    """Adjoint of pad_signal: every padded position hands its gradient to the
+    source sample it was copied from; constant-zero positions drop theirs."""
+    idx = padded_index(np.arange(-left, length + right), length, mode)
+    keep = idx >= 0
+    out = np.zeros(g.shape[:-1] + (length,))
+    flat_out = out.reshape(-1, length)
+    flat_g = g.reshape(-1, g.shape[-1])
+    for r in range(flat_g.shape[0]):
+        np.add.at(flat_out[r], idx[keep], flat_g[r][keep])
+    return out
+
+
+def mel_spectrogram_vjp(x, grad_out, *, sample_rate: int = 16000, n_fft: int = 400,
+                        win_length: int | None = None, hop_length: int | None = None,
+                        f_min: float = 0.0, f_max: float | None = None, pad: int = 0,
+                        n_mels: int = 128, power: float = 2.0, normalized=False,
+                        center: bool = True, pad_mode: str = "reflect", norm=None,
+                        mel_scale: str = "htk", chunk: int = 1) -> np.ndarray:
+    """f64 gradient of sum(grad_out * mel_spectrogram(x)) with respect to x.
+
+    The forward chain (padding, framing, window, one-sided DFT, |X|**power,
+    mel projection) is run again and each step is replaced by its adjoint, in
+    reverse order: the transposed filterbank, power_gradient,
+    dft_onesided_adjoint, the window, overlap-add of the frames, and the
+    adjoint of the padding maps.  x is a float array (..., time); grad_out has
+    the forward output's shape (..., n_mels, T).  The derivative is with
+    respect to the float signal; integer PCM has no gradient.
+    """
+    win_length = n_fft if win_length is None else win_length
+    hop_length = win_length // 2 if hop_length is None else hop_length
+    f_max = float(sample_rate // 2) if f_max is None else float(f_max)
+    if pad_mode not in PAD_MODES:
+        raise ValueError(f"unknown pad_mode {pad_mode!r}")
+    xf = np.asarray(x)
+    if xf.dtype.kind != "f":
+        raise TypeError("the gradient is defined for floating-point input only")
+    xf = xf.astype(np.float64)
+    lead = xf.shape[:-1]
+    L = xf.shape[-1]
+    xf = xf.reshape(-1, L)
+    g = np.asarray(grad_out, dtype=np.float64).reshape((xf.shape[0],) + np.shape(grad_out)[-2:])
+    window = make_window(n_fft, win_length, normalized)
+    fb = mel_filterbank(n_fft // 2 + 1, f_min, f_max, n_mels, sample_rate, norm, mel_scale)
+    outs = []
+    for s in range(0, xf.shape[0], max(1, chunk)):
+        sig = xf[s:s + max(1, chunk)]
+        if pad > 0:
+            sig = pad_signal(sig, pad, pad, "constant")
+        lz = sig.shape[-1]
+        p = n_fft // 2 if center else 0
+        if center:
+            if pad_mode == "reflect" and p >= lz:
+                raise ValueError("reflect padding needs n_fft//2 < signal length")
+            sig = pad_signal(sig, p, p, pad_mode)
+        fr = frame_signal(sig, n_fft, hop_length)                  # [b, T, N]
+        T = fr.shape[-2]
+        X = dft_onesided(fr * window)                               # [b, T, K]
+        gs = g[s:s + max(1, chunk)]
+        if gs.shape[-1] != T or gs.shape[-2] != n_mels:
+            raise ValueError("grad_out must have the forward output's shape")
+        dP = np.swapaxes(gs, -1, -2) @ fb.T                         # [b, T, K]
+        dfr = dft_onesided_adjoint(power_gradient(X, dP, power), n_fft) * window
+        dsig = np.zeros(sig.shape)                                  # overlap-add
+        for t in range(T):
+            dsig[..., t * hop_length:t * hop_length + n_fft] += dfr[..., t, :]
+        if center:
+            dsig = pad_signal_adjoint(dsig, lz, p, p, pad_mode)
+        if pad > 0:
+            dsig = dsig[..., pad:pad + L]
+        outs.append(dsig)
+    out = np.concatenate(outs, axis=0)
+    return out.reshape(lead + (L,))
