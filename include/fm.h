@@ -159,6 +159,37 @@ int fm_forward(const fm_plan* plan, const void* in, int in_dtype,
                int64_t batch, int64_t length, void* out, void* stream);
 
 /*
+ * fm_backward -- enqueue the gradient of the forward pass with respect to
+ * its float32 input: grad_in = d/dx sum(grad_out * mel(x)).
+ *
+ * The flashmel 0.1.0 page (README "Usage") leaves the transform
+ * inference-only; the specux "Backends" page (section "Gradients") computes
+ * a spectrogram's gradient as the analytic adjoint, in kernels of the same
+ * family as the forward, with a bitwise-reproducible mode.  This entry point
+ * applies that adjoint, always deterministically: the transposed filterbank, the gradient of |X|^power
+ * (p |X|^(p-2) X, taken as 0 where X = 0 and power != 2), the adjoint of
+ * the one-sided DFT (an inverse real FFT), the window, overlap-add of the
+ * frames, and the adjoint of the padding (gradients of padded positions go
+ * to the samples they copy).
+ *
+ *   in        device pointer to the forward input [batch, length], float32,
+ *             row-major, contiguous (the spectrum is recomputed from it).
+ *   grad_out  device pointer to [batch, n_mels, n_frames] float32 (whatever
+ *             the plan's out_dtype), n_frames = fm_out_frames(plan, length).
+ *   grad_in   device pointer to [batch, length] float32; every element is
+ *             written (not accumulated).  Must not overlap the inputs.
+ *   batch, length  as for fm_forward.
+ *
+ * FM_E_UNSUPPORTED when the frames overlapping one sample exceed what one
+ * workgroup pass holds: hop >= n_fft / (c - 1) is needed, c = 64 frames for
+ * n_fft <= 256, 40 for 400, 32 for 512, 16 for 1024 and 2048, 8 for 4096
+ * (fewer when a large n_mels takes LDS).  One kernel launch; no
+ * allocation, no synchronisation.
+ */
+int fm_backward(const fm_plan* plan, const float* in, int64_t batch, int64_t length,
+                const float* grad_out, float* grad_in, void* stream);
+
+/*
  * fm_out_frames -- frames per signal for a given length (L = length + 2*pad):
  *   center: 1 + floor(L / hop) for even n_fft (generally
  *           1 + floor((L + 2*(n_fft/2) - n_fft) / hop));

@@ -70,6 +70,7 @@ def _load() -> ctypes.CDLL:
         "fm_plan_create_args": (I, [ctypes.POINTER(P), ctypes.POINTER(Args)]),
         "fm_plan_create_args_host": (I, [ctypes.POINTER(P), ctypes.POINTER(Args)]),
         "fm_forward": (I, [P, P, I, I64, I64, P, P]),
+        "fm_backward": (I, [P, P, I64, I64, P, P, P]),
         "fm_out_frames": (I64, [P, I64]),
         "fm_plan_destroy": (I, [P]),
         "fm_strerror": (ctypes.c_char_p, [I]),
@@ -186,6 +187,14 @@ class Plan:
         """Raw device-pointer entry (fm_forward)."""
         check(lib.fm_forward(self.handle, ctypes.c_void_p(in_ptr), int(in_dtype), int(batch),
                              int(length), ctypes.c_void_p(out_ptr), ctypes.c_void_p(stream)))
+
+    def backward_ptr(self, in_ptr: int, batch: int, length: int, grad_out_ptr: int,
+                     grad_in_ptr: int, stream: int = 0) -> None:
+        """Raw device-pointer entry (fm_backward): float32 signal, float32
+        output gradient [batch, n_mels, T] -> float32 signal gradient."""
+        check(lib.fm_backward(self.handle, ctypes.c_void_p(in_ptr), int(batch), int(length),
+                              ctypes.c_void_p(grad_out_ptr), ctypes.c_void_p(grad_in_ptr),
+                              ctypes.c_void_p(stream)))
 
     def close(self) -> None:
         if self._h:

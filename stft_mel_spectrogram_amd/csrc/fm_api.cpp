@@ -101,6 +101,12 @@ int fm_forward(const fm_plan* plan, const void* in, int in_dtype, int64_t batch,
   return fm::launch_forward(plan->p, in, in_dtype, batch, length, out, stream);
 }
 
+int fm_backward(const fm_plan* plan, const float* in, int64_t batch, int64_t length,
+                const float* grad_out, float* grad_in, void* stream) {
+  if (!plan) return fm::set_error(FM_E_INVAL, "plan must not be NULL");
+  return fm::launch_backward(plan->p, in, batch, length, grad_out, grad_in, stream);
+}
+
 int64_t fm_out_frames(const fm_plan* plan, int64_t length) {
   if (!plan) return fm::set_error(FM_E_INVAL, "plan must not be NULL");
   return fm::out_frames(plan->p, length);

@@ -77,6 +77,33 @@ constexpr int kPowerPad = 0;
 constexpr int exchange_stride(int half) { return half + kExchangePad; }
 constexpr int power_stride(int half) { return half + 1 + kPowerPad; }
 
+// Backward pass: the filters that touch one one-sided bin.  A triangular
+// filterbank puts every bin in at most two filters; an unused tap has
+// m = n_mels and weight 0.
+struct BinTap {
+  int32_t m0, m1;
+  float w0, w1;
+};
+
+// Threads of a backward workgroup: 256 for every shape.  (n_fft = 2048
+// tiles fill a CU's LDS on their own; at 256 threads a wave may use 512
+// registers, which the two 32-point rows of its second pass need.)
+constexpr int kBwdThreads = 256;
+// Waves per SIMD the backward kernel is built for: 2 (<= 256 registers each)
+// up to n_fft = 1024, else 1.
+constexpr int bwd_min_waves(int n1, int n2) { return n1 * n2 <= 512 ? 2 : 1; }
+
+// Most frames one backward pass of a workgroup can hold: its second FFT
+// pass gives each thread one frame's pair of rows (threads / (n1/2) frames),
+// and shapes with n1 <= 8 keep every frame's samples of a pass in registers
+// (at most 4 rounds of threads / n2 frames).
+constexpr int bwd_chunk_cap(int n1, int n2, int threads) {
+  const int pass2 = threads / (n1 / 2);
+  const int pass1 = n1 <= 8 ? 4 * (threads / n2) : 64;
+  const int c = pass2 < pass1 ? pass2 : pass1;
+  return c < 64 ? c : 64;
+}
+
 // Threads per workgroup of an FFT shape.  n_fft = 2048 (32 x 32) tiles fill
 // the LDS of a CU on their own; 8 waves instead of 4 give the CU two waves
 // per SIMD and each pass-1 thread a single frame.
@@ -129,6 +156,11 @@ struct Plan {
   const void* d_mel_w = nullptr;  // float[nnz]
   const void* d_mel_tbl = nullptr;    // int32[8 + 4*n_blocks]: wave_beg, pad, blocks
   const void* d_blk_w = nullptr;      // float[blk_w.size()]
+  // backward
+  std::vector<BinTap> taps;      // [n_fft/2 + 1]
+  int bwd_chunk_max = 0;         // frames per backward pass at most
+  std::vector<int> bwd_wg_per_cu;  // [chunk frames] resident backward workgroups per CU
+  const void* d_taps = nullptr;  // BinTap[n_fft/2 + 1]
 };
 
 // Thread-local error reporting.
@@ -149,6 +181,17 @@ int tile_weights_offset(const Plan& p, int frames);
 int tile_tables_offset(const Plan& p, int frames);  // bytes; pass-1 tables in LDS
 int tile_lds_bytes(const Plan& p, int frames);
 
+// LDS layout of a backward pass of `chunk` frames (floats from the start):
+// the exchange buffer (frame stride n_fft/2 + 4 complex), which after the
+// inverse transform holds the windowed frame gradients; at bwd_grad_offset
+// the bin gradients dP[f][k] (frame stride n_fft/2 + 1, odd); at
+// bwd_acc_offset the edge accumulators (2 * bwd_edge floats) and 2 floats
+// per wave for block sums.
+int bwd_edge(const Plan& p);  // samples at each signal end owned by edge workgroups
+int bwd_grad_offset(const Plan& p, int chunk);
+int bwd_acc_offset(const Plan& p, int chunk);
+int bwd_lds_bytes(const Plan& p, int chunk);
+
 // Frames per signal for a plan (negative FM_E_* on invalid length).
 int64_t out_frames(const Plan& p, int64_t length);
 
@@ -157,5 +200,7 @@ int upload_plan(Plan& p);
 void free_plan_device(Plan& p);
 int launch_forward(const Plan& p, const void* in, int in_dtype, int64_t batch,
                    int64_t length, void* out, void* stream);
+int launch_backward(const Plan& p, const float* in, int64_t batch, int64_t length,
+                    const float* grad_out, float* grad_in, void* stream);
 
 }  // namespace fm

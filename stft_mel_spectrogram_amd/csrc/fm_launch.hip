@@ -7,7 +7,7 @@
 #include <string>
 #include <vector>
 
-#include "fm_kernel.h"
+#include "fm_backward.h"
 
 namespace fm {
 
@@ -23,6 +23,15 @@ int power_mode(const Plan& p) { return p.power == 2.0 ? 0 : (p.power == 1.0 ? 1 
 // frames overlap at least 4 times (each sample gathered 4+ times): n_fft
 // 128/256 at hop n_fft/4 run 6-9% faster, n_fft 400 at hop 160 2% slower.
 bool use_tile_copy(const Plan& p) { return 4 * p.hop <= p.n_fft; }
+
+void* select_backward_kernel(const Plan& p) {
+  const int pm = power_mode(p);
+#define FM_SELECT_SHAPE(A, B) \
+  if (p.fft.n1 == A && p.fft.n2 == B) return backward_kernel_for<A, B>(pm);
+  FM_FOR_EACH_SHAPE(FM_SELECT_SHAPE)
+#undef FM_SELECT_SHAPE
+  return nullptr;
+}
 
 void* select_kernel(const Plan& p, int in_dtype, bool copy) {
   const int pm = power_mode(p);
@@ -56,7 +65,8 @@ int upload_plan(Plan& p) {
   const size_t o_w = o_rows + al(p.n_mels * sizeof(MelRow));
   const size_t o_tbl = o_w + al(static_cast<size_t>(p.nnz > 0 ? p.nnz : 1) * sizeof(float));
   const size_t o_bw = o_tbl + al((8 + 4 * p.blocks.size()) * sizeof(int32_t));
-  const size_t total = o_bw + al(std::max<size_t>(p.blk_w.size(), 1) * sizeof(float));
+  const size_t o_taps = o_bw + al(std::max<size_t>(p.blk_w.size(), 1) * sizeof(float));
+  const size_t total = o_taps + al(p.taps.size() * sizeof(BinTap));
   // the kernels copy win2 and tw_m as one block of 16*M bytes
   if (o_twm != o_win + static_cast<size_t>(M) * sizeof(float2) && tables_in_lds(p.fft.n1, M))
     return set_error(FM_E_HIP, "internal: pass-1 tables are not contiguous");
@@ -76,6 +86,7 @@ int upload_plan(Plan& p) {
     tbl[8 + 4 * j + 3] = p.blocks[j].mel0;
   }
   std::copy(p.blk_w.begin(), p.blk_w.end(), reinterpret_cast<float*>(host.data() + o_bw));
+  std::copy(p.taps.begin(), p.taps.end(), reinterpret_cast<BinTap*>(host.data() + o_taps));
   void* d = nullptr;
   e = hipMalloc(&d, total);
   if (e != hipSuccess) return set_error(FM_E_NOMEM, std::string("hipMalloc: ") + hipGetErrorString(e));
@@ -93,6 +104,7 @@ int upload_plan(Plan& p) {
   p.d_mel_w = base + o_w;
   p.d_mel_tbl = base + o_tbl;
   p.d_blk_w = base + o_bw;
+  p.d_taps = base + o_taps;
   // Tiles above 64 KB of LDS need the per-kernel opt-in.
   for (int dt : {FM_F32, FM_I16}) {
     void* k = select_kernel(p, dt, use_tile_copy(p));
@@ -107,6 +119,19 @@ int upload_plan(Plan& p) {
       int n = 0;
       if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k, p.threads, tile_lds_bytes(p, g)) == hipSuccess)
         p.wg_per_cu[g] = std::max(1, n);
+    }
+  }
+  // The backward kernel of the plan's power mode: LDS opt-in and residency.
+  p.bwd_wg_per_cu.assign(p.bwd_chunk_max + 1, 1);
+  if (p.bwd_chunk_max > 0) {
+    void* kb = select_backward_kernel(p);
+    if (!kb) return set_error(FM_E_UNSUPPORTED, "no backward kernel for this n_fft");
+    e = hipFuncSetAttribute(kb, hipFuncAttributeMaxDynamicSharedMemorySize, bwd_lds_bytes(p, p.bwd_chunk_max));
+    if (e != hipSuccess) return hip_fail(e, "hipFuncSetAttribute (backward)");
+    for (int c = 1; c <= p.bwd_chunk_max; ++c) {
+      int n = 0;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kb, kBwdThreads, bwd_lds_bytes(p, c)) == hipSuccess)
+        p.bwd_wg_per_cu[c] = std::max(1, n);
     }
   }
   p.has_device = true;
@@ -218,6 +243,98 @@ int launch_forward(const Plan& p, const void* in, int in_dtype, int64_t batch, i
   // (the launch's own status only: hipGetLastError would also report, and
   // clear, an unrelated earlier failure on the caller's thread)
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
+  return FM_OK;
+}
+
+namespace {
+
+// Frames per backward pass for this call.  A main workgroup recomputes the
+// `halo` frames before its tile, so a pass of c frames advances c - halo;
+// the cost model is the forward's (rounds of resident workgroups times a
+// workgroup's pass-1 rounds plus a fixed part), ties to smaller passes.
+int choose_bwd_chunk(const Plan& p, int64_t batch, int64_t T, int halo, int64_t n_edge) {
+  const int ncu = p.n_cu > 0 ? p.n_cu : 256;
+  const int slots = std::max(1, kBwdThreads / p.fft.n2);
+  int best = p.bwd_chunk_max;
+  int64_t best_cost = INT64_MAX;
+  for (int c = halo + 1; c <= p.bwd_chunk_max; ++c) {
+    const int g = c - halo;
+    const int64_t wgs = batch * ((T + g - 1) / g) + n_edge;
+    const int occ = p.bwd_wg_per_cu[c] > 0 ? p.bwd_wg_per_cu[c] : 1;
+    const int64_t per_round = static_cast<int64_t>(ncu) * occ;
+    const int64_t cost = (wgs + per_round - 1) / per_round * ((c + slots - 1) / slots + 4);
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = c;
+    }
+  }
+  return best;
+}
+
+}  // namespace
+
+int launch_backward(const Plan& p, const float* in, int64_t batch, int64_t length,
+                    const float* grad_out, float* grad_in, void* stream) {
+  if (!p.has_device) return set_error(FM_E_NODEVICE, "plan was built without device tables");
+  if (batch < 0) return set_error(FM_E_INVAL, "batch must be >= 0");
+  const int64_t T = out_frames(p, length);
+  if (T < 0) return static_cast<int>(T);
+  if (batch == 0) return FM_OK;
+  if (!in || !grad_out || !grad_in) return set_error(FM_E_INVAL, "null input, gradient or output pointer");
+  int cur = -1;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (cur != p.device) return set_error(FM_E_INVAL, "plan belongs to another device than the current one");
+  if (length > (1 << 29)) return set_error(FM_E_INVAL, "problem too large for one launch (length <= 2^29)");
+  const int halo = (p.n_fft - 1) / p.hop;
+  if (p.bwd_chunk_max < halo + 1)
+    return set_error(FM_E_UNSUPPORTED, "backward: hop too small for this n_fft (a workgroup pass holds " +
+                                           std::to_string(p.bwd_chunk_max) + " frames, the overlap needs " +
+                                           std::to_string(halo + 1) + ")");
+  const int edge = bwd_edge(p);
+  const int whole = 2 * static_cast<int64_t>(edge) >= length ? 1 : 0;
+  const int64_t n_edge = edge > 0 ? batch : 0;
+  const int chunk = choose_bwd_chunk(p, batch, T, halo, n_edge);
+  const int tile = chunk - halo;
+  const int64_t tiles = (T + tile - 1) / tile;
+  const int64_t n_main = whole ? 0 : batch * tiles;
+  if (n_main + n_edge > INT32_MAX) return set_error(FM_E_INVAL, "problem too large for one launch");
+
+  BArgs a;
+  a.in = in;
+  a.gout = grad_out;
+  a.gin = grad_in;
+  a.win2 = static_cast<const float2*>(p.d_win2);
+  a.tw_m = static_cast<const float2*>(p.d_tw_m);
+  a.tw_n = static_cast<const float2*>(p.d_tw_n);
+  a.taps = static_cast<const BinTap*>(p.d_taps);
+  a.length = length;
+  a.n_frames = static_cast<int>(T);
+  a.hop = p.hop;
+  a.pad = p.pad_left + p.zpad;
+  a.zpad = p.zpad;
+  a.pad_mode = p.pad_mode;
+  a.n_mels = p.n_mels;
+  a.tile = tile;
+  a.halo = halo;
+  a.tiles_per_signal = static_cast<int>(tiles);
+  a.n_edge = static_cast<int>(n_edge);
+  a.edge = edge;
+  a.whole = whole;
+  a.chunk = chunk;
+  const uintptr_t ia = reinterpret_cast<uintptr_t>(in);
+  a.vec_ok = (ia % 8 == 0) && (length % 2 == 0) && (p.hop % 2 == 0) && ((p.pad_left + p.zpad) % 2 == 0);
+  a.g_off = bwd_grad_offset(p, chunk);
+  a.acc_off = bwd_acc_offset(p, chunk);
+  a.power = static_cast<float>(p.power);
+  a.half_power = static_cast<float>(p.power * 0.5);
+
+  void* k = select_backward_kernel(p);
+  if (!k) return set_error(FM_E_UNSUPPORTED, "no backward kernel for this n_fft");
+  void* args[] = {&a};
+  e = hipLaunchKernel(k, dim3(static_cast<unsigned>(n_main + n_edge)), dim3(kBwdThreads), args,
+                      static_cast<size_t>(bwd_lds_bytes(p, chunk)), static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "backward kernel launch");
   return FM_OK;
 }
 

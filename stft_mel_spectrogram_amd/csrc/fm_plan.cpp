@@ -114,6 +114,22 @@ int tile_lds_bytes(const Plan& p, int frames) {
   return static_cast<int>(std::max<long>(pass1, after_fft));
 }
 
+int bwd_edge(const Plan& p) {
+  // centre padding that copies signal samples hands gradients back to the
+  // first and last n_fft/2 + 1 samples (constant padding copies none)
+  return (p.center && p.pad_mode != FM_PAD_CONSTANT) ? p.pad_left + 1 : 0;
+}
+
+int bwd_grad_offset(const Plan& p, int chunk) { return tile_exchange_bytes(p, chunk) / 4; }
+
+int bwd_acc_offset(const Plan& p, int chunk) {
+  return bwd_grad_offset(p, chunk) + std::max(chunk, 1) * p.n_freqs;
+}
+
+int bwd_lds_bytes(const Plan& p, int chunk) {
+  return (bwd_acc_offset(p, chunk) + 2 * bwd_edge(p) + 2 * (kBwdThreads / 64)) * 4;
+}
+
 int64_t out_frames(const Plan& p, int64_t length) {
   if (length < 1) return set_error(FM_E_INVAL, "length must be >= 1");
   const int64_t le = length + 2 * static_cast<int64_t>(p.zpad);  // zero-extended signal
@@ -250,6 +266,30 @@ int build_host_plan(Plan& p, const fm_args& a) {
   }
   p.nnz = static_cast<int>(p.mel_w.size());
 
+  // ---- backward taps: the (at most two) filters of every bin -------------
+  // A bin at frequency f has a positive weight in filter m only when
+  // f_pts[m] < f < f_pts[m+2]; with increasing corners that holds for two
+  // consecutive filters at most.
+  p.taps.assign(p.n_freqs, BinTap{n_mels, n_mels, 0.0f, 0.0f});
+  {
+    std::vector<int> used(p.n_freqs, 0);
+    for (int m = 0; m < n_mels; ++m)
+      for (int j = 0; j < p.rows[m].len; ++j) {
+        const int k = p.rows[m].first + j;
+        const float w = p.mel_w[p.rows[m].off + j];
+        if (used[k] == 0) {
+          p.taps[k].m0 = m;
+          p.taps[k].w0 = w;
+        } else if (used[k] == 1) {
+          p.taps[k].m1 = m;
+          p.taps[k].w1 = w;
+        } else {
+          return set_error(FM_E_UNSUPPORTED, "a frequency bin lies in more than two mel filters");
+        }
+        ++used[k];
+      }
+  }
+
   // ---- twiddles ------------------------------------------------------------
   p.tw_m.assign(2 * M, 0.0f);
   p.tw_n.assign(2 * M, 0.0f);
@@ -345,6 +385,11 @@ int build_host_plan(Plan& p, const fm_args& a) {
     return set_error(FM_E_UNSUPPORTED, "mel filterbank too large for the LDS of one tile");
   p.tile_max = tmax;
   p.lds_bytes = tile_lds_bytes(p, tmax);
+  // backward passes: as many frames as the kernel's registers and the LDS
+  // allow
+  int cmax = bwd_chunk_cap(fs.n1, fs.n2, kBwdThreads);
+  while (cmax > 1 && bwd_lds_bytes(p, cmax) > 160 * 1024) --cmax;
+  p.bwd_chunk_max = bwd_lds_bytes(p, cmax) <= 160 * 1024 ? cmax : 0;
   p.tile_override = 0;
   if (const char* e = std::getenv("FM_TILE_FRAMES")) {
     int v = std::atoi(e);

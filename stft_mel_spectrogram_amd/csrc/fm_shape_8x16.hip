@@ -1,6 +1,7 @@
 // Kernels for n_fft = 256: complex FFT of 128 = 8 x 16 points.
-#include "fm_kernel.h"
+#include "fm_backward.h"
 
 namespace fm {
 template void* kernel_for<8, 16>(int, int, bool);
+template void* backward_kernel_for<8, 16>(int);
 }  // namespace fm

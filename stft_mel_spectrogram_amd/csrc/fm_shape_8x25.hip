@@ -1,6 +1,7 @@
 // Kernels for n_fft = 400: complex FFT of 200 = 8 x 25 points.
-#include "fm_kernel.h"
+#include "fm_backward.h"
 
 namespace fm {
 template void* kernel_for<8, 25>(int, int, bool);
+template void* backward_kernel_for<8, 25>(int);
 }  // namespace fm

@@ -23,7 +23,7 @@ def header_functions():
 
 def test_library_exports_every_declared_function():
     names = header_functions()
-    assert {"fm_plan_create", "fm_forward", "fm_plan_destroy", "fm_out_frames",
+    assert {"fm_plan_create", "fm_forward", "fm_backward", "fm_plan_destroy", "fm_out_frames",
             "fm_strerror", "fm_last_error", "fm_plan_tables"} <= set(names)
     lib = ctypes.CDLL(N.LIB_PATH)
     for n in names:
@@ -274,6 +274,7 @@ def test_raw_enum_validation_and_null_handling():
     assert lib.fm_plan_create_host(None, *base, 1, 0, 0, 0) == N.FM_E_INVAL
     assert lib.fm_plan_destroy(None) == N.FM_OK
     assert lib.fm_forward(None, None, 0, 1, 1000, None, None) == N.FM_E_INVAL
+    assert lib.fm_backward(None, None, 1, 1000, None, None, None) == N.FM_E_INVAL
     assert lib.fm_out_frames(None, 100) == N.FM_E_INVAL
     assert b"NULL" in lib.fm_last_error()
     assert lib.fm_strerror(N.FM_E_UNSUPPORTED) == b"unsupported configuration"
@@ -283,6 +284,9 @@ def test_forward_on_host_plan_and_bad_lengths():
     p = N.Plan(device=False, n_fft=400, hop_length=160, n_mels=80)
     with pytest.raises(N.FmError) as e:
         p.forward_ptr(0, N.FM_F32, 1, 1000, 0)
+    assert e.value.status == N.FM_E_NODEVICE
+    with pytest.raises(N.FmError) as e:
+        p.backward_ptr(0, 1, 1000, 0, 0)
     assert e.value.status == N.FM_E_NODEVICE
     with pytest.raises(N.FmError) as e:
         p.out_frames(200)          # reflect needs length > n_fft/2
