@@ -7,6 +7,12 @@ Whisper-shaped case).  Inputs are resident in HBM before timing starts.  To
 keep the 256 MB Infinity Cache from serving the data, the steps rotate over
 enough input/output buffer sets to exceed 2 x 256 MB.
 
+With --backward a step is one fm_backward launch instead (the gradient of
+sum(grad_out * mel(x)) with respect to the float32 signal), over the same
+rotation of buffer sets (signal, output gradient, signal gradient); its
+algorithmic bytes are the signal and the output gradient read plus the
+signal gradient written.
+
 Prints ONE JSON line (rank 0, N = 1):
   value        mel frames per second over the K timed steps (events around
                the whole timed region, torch's current stream);
@@ -44,6 +50,8 @@ def parse():
     ap.add_argument("--sets", type=int, default=0, help="rotating buffer sets (0: enough for 512 MB)")
     ap.add_argument("--out-dtype", default="f32", choices=["f32", "f16"],
                     help="output element type (f16: the f32 result rounded at the store)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time fm_backward (gradient w.r.t. the signal) instead of the forward")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-copy-probe", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle sample")
@@ -52,9 +60,10 @@ def parse():
     return ap.parse_args()
 
 
-def cpu_baseline(cfg: dict, budget_s: float) -> dict:
+def cpu_baseline(cfg: dict, budget_s: float, backward: bool = False) -> dict:
     """The oracle as it stands, on whole signals of the workload, repeated
-    until about `budget_s` seconds of CPU work; frames/s."""
+    until about `budget_s` seconds of CPU work; frames/s (with `backward`,
+    the oracle's vector-Jacobian product)."""
     from oracle import mel_oracle as O
     try:
         from threadpoolctl import threadpool_info
@@ -64,19 +73,28 @@ def cpu_baseline(cfg: dict, budget_s: float) -> dict:
         threads = os.cpu_count() or 1
     targs = W.transform_args(cfg)
     x = W.make_signal(W.workload(cfg["name"], batch=1))
+    if backward:
+        T = O.frame_count(x.shape[-1], targs["n_fft"], targs["hop_length"], targs.get("center", True),
+                          targs.get("pad", 0))
+        u = np.random.default_rng(1).standard_normal((1, targs["n_mels"], T))
     t0 = time.perf_counter()
     frames = 0
     runs = 0
     while True:
-        y = O.mel_spectrogram(x, **targs)
-        frames += y.shape[0] * y.shape[-1]
+        if backward:
+            O.mel_spectrogram_vjp(x, u, **targs)
+            frames += T
+        else:
+            y = O.mel_spectrogram(x, **targs)
+            frames += y.shape[0] * y.shape[-1]
         runs += 1
         if time.perf_counter() - t0 >= budget_s:
             break
     dt = time.perf_counter() - t0
     return {"value": frames / dt, "unit": "frames/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{runs} x one {cfg['length']}-sample signal of the {cfg['name']} workload "
-                      f"({frames} frames, {dt:.1f} s, numpy f64 with BLAS threads)"}
+                      f"({'backward, ' if backward else ''}"
+                      f"{frames} frames, {dt:.1f} s, numpy f64 with BLAS threads)"}
 
 
 def copy_probe(torch, dev, nbytes: int, reps: int = 50) -> dict:
@@ -150,17 +168,35 @@ def main():
     T = mel.out_frames(L)
     in_bytes = x_np.nbytes
     out_bytes = B * cfg["n_mels"] * T * (2 if args.out_dtype == "f16" else 4)
-    algo_bytes = in_bytes + out_bytes
+    if args.backward:
+        if x_np.dtype != np.float32 or args.out_dtype != "f32":
+            print("--backward needs a float32 workload and f32 gradients", file=sys.stderr)
+            sys.exit(2)
+        algo_bytes = in_bytes + out_bytes + in_bytes   # x, grad_out read; grad_x written
+    else:
+        algo_bytes = in_bytes + out_bytes
     frames = B * T
 
     sets = args.sets or max(2, int(np.ceil(2 * 256e6 / algo_bytes)) + 1)
     x0 = torch.from_numpy(x_np).to(dev)
     xs = [x0] + [x0.clone() for _ in range(sets - 1)]
     ys = [torch.empty((B, cfg["n_mels"], T), dtype=out_dt, device=dev) for _ in range(sets)]
+    if args.backward:
+        g0 = torch.from_numpy(np.random.default_rng(11).standard_normal((B, cfg["n_mels"], T))
+                              .astype(np.float32)).to(dev)
+        for y in ys:
+            y.copy_(g0)            # the output gradients
+        dxs = [torch.empty((B, L), dtype=torch.float32, device=dev) for _ in range(sets)]
+
+        def step(i):
+            mel.backward(xs[i % sets], ys[i % sets], out=dxs[i % sets])
+    else:
+        def step(i):
+            mel(xs[i % sets], out=ys[i % sets])
     stream = torch.cuda.current_stream(dev)
 
     for i in range(args.warmup):
-        mel(xs[i % sets], out=ys[i % sets])
+        step(i)
     torch.cuda.synchronize()
 
     # The launches are queued behind a GPU sleep, so the device runs them
@@ -184,7 +220,7 @@ def main():
     def timed_steps():
         ev0.record(stream)
         for i in range(args.steps):
-            mel(xs[i % sets], out=ys[i % sets])
+            step(i)
         ev1.record(stream)
 
     torch.cuda.synchronize()
@@ -201,7 +237,7 @@ def main():
     def timed_each():
         for i in range(n_k):
             starts[i].record(stream)
-            mel(xs[i % sets], out=ys[i % sets])
+            step(i)
             ends[i].record(stream)
 
     torch.cuda.synchronize()
@@ -218,7 +254,7 @@ def main():
     torch.cuda.synchronize()
     t = time.perf_counter()
     for i in range(args.steps):
-        mel(xs[i % sets], out=ys[i % sets])
+        step(i)
     torch.cuda.synchronize()
     host_loop_ms = (time.perf_counter() - t) * 1e3 / args.steps
 
@@ -230,13 +266,14 @@ def main():
         try:
             for t in json.load(open(args.traffic_json)).get("entries", []):
                 if (t.get("workload") == cfg["name"] and t.get("out_dtype", "f32") == args.out_dtype
+                        and bool(t.get("backward", False)) == args.backward
                         and t.get("kernel_sources_sha256_16") == kernel_sources_hash()):
                     traffic = t.get("bytes_per_launch")
         except Exception:
             traffic = None
 
     res = {
-        "metric": METRIC,
+        "metric": ("backward (gradient w.r.t. the signal): " + METRIC) if args.backward else METRIC,
         "value": frames / (ms_per_step * 1e-3),
         "unit": "frames/s",
         "n_gpus": 1,
@@ -250,7 +287,7 @@ def main():
         "data": "synthetic (seeded; see workloads.py)",
         "config": {"workload": f"{cfg['name']}: {B}x{L} {cfg['dtype']}, n_fft={cfg['n_fft']} "
                                f"hop={cfg['hop_length']} {cfg['n_mels']} mels, power={cfg['power']}, "
-                               f"{args.out_dtype} out",
+                               f"{args.out_dtype} out" + (", backward" if args.backward else ""),
                    "batch": B, "length": L, "n_frames": T, "buffer_sets": sets,
                    "in_dtype": cfg["dtype"], "out_dtype": args.out_dtype,
                    "parallelism": "single GPU"},
@@ -268,7 +305,7 @@ def main():
         res["copy_probe"] = copy_probe(torch, dev, in_bytes)
         res["copy_probe_large"] = copy_probe(torch, dev, 512 << 20, reps=20)
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds, args.backward)
     print(json.dumps(res), flush=True)
 
 

@@ -59,10 +59,12 @@ struct BArgs {
   int tiles_per_signal;
   int n_edge;            // edge workgroups (first in the grid), one per signal
   int edge;              // samples at each end owned by the edge workgroups
+  int edge_split;        // 1: two edge workgroups per signal (head, tail)
   int whole;             // 1: the edge workgroup owns the whole signal
   int chunk;             // frames per pass
   int vec_ok;            // interior frames may use paired loads
   int g_off;             // LDS float offset of the bin-gradient tile dP[f][k]
+  int gt_off;            // LDS float offset of the output-gradient tile g[m][f]
   int acc_off;           // LDS float offset of the edge accumulators
   float power;
   float half_power;
@@ -113,6 +115,7 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves(N1, N2)) void mel_backwa
   float2* Y = reinterpret_cast<float2*>(lds);
   float* D = reinterpret_cast<float*>(lds);  // D[f][n], aliases Y
   float* dPt = reinterpret_cast<float*>(lds) + a.g_off;  // dP[f][k]
+  float* Gt = reinterpret_cast<float*>(lds) + a.gt_off;  // g[m][f] of the pass
   float* acc = reinterpret_cast<float*>(lds) + a.acc_off;
   float* red = acc + 2 * a.edge;
 
@@ -124,23 +127,36 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves(N1, N2)) void mel_backwa
 
   // ---- this workgroup's signal, frame segments and owned samples ----------
   const bool edge_wg = static_cast<int>(blockIdx.x) < a.n_edge;
-  int b, seg0_lo, seg0_hi, seg1_lo = 0, seg1_hi = 0, own_lo = 0, own_hi = 0, n_acc = 0;
+  int b, seg0_lo, seg0_hi, seg1_lo = 0, seg1_hi = 0, own_lo = 0, own_hi = 0;
+  int n_acc = 0, s_lo = 0, s_hi = 0;  // edge: accumulator slots, owned ones
   if (edge_wg) {
-    b = blockIdx.x;
+    // side 0: the head zone [0, edge), side 1: the tail zone [L - edge, L),
+    // each in a workgroup of its own (edge_split), else both in one
+    const int side = a.edge_split ? static_cast<int>(blockIdx.x & 1) : -1;
+    b = a.edge_split ? static_cast<int>(blockIdx.x >> 1) : static_cast<int>(blockIdx.x);
     n_acc = a.whole ? L : 2 * a.edge;
-    // frames reaching the head zone [0, edge) and the tail zone [L - edge, L)
+    s_lo = side == 1 ? a.edge : 0;
+    s_hi = side == 0 ? a.edge : n_acc;
+    // frames reaching the head zone and the tail zone
     const int th = min(T, (a.edge + a.pad + hop - 1) / hop);
     const int num = L - a.edge + a.pad - NF;
     const int tt = num < 0 ? 0 : num / hop + 1;
-    seg0_lo = 0;
-    if (a.whole || th >= tt) {
+    if (side == 0) {
+      seg0_lo = 0;
+      seg0_hi = th;
+    } else if (side == 1) {
+      seg0_lo = tt;
+      seg0_hi = T;
+    } else if (a.whole || th >= tt) {
+      seg0_lo = 0;
       seg0_hi = T;
     } else {
+      seg0_lo = 0;
       seg0_hi = th;
       seg1_lo = tt;
       seg1_hi = T;
     }
-    for (int s = tid; s < n_acc; s += NT) acc[s] = 0.0f;
+    for (int s = s_lo + tid; s < s_hi; s += NT) acc[s] = 0.0f;
   } else {
     const int w = blockIdx.x - a.n_edge;
     // (the division expands to vector code: bring the uniform result back to
@@ -160,12 +176,20 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves(N1, N2)) void mel_backwa
   float* gx = a.gin + static_cast<long long>(b) * L;
 
   // Sum of the frame gradients of frames [ca, ca + nf) at padded position q
-  // (q = thi*hop + qr, 0 <= qr < hop), latest frame first.
+  // (q = thi*hop + qr, 0 <= qr < hop), latest frame first: at most
+  // ceil(n_fft / hop) frames, as a fixed predicated loop so that the reads
+  // are in flight together.
+  const int nover = (NF + hop - 1) / hop;
   auto gather_at = [&](int ca, int nf, int thi, int qr) -> float {
-    int t = min(thi, ca + nf - 1);
-    int n = qr + (thi - t) * hop;
+    const int t = min(thi, ca + nf - 1);
+    const int n = qr + (thi - t) * hop;
     float s = 0.0f;
-    for (; t >= ca && n < NF; --t, n += hop) s += D[(t - ca) * DS + n];
+#pragma unroll 4
+    for (int j = 0; j < nover; ++j) {
+      const bool ok = t - j >= ca && n + j * hop < NF;
+      const float v = D[(ok ? t - j - ca : 0) * DS + (ok ? n + j * hop : 0)];
+      s += ok ? v : 0.0f;
+    }
     return s;
   };
   auto gather = [&](int ca, int nf, int i) -> float {  // i: sample position
@@ -200,22 +224,6 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves(N1, N2)) void mel_backwa
       return v;
     };
     const int lane = opaque_tid() & 63;
-
-    // ---- bin gradients dP[f][k] = sum_m W[m,k] g[m][ca+f]: wave-uniform
-    //      taps (scalar loads), lane = frame (coalesced reads of g) ---------
-    if (lane < nf) {
-      CInt* tp = (CInt*)(a.taps);  // address-space cast: scalar loads
-      const float* gc = g + ca;    // uniform base, 32-bit lane offsets
-      float* drow = dPt + lane * K;
-      for (int k = wave; k < K; k += NW) {
-        const int m0 = tp[4 * k], m1 = tp[4 * k + 1];
-        const float w0 = __int_as_float(tp[4 * k + 2]), w1 = __int_as_float(tp[4 * k + 3]);
-        float v = 0.0f;
-        if (m0 < a.n_mels) v = w0 * (gc + static_cast<long long>(m0) * T)[lane];
-        if (m1 < a.n_mels) v = fmaf(w1, (gc + static_cast<long long>(m1) * T)[lane], v);
-        drow[k] = v;
-      }
-    }
 
     // ---- pass 1 (forward transform): window, N1-point DFTs, twiddle -> Y --
     {
@@ -262,6 +270,15 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves(N1, N2)) void mel_backwa
         for (int k1 = 1; k1 < N1; ++k1)
           yrow[k1 * N2] = cmul(v[k1], kHoist ? twv[kHoist ? k1 : 0] : a.tw_m[n2v * k1]);
       };
+      // The output-gradient tile g[m][ca .. ca+nf) goes to LDS by direct
+      // global -> LDS loads (one row per wave instruction, no registers),
+      // issued before the samples so that both arrive in one round trip;
+      // the bin gradients are formed from it after pass 1.
+      if (lane < nf) {
+        for (int m = wave; m < a.n_mels; m += NW)
+          __builtin_amdgcn_global_load_lds(g + static_cast<long long>(m) * T + ca + lane, Gt + m * nf, 4, 0, 0);
+        if (wave == NW - 1) Gt[a.n_mels * nf + lane] = 0.0f;  // row n_mels: unused taps
+      }
       if constexpr (kHoist) {
         constexpr int RMAX = (CAP + SLOTS - 1) / SLOTS;
         // (every round loads, rounds past the pass repeat its last frame: a
@@ -281,6 +298,19 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves(N1, N2)) void mel_backwa
           compute(f, s0);
         }
       }
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's gradient-tile rows have landed
+    __syncthreads();
+
+    // ---- bin gradients dP[f][k] = sum_m W[m,k] g[m][ca+f]: thread = bin
+    //      (its two taps one vector load), frames in an unrolled loop of
+    //      independent LDS reads -----------------------------------------
+    for (int k = opaque_tid(); k < K; k += NT) {
+      const BinTap tap = a.taps[k];
+      const float* g0 = Gt + tap.m0 * nf;
+      const float* g1 = Gt + tap.m1 * nf;
+#pragma unroll 4
+      for (int f = 0; f < nf; ++f) dPt[f * K + k] = fmaf(tap.w1, g1[f], tap.w0 * g0[f]);
     }
     __syncthreads();
 
@@ -449,7 +479,7 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves(N1, N2)) void mel_backwa
       // each owned sample: its own position plus the padded positions that
       // the padding map sends to it (one reflection or wrap at most)
       const int ly = L + 2 * a.zpad;
-      for (int s = t4; s < n_acc; s += NT) {
+      for (int s = s_lo + t4; s < s_hi; s += NT) {
         const int j = (a.whole || s < a.edge) ? s : L - 2 * a.edge + s;
         float v = gather(ca, nf, j);
         if (a.pad_mode == FM_PAD_REFLECT) {
@@ -498,7 +528,7 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves(N1, N2)) void mel_backwa
   }
 
   if (edge_wg) {
-    for (int s = tid; s < n_acc; s += NT) {
+    for (int s = s_lo + tid; s < s_hi; s += NT) {
       const int j = (a.whole || s < a.edge) ? s : L - 2 * a.edge + s;
       gx[j] = acc[s];
     }

@@ -79,7 +79,7 @@ constexpr int power_stride(int half) { return half + 1 + kPowerPad; }
 
 // Backward pass: the filters that touch one one-sided bin.  A triangular
 // filterbank puts every bin in at most two filters; an unused tap has
-// m = n_mels and weight 0.
+// m = n_mels (a zero row of the kernel's gradient tile) and weight 0.
 struct BinTap {
   int32_t m0, m1;
   float w0, w1;
@@ -186,10 +186,12 @@ int tile_lds_bytes(const Plan& p, int frames);
 // inverse transform holds the windowed frame gradients; at bwd_grad_offset
 // the bin gradients dP[f][k] (frame stride n_fft/2 + 1, odd); at
 // bwd_acc_offset the edge accumulators (2 * bwd_edge floats) and 2 floats
-// per wave for block sums.
+// per wave for block sums; at bwd_gtile_offset the output-gradient tile
+// g[m][f] of the pass, n_mels + 1 rows (the last one zero).
 int bwd_edge(const Plan& p);  // samples at each signal end owned by edge workgroups
 int bwd_grad_offset(const Plan& p, int chunk);
 int bwd_acc_offset(const Plan& p, int chunk);
+int bwd_gtile_offset(const Plan& p, int chunk);  // output-gradient tile [n_mels][chunk]
 int bwd_lds_bytes(const Plan& p, int chunk);
 
 // Frames per signal for a plan (negative FM_E_* on invalid length).

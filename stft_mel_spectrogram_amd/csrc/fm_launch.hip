@@ -293,7 +293,10 @@ int launch_backward(const Plan& p, const float* in, int64_t batch, int64_t lengt
                                            std::to_string(halo + 1) + ")");
   const int edge = bwd_edge(p);
   const int whole = 2 * static_cast<int64_t>(edge) >= length ? 1 : 0;
-  const int64_t n_edge = edge > 0 ? batch : 0;
+  // head and tail zones in workgroups of their own, unless circular padding
+  // sends tail frames' gradients to the head (or one zone covers the signal)
+  const int edge_split = (edge > 0 && !whole && p.pad_mode != FM_PAD_CIRCULAR) ? 1 : 0;
+  const int64_t n_edge = edge > 0 ? batch * (edge_split ? 2 : 1) : 0;
   const int chunk = choose_bwd_chunk(p, batch, T, halo, n_edge);
   const int tile = chunk - halo;
   const int64_t tiles = (T + tile - 1) / tile;
@@ -320,11 +323,13 @@ int launch_backward(const Plan& p, const float* in, int64_t batch, int64_t lengt
   a.tiles_per_signal = static_cast<int>(tiles);
   a.n_edge = static_cast<int>(n_edge);
   a.edge = edge;
+  a.edge_split = edge_split;
   a.whole = whole;
   a.chunk = chunk;
   const uintptr_t ia = reinterpret_cast<uintptr_t>(in);
   a.vec_ok = (ia % 8 == 0) && (length % 2 == 0) && (p.hop % 2 == 0) && ((p.pad_left + p.zpad) % 2 == 0);
   a.g_off = bwd_grad_offset(p, chunk);
+  a.gt_off = bwd_gtile_offset(p, chunk);
   a.acc_off = bwd_acc_offset(p, chunk);
   a.power = static_cast<float>(p.power);
   a.half_power = static_cast<float>(p.power * 0.5);

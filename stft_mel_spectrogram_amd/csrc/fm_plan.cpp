@@ -126,8 +126,12 @@ int bwd_acc_offset(const Plan& p, int chunk) {
   return bwd_grad_offset(p, chunk) + std::max(chunk, 1) * p.n_freqs;
 }
 
+int bwd_gtile_offset(const Plan& p, int chunk) {
+  return bwd_acc_offset(p, chunk) + 2 * bwd_edge(p) + 2 * (kBwdThreads / 64);
+}
+
 int bwd_lds_bytes(const Plan& p, int chunk) {
-  return (bwd_acc_offset(p, chunk) + 2 * bwd_edge(p) + 2 * (kBwdThreads / 64)) * 4;
+  return (bwd_gtile_offset(p, chunk) + (p.n_mels + 1) * std::max(chunk, 1)) * 4;
 }
 
 int64_t out_frames(const Plan& p, int64_t length) {
