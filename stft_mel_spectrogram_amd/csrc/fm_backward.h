@@ -180,16 +180,24 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves(N1, N2)) void mel_backwa
   // ceil(n_fft / hop) frames, as a fixed predicated loop so that the reads
   // are in flight together.
   const int nover = (NF + hop - 1) / hop;
+  const int dstep = hop - DS;  // index step to the previous frame's sample
   auto gather_at = [&](int ca, int nf, int thi, int qr) -> float {
     const int t = min(thi, ca + nf - 1);
     const int n = qr + (thi - t) * hop;
-    float s = 0.0f;
-#pragma unroll 4
-    for (int j = 0; j < nover; ++j) {
-      const bool ok = t - j >= ca && n + j * hop < NF;
-      const float v = D[(ok ? t - j - ca : 0) * DS + (ok ? n + j * hop : 0)];
-      s += ok ? v : 0.0f;
+    const int idx = (t - ca) * DS + n;
+    // four frames' reads issued together, then summed in order
+    float v[4];
+    bool ok[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      ok[j] = t - j >= ca && n + j * hop < NF;
+      v[j] = D[ok[j] ? idx + j * dstep : 0];
     }
+    float s = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s += ok[j] ? v[j] : 0.0f;
+    for (int j = 4; j < nover; ++j)  // (hop < n_fft / 4)
+      if (t - j >= ca && n + j * hop < NF) s += D[idx + j * dstep];
     return s;
   };
   auto gather = [&](int ca, int nf, int i) -> float {  // i: sample position
