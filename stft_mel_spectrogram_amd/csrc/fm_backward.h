@@ -107,6 +107,7 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves(N1, N2)) void mel_backwa
   constexpr int SLOTS = NT / N2;
   constexpr bool kHoist = N1 <= 8;
   constexpr int CAP = bwd_chunk_cap(N1, N2, NT);
+  constexpr bool kRowPass2 = N1 <= 8;  // pass 2: a thread per row (else per row pair)
   constexpr int CA = N2 / 2 + 1;
   constexpr int D2 = N1 / 2 - N1 * CA;
   constexpr int JX = N2 - CA;
@@ -207,6 +208,82 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves(N1, N2)) void mel_backwa
     return gather_at(ca, nf, thi, q - thi * hop);
   };
 
+  // Every phase derives its lane indices from its own copy of the thread
+  // index, which the compiler cannot prove invariant: addresses and table
+  // loads stay inside their phase instead of being hoisted out of it (and out
+  // of the pass loop) and held in registers, or spilled, meanwhile.
+  auto opaque_tid = [&]() {
+    int v = tid;
+    asm volatile("" : "+v"(v));
+    return v;
+  };
+
+  // Pass 2 with one thread per (frame, row k1) (shapes with N1 <= 8): the
+  // row's N2-point DFT, then for each of its bins k = k1 + N1*k2 the split
+  // with the mirrored bin M - k read from the partner row (row N1 - k1, or
+  // the row itself for k1 = 0 and N1/2) through LDS, the gradient of |X|^p on
+  // both bins and the inverse-split value C[k] of its own bin, and the row's
+  // inverse DFT.  Partners are lanes of the same wave, and a wave's LDS
+  // operations complete in order, so no barrier is needed inside.
+  auto pass2_rows = [&](int nf) {
+    const int t2 = opaque_tid();
+    const int f2 = t2 / N1;
+    const int r = t2 - f2 * N1;
+    if (f2 >= nf) return;
+    const int rp = (N1 - r) & (N1 - 1);  // partner row
+    float2* row = Y + f2 * SY + r * N2;
+    const float2* prow = Y + f2 * SY + rp * N2;
+    float2 z[N2];
+#pragma unroll
+    for (int j = 0; j < N2; ++j) z[j] = row[j];
+    Dft<N2>::run(z);
+#pragma unroll
+    for (int j = 0; j < N2; ++j) row[j] = z[j];
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's rows are written
+    __builtin_amdgcn_wave_barrier();
+    float2 zp[N2];
+#pragma unroll
+    for (int j = 0; j < N2; ++j) zp[j] = prow[j];
+    const bool r0 = (r == 0);
+    // split twiddle exp(-2 pi i k/N), k = r + N1*k2: the table value of r times
+    // the compile-time rotation exp(-2 pi i k2/(2 N2))
+    const float2 w_r = a.tw_n[r];
+    const float* dprow = dPt + f2 * K;
+    const float* dk = dprow + r;        // dP[k]     = dk[N1*k2]
+    const float* dm = dprow + (M - r);  // dP[M - k] = dm[-N1*k2]
+    static_for<0, N2>([&](auto k2c) {
+      constexpr int k2 = decltype(k2c)::value;
+      const float2 zk = z[k2];
+      // mirror of bin k: row 0 -> index (N2 - k2) % N2 of row 0 (k2 = 0: bin M,
+      // i.e. Z[0]); other rows -> index N2 - 1 - k2 of the partner row
+      const float2 zm = r0 ? zp[(N2 - k2) % N2] : zp[N2 - 1 - k2];
+      const float2 w = twiddle<k2, 2 * N2>(w_r);
+      const bool dc = r0 && k2 == 0;
+      const float2 e = make_float2(zk.x + zm.x, zk.y - zm.y);   // Z[k] + conj Z[M-k]
+      const float2 o = make_float2(zk.x - zm.x, zk.y + zm.y);   // Z[k] - conj Z[M-k]
+      const float2 v = cmul(w, o);
+      const float2 xk = make_float2(e.x + v.y, e.y - v.x);      // X[k]   = e - i v
+      const float2 xm = make_float2(e.x - v.y, -(e.y + v.x));   // X[M-k] = conj(e + i v)
+      const float sk = grad_scale<PMODE>(xk, dk[N1 * k2], a.power, a.half_power);
+      const float sm = grad_scale<PMODE>(xm, dm[-N1 * k2], a.power, a.half_power);
+      const float hs = dc ? 1.0f : 0.5f;
+      const float2 hk = make_float2(hs * sk * xk.x, dc ? 0.0f : hs * sk * xk.y);
+      const float2 hm = make_float2(hs * sm * xm.x, dc ? 0.0f : hs * sm * xm.y);
+      const float2 E = make_float2(hk.x + hm.x, hk.y - hm.y);   // H[k] + conj H[M-k]
+      const float2 O = make_float2(hk.x - hm.x, hk.y + hm.y);   // H[k] - conj H[M-k]
+      const float2 V = cmul(make_float2(w.x, -w.y), O);         // exp(+2 pi i k/N) O
+      z[k2] = make_float2(E.x - V.y, E.y + V.x);                // C[k] = E + i V
+      if constexpr (k2 % kBwdPairGroup == kBwdPairGroup - 1) __builtin_amdgcn_sched_barrier(0);
+    });
+    // inverse N2-point DFT over k2 (conjugate, forward DFT, conjugate); the
+    // partner's reads of this row were issued before these writes
+#pragma unroll
+    for (int j = 0; j < N2; ++j) z[j].y = -z[j].y;
+    Dft<N2>::run(z);
+#pragma unroll
+    for (int j = 0; j < N2; ++j) row[j] = make_float2(z[j].x, -z[j].y);
+  };
+
   int cur = seg0_lo, seg_hi = seg0_hi;
   bool second = false;
   for (;;) {
@@ -222,15 +299,6 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves(N1, N2)) void mel_backwa
     const int ca = cur;
     const int nf = min(a.chunk, seg_hi - cur);
     cur += nf;
-    // Every phase derives its lane indices from its own copy of the thread
-    // index, which the compiler cannot prove invariant: addresses and table
-    // loads stay inside their phase instead of being hoisted out of it (and
-    // out of the pass loop) and held in registers, or spilled, meanwhile.
-    auto opaque_tid = [&]() {
-      int v = tid;
-      asm volatile("" : "+v"(v));
-      return v;
-    };
     const int lane = opaque_tid() & 63;
 
     // ---- pass 1 (forward transform): window, N1-point DFTs, twiddle -> Y --
@@ -323,6 +391,10 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves(N1, N2)) void mel_backwa
     __syncthreads();
 
     // ---- pass 2, split, gradient of |X|^p, inverse split, inverse pass 2 --
+    if constexpr (kRowPass2) {
+      pass2_rows(nf);
+      __syncthreads();
+    } else {
     const int t2 = opaque_tid();
     const int f2 = t2 / NPAIR;  // frame f2, pair pv of rows
     const int pv = t2 - f2 * NPAIR;
@@ -434,6 +506,7 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves(N1, N2)) void mel_backwa
       }
     }
     __syncthreads();
+    }
 
     // ---- inverse pass 1: twiddle, N1-point inverse DFTs, window -> D -------
     const int t3 = opaque_tid();

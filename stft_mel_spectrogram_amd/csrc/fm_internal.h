@@ -94,11 +94,12 @@ constexpr int kBwdThreads = 256;
 constexpr int bwd_min_waves(int n1, int n2) { return n1 * n2 <= 512 ? 2 : 1; }
 
 // Most frames one backward pass of a workgroup can hold: its second FFT
-// pass gives each thread one frame's pair of rows (threads / (n1/2) frames),
-// and shapes with n1 <= 8 keep every frame's samples of a pass in registers
-// (at most 4 rounds of threads / n2 frames).
+// pass gives each thread one frame's row (n1 <= 8: threads / n1 frames) or
+// pair of rows (threads / (n1/2) frames), and shapes with n1 <= 8 keep every
+// frame's samples of a pass in registers (at most 4 rounds of threads / n2
+// frames).
 constexpr int bwd_chunk_cap(int n1, int n2, int threads) {
-  const int pass2 = threads / (n1 / 2);
+  const int pass2 = n1 <= 8 ? threads / n1 : threads / (n1 / 2);
   const int pass1 = n1 <= 8 ? 4 * (threads / n2) : 64;
   const int c = pass2 < pass1 ? pass2 : pass1;
   return c < 64 ? c : 64;
