@@ -241,10 +241,13 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves(N1, N2)) void mel_backwa
     for (int j = 0; j < N2; ++j) row[j] = z[j];
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's rows are written
     __builtin_amdgcn_wave_barrier();
+    // zp[k2] = the mirror of bin r + N1*k2: row 0 -> its index (N2 - k2) % N2
+    // (k2 = 0: bin M, i.e. Z[0]); other rows -> index N2 - 1 - k2 of the
+    // partner row (the choice is made on the LDS address, not on registers)
+    const bool r0 = (r == 0);
     float2 zp[N2];
 #pragma unroll
-    for (int j = 0; j < N2; ++j) zp[j] = prow[j];
-    const bool r0 = (r == 0);
+    for (int j = 0; j < N2; ++j) zp[j] = prow[r0 ? (N2 - j) % N2 : N2 - 1 - j];
     // split twiddle exp(-2 pi i k/N), k = r + N1*k2: the table value of r times
     // the compile-time rotation exp(-2 pi i k2/(2 N2))
     const float2 w_r = a.tw_n[r];
@@ -254,9 +257,7 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves(N1, N2)) void mel_backwa
     static_for<0, N2>([&](auto k2c) {
       constexpr int k2 = decltype(k2c)::value;
       const float2 zk = z[k2];
-      // mirror of bin k: row 0 -> index (N2 - k2) % N2 of row 0 (k2 = 0: bin M,
-      // i.e. Z[0]); other rows -> index N2 - 1 - k2 of the partner row
-      const float2 zm = r0 ? zp[(N2 - k2) % N2] : zp[N2 - 1 - k2];
+      const float2 zm = zp[k2];
       const float2 w = twiddle<k2, 2 * N2>(w_r);
       const bool dc = r0 && k2 == 0;
       const float2 e = make_float2(zk.x + zm.x, zk.y - zm.y);   // Z[k] + conj Z[M-k]
