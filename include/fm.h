@@ -180,10 +180,10 @@ int fm_forward(const fm_plan* plan, const void* in, int in_dtype,
  *             written (not accumulated).  Must not overlap the inputs.
  *   batch, length  as for fm_forward.
  *
- * FM_E_UNSUPPORTED when the frames overlapping one sample exceed what one
- * workgroup pass holds: hop >= n_fft / (c - 1) is needed, c = 64 frames for
- * n_fft <= 256, 40 for 400, 32 for 512, 16 for 1024 and 2048, 8 for 4096
- * (fewer when a large n_mels takes LDS).  One kernel launch; no
+ * Any hop: when more frames overlap one sample than one workgroup pass
+ * holds, the workgroups take several passes.  FM_E_UNSUPPORTED only when the
+ * samples one workgroup owns (2 n_fft + 2 pad floats or so) do not fit its
+ * LDS next to one frame's pass (a very large `pad`).  One kernel launch; no
  * allocation, no synchronisation.
  */
 int fm_backward(const fm_plan* plan, const float* in, int64_t batch, int64_t length,

@@ -25,7 +25,9 @@
 // deterministic and needs no atomics or zero-fill.
 //   * main workgroups each own a run of samples (their tile of frames' hops)
 //     and recompute the frames that reach into it: the tile plus the
-//     floor((n_fft-1)/hop) frames before it;
+//     floor((n_fft-1)/hop) frames before it, in one pass, or, when more
+//     frames overlap than a pass holds (small hops), in several passes that
+//     accumulate the owned samples in LDS;
 //   * one edge workgroup per signal owns the first and last n_fft/2 + 1
 //     samples, where the centre padding folds gradients of padded positions
 //     back onto signal samples (reflect: the mirrored sample; circular: the
@@ -66,6 +68,9 @@ struct BArgs {
   int g_off;             // LDS float offset of the bin-gradient tile dP[f][k]
   int gt_off;            // LDS float offset of the output-gradient tile g[m][f]
   int acc_off;           // LDS float offset of the edge accumulators
+  int multi;             // 1: a main workgroup's frames take several passes; its
+                         // samples accumulate in LDS at oacc_off
+  int oacc_off;
   float power;
   float half_power;
 };
@@ -197,8 +202,9 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves(N1, N2)) void mel_backwa
     float s = 0.0f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) s += ok[j] ? v[j] : 0.0f;
-    for (int j = 4; j < nover; ++j)  // (hop < n_fft / 4)
-      if (t - j >= ca && n + j * hop < NF) s += D[idx + j * dstep];
+    const int jmax = min(nover, t - ca + 1);  // (hop < n_fft / 4)
+    for (int j = 4; j < jmax; ++j)
+      if (n + j * hop < NF) s += D[idx + j * dstep];
     return s;
   };
   auto gather = [&](int ca, int nf, int i) -> float {  // i: sample position
@@ -547,8 +553,14 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves(N1, N2)) void mel_backwa
         const int q = i + a.pad;
         int thi = q / hop, qr = q - thi * hop;
         const int dq = NT / hop, rq = NT - dq * hop;
+        // several passes: each thread adds this pass's frames to its own
+        // samples' accumulators (the same thread every pass, no barrier)
+        float* oacc = reinterpret_cast<float*>(lds) + a.oacc_off - own_lo;
+        const bool first = ca == seg0_lo;
         for (; i < own_hi; i += NT) {
-          __builtin_nontemporal_store(gather_at(ca, nf, thi, qr), gx + i);
+          const float v = gather_at(ca, nf, thi, qr);
+          if (!a.multi) __builtin_nontemporal_store(v, gx + i);
+          else oacc[i] = first ? v : oacc[i] + v;
           thi += dq;
           qr += rq;
           if (qr >= hop) {
@@ -609,6 +621,10 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves(N1, N2)) void mel_backwa
     __syncthreads();  // LDS is reused by the next pass
   }
 
+  if (!edge_wg && a.multi) {
+    const float* oacc = reinterpret_cast<const float*>(lds) + a.oacc_off - own_lo;
+    for (int i = own_lo + tid; i < own_hi; i += NT) __builtin_nontemporal_store(oacc[i], gx + i);
+  }
   if (edge_wg) {
     for (int s = s_lo + tid; s < s_hi; s += NT) {
       const int j = (a.whole || s < a.edge) ? s : L - 2 * a.edge + s;

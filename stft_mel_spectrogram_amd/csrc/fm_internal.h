@@ -89,6 +89,7 @@ struct BinTap {
 // tiles fill a CU's LDS on their own; at 256 threads a wave may use 512
 // registers, which the two 32-point rows of its second pass need.)
 constexpr int kBwdThreads = 256;
+constexpr int kBwdLdsMax = 160 * 1024;  // LDS of a CU
 // Waves per SIMD the backward kernel is built for: 2 (<= 256 registers each)
 // up to n_fft = 1024, else 1.
 constexpr int bwd_min_waves(int n1, int n2) { return n1 * n2 <= 512 ? 2 : 1; }

@@ -126,7 +126,7 @@ int upload_plan(Plan& p) {
   if (p.bwd_chunk_max > 0) {
     void* kb = select_backward_kernel(p);
     if (!kb) return set_error(FM_E_UNSUPPORTED, "no backward kernel for this n_fft");
-    e = hipFuncSetAttribute(kb, hipFuncAttributeMaxDynamicSharedMemorySize, bwd_lds_bytes(p, p.bwd_chunk_max));
+    e = hipFuncSetAttribute(kb, hipFuncAttributeMaxDynamicSharedMemorySize, kBwdLdsMax);
     if (e != hipSuccess) return hip_fail(e, "hipFuncSetAttribute (backward)");
     for (int c = 1; c <= p.bwd_chunk_max; ++c) {
       int n = 0;
@@ -287,18 +287,29 @@ int launch_backward(const Plan& p, const float* in, int64_t batch, int64_t lengt
   if (cur != p.device) return set_error(FM_E_INVAL, "plan belongs to another device than the current one");
   if (length > (1 << 29)) return set_error(FM_E_INVAL, "problem too large for one launch (length <= 2^29)");
   const int halo = (p.n_fft - 1) / p.hop;
-  if (p.bwd_chunk_max < halo + 1)
-    return set_error(FM_E_UNSUPPORTED, "backward: hop too small for this n_fft (a workgroup pass holds " +
-                                           std::to_string(p.bwd_chunk_max) + " frames, the overlap needs " +
-                                           std::to_string(halo + 1) + ")");
   const int edge = bwd_edge(p);
   const int whole = 2 * static_cast<int64_t>(edge) >= length ? 1 : 0;
   // head and tail zones in workgroups of their own, unless circular padding
   // sends tail frames' gradients to the head (or one zone covers the signal)
   const int edge_split = (edge > 0 && !whole && p.pad_mode != FM_PAD_CIRCULAR) ? 1 : 0;
   const int64_t n_edge = edge > 0 ? batch * (edge_split ? 2 : 1) : 0;
-  const int chunk = choose_bwd_chunk(p, batch, T, halo, n_edge);
-  const int tile = chunk - halo;
+  // One pass per main workgroup when the overlap fits a pass; else tiles of
+  // halo + 1 frames whose frames (2 halo + 1) take several passes, the owned
+  // samples (at most tile*hop + n_fft + padding) accumulating in LDS.
+  int chunk, tile, multi = 0, oacc = 0;
+  if (p.bwd_chunk_max >= halo + 1) {
+    chunk = choose_bwd_chunk(p, batch, T, halo, n_edge);
+    tile = chunk - halo;
+  } else {
+    multi = 1;
+    tile = halo + 1;
+    oacc = tile * p.hop + p.n_fft + p.pad_left + p.zpad;
+    chunk = p.bwd_chunk_max;
+    while (chunk > 1 && bwd_lds_bytes(p, chunk) + 4L * oacc > kBwdLdsMax) --chunk;
+    if (p.bwd_chunk_max < 1 || bwd_lds_bytes(p, chunk) + 4L * oacc > kBwdLdsMax)
+      return set_error(FM_E_UNSUPPORTED, "backward: the samples one workgroup owns do not fit its LDS "
+                                         "(hop " + std::to_string(p.hop) + ", n_fft " + std::to_string(p.n_fft) + ")");
+  }
   const int64_t tiles = (T + tile - 1) / tile;
   const int64_t n_main = whole ? 0 : batch * tiles;
   if (n_main + n_edge > INT32_MAX) return set_error(FM_E_INVAL, "problem too large for one launch");
@@ -328,6 +339,8 @@ int launch_backward(const Plan& p, const float* in, int64_t batch, int64_t lengt
   a.chunk = chunk;
   const uintptr_t ia = reinterpret_cast<uintptr_t>(in);
   a.vec_ok = (ia % 8 == 0) && (length % 2 == 0) && (p.hop % 2 == 0) && ((p.pad_left + p.zpad) % 2 == 0);
+  a.multi = multi;
+  a.oacc_off = bwd_lds_bytes(p, chunk) / 4;
   a.g_off = bwd_grad_offset(p, chunk);
   a.gt_off = bwd_gtile_offset(p, chunk);
   a.acc_off = bwd_acc_offset(p, chunk);
@@ -338,7 +351,7 @@ int launch_backward(const Plan& p, const float* in, int64_t batch, int64_t lengt
   if (!k) return set_error(FM_E_UNSUPPORTED, "no backward kernel for this n_fft");
   void* args[] = {&a};
   e = hipLaunchKernel(k, dim3(static_cast<unsigned>(n_main + n_edge)), dim3(kBwdThreads), args,
-                      static_cast<size_t>(bwd_lds_bytes(p, chunk)), static_cast<hipStream_t>(stream));
+                      static_cast<size_t>(bwd_lds_bytes(p, chunk) + 4 * oacc), static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "backward kernel launch");
   return FM_OK;
 }

@@ -88,6 +88,12 @@ CASES = [
     ("nfft2048_p1", 2, 22050, dict(sample_rate=22050, n_fft=2048, hop_length=512, n_mels=128,
                                    power=1.0)),
     ("nfft4096", 1, 44100, dict(sample_rate=44100, n_fft=4096, hop_length=1024, n_mels=128)),
+    # small hops: more frames overlap a sample than one pass holds (several passes)
+    ("hop8_nfft400", 2, 3000, dict(n_fft=400, hop_length=8, n_mels=40)),
+    ("hop32_nfft1024_p1", 1, 8000, dict(n_fft=1024, hop_length=32, n_mels=64, power=1.0)),
+    ("hop100_nfft2048_circ", 2, 9000, dict(sample_rate=22050, n_fft=2048, hop_length=100,
+                                           n_mels=80, pad_mode="circular")),
+    ("hop64_nfft4096", 1, 8192, dict(sample_rate=44100, n_fft=4096, hop_length=64, n_mels=128)),
 ]
 
 
@@ -166,8 +172,9 @@ def test_backward_errors_and_empty_batch():
         mel.backward(torch.zeros(4000, device="cuda"), torch.zeros(40, 25, device="cuda"))
     z = mel.backward(torch.empty((0, 4000), device="cuda"), torch.empty((0, 40, 26), device="cuda"))
     assert tuple(z.shape) == (0, 4000)
-    # heavy overlap: 64 frames cover each sample, more than one pass holds
-    big = MelSpectrogram(sample_rate=44100, n_fft=4096, hop_length=64, n_mels=128)
+    # a zero padding so wide that one workgroup's samples cannot fit its LDS
+    wide = MelSpectrogram(sample_rate=44100, n_fft=4096, hop_length=64, n_mels=128, pad=40000)
+    T = wide.out_frames(8192)
     with pytest.raises(FmError) as e:
-        big.backward(torch.zeros(1, 8192, device="cuda"), torch.zeros(1, 128, 129, device="cuda"))
+        wide.backward(torch.zeros(1, 8192, device="cuda"), torch.zeros(1, 128, T, device="cuda"))
     assert e.value.status == FM_E_UNSUPPORTED
