@@ -122,6 +122,22 @@ def test_backward_full_whisper_shape():
     assert_grad_parity(got, ref, "full whisper")
 
 
+@pytest.mark.parametrize("name,rows", [("large", [0, 37, 63]), ("pow2", None)])
+def test_backward_full_other_workloads(name, rows):
+    """64 x 220500 (n_fft 2048, power 1) on sampled rows of the full launch;
+    8 x 32768 (n_fft 1024) on every row."""
+    cfg = W.workload(name)
+    x = W.make_signal(cfg)
+    targs = W.transform_args(cfg)
+    T = O.frame_count(x.shape[-1], targs["n_fft"], targs["hop_length"], center=True)
+    u = np.random.default_rng(22).standard_normal((x.shape[0], targs["n_mels"], T)).astype(np.float32)
+    print(f"[case] backward full {name} {x.shape} rows {rows}", flush=True)
+    got = gpu_backward(x, u, **targs)
+    sel = slice(None) if rows is None else rows
+    ref = O.mel_spectrogram_vjp(x[sel], u[sel], chunk=2, **targs)
+    assert_grad_parity(got[sel], ref, f"full {name}")
+
+
 def test_backward_is_deterministic_and_autograd_matches():
     from stft_mel_spectrogram_amd import MelSpectrogram
     _require_gpu()
