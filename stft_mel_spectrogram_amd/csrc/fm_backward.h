@@ -132,14 +132,16 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves(N1, N2)) void mel_backwa
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   // ---- this workgroup's signal, frame segments and owned samples ----------
-  const bool edge_wg = static_cast<int>(blockIdx.x) < a.n_edge;
+  // logical workgroup id in the XCD-aware order (edge workgroups first)
+  const int wid = __builtin_amdgcn_readfirstlane(xcd_tile_order(blockIdx.x, gridDim.x));
+  const bool edge_wg = wid < a.n_edge;
   int b, seg0_lo, seg0_hi, seg1_lo = 0, seg1_hi = 0, own_lo = 0, own_hi = 0;
   int n_acc = 0, s_lo = 0, s_hi = 0;  // edge: accumulator slots, owned ones
   if (edge_wg) {
     // side 0: the head zone [0, edge), side 1: the tail zone [L - edge, L),
     // each in a workgroup of its own (edge_split), else both in one
-    const int side = a.edge_split ? static_cast<int>(blockIdx.x & 1) : -1;
-    b = a.edge_split ? static_cast<int>(blockIdx.x >> 1) : static_cast<int>(blockIdx.x);
+    const int side = a.edge_split ? (wid & 1) : -1;
+    b = a.edge_split ? (wid >> 1) : wid;
     n_acc = a.whole ? L : 2 * a.edge;
     s_lo = side == 1 ? a.edge : 0;
     s_hi = side == 0 ? a.edge : n_acc;
@@ -164,7 +166,7 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves(N1, N2)) void mel_backwa
     }
     for (int s = s_lo + tid; s < s_hi; s += NT) acc[s] = 0.0f;
   } else {
-    const int w = blockIdx.x - a.n_edge;
+    const int w = wid - a.n_edge;
     // (the division expands to vector code: bring the uniform result back to
     // a scalar register)
     b = __builtin_amdgcn_readfirstlane(w / a.tiles_per_signal);

@@ -221,6 +221,19 @@ __device__ __forceinline__ float2 lds_pair_raw<int16_t>(const unsigned char* p) 
 template <typename T>
 constexpr float kSampleScale = std::is_same<T, int16_t>::value ? (1.0f / 32768.0f) : 1.0f;
 
+// Workgroup -> tile order.  The dispatcher deals workgroups to the chip's 8
+// XCDs in turn (workgroup i to XCD i mod 8), and each XCD has its own L2:
+// tile i + 1 on another XCD than tile i would fetch the 128-byte lines the
+// two tiles share (input halo, output rows where tiles meet) a second time.
+// This order gives XCD x the contiguous tiles [x*q + min(x, r), ...) of n
+// = 8q + r, so neighbouring tiles share an L2 (a bijection on [0, n)).
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_tile_order(int wg, int n) {
+  const int q = n / kXcds, r = n - q * kXcds;
+  const int x = wg % kXcds, i = wg / kXcds;
+  return x * q + min(x, r) + i;
+}
+
 // |X|^p from |X|^2: PMODE 0 -> p = 2, 1 -> p = 1, 2 -> any p > 0 (hp = p/2).
 template <int PMODE>
 __device__ __forceinline__ float power_of(float sq, float hp) {
@@ -302,7 +315,7 @@ __global__ __launch_bounds__((kThreads<N1, N2>), (kMinWavesPerSimd<N1, N2>)) voi
   // the per-thread table loads out of the loop and keep them live across
   // every pass, which costs more registers than it saves.)
   {
-    const int tile = blockIdx.x;
+    const int tile = __builtin_amdgcn_readfirstlane(xcd_tile_order(blockIdx.x, gridDim.x));
     const int b = tile / a.tiles_per_signal;
     const int t0 = (tile - b * a.tiles_per_signal) * G;
     const int nvalid = min(G, a.n_frames - t0);
