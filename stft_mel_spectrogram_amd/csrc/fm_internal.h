@@ -161,6 +161,7 @@ struct Plan {
   // backward
   std::vector<BinTap> taps;      // [n_fft/2 + 1]
   int bwd_chunk_max = 0;         // frames per backward pass at most
+  int bwd_chunk_override = 0;    // FM_BWD_CHUNK, for sweeps (0: chosen per call)
   std::vector<int> bwd_wg_per_cu;  // [chunk frames] resident backward workgroups per CU
   const void* d_taps = nullptr;  // BinTap[n_fft/2 + 1]
 };

@@ -253,6 +253,7 @@ namespace {
 // the cost model is the forward's (rounds of resident workgroups times a
 // workgroup's pass-1 rounds plus a fixed part), ties to smaller passes.
 int choose_bwd_chunk(const Plan& p, int64_t batch, int64_t T, int halo, int64_t n_edge) {
+  if (p.bwd_chunk_override > halo) return p.bwd_chunk_override;
   const int ncu = p.n_cu > 0 ? p.n_cu : 256;
   const int slots = std::max(1, kBwdThreads / p.fft.n2);
   int best = p.bwd_chunk_max;

@@ -395,6 +395,11 @@ int build_host_plan(Plan& p, const fm_args& a) {
   while (cmax > 1 && bwd_lds_bytes(p, cmax) > 160 * 1024) --cmax;
   p.bwd_chunk_max = bwd_lds_bytes(p, cmax) <= 160 * 1024 ? cmax : 0;
   p.tile_override = 0;
+  p.bwd_chunk_override = 0;
+  if (const char* e = std::getenv("FM_BWD_CHUNK")) {
+    int v = std::atoi(e);
+    if (v >= 1 && v <= p.bwd_chunk_max) p.bwd_chunk_override = v;
+  }
   if (const char* e = std::getenv("FM_TILE_FRAMES")) {
     int v = std::atoi(e);
     if (v >= 1 && v <= tmax) p.tile_override = v;
