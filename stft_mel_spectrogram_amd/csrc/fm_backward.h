@@ -227,10 +227,10 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves(N1, N2)) void mel_backwa
   };
 
   // Pass 2 with one thread per (frame, row k1) (shapes with N1 <= 8): the
-  // row's N2-point DFT, then for each of its bins k = k1 + N1*k2 the split
-  // with the mirrored bin M - k read from the partner row (row N1 - k1, or
-  // the row itself for k1 = 0 and N1/2) through LDS, the gradient of |X|^p on
-  // both bins and the inverse-split value C[k] of its own bin, and the row's
+  // row's N2-point DFT, then the split with the mirrored bins M - k read from
+  // the partner row (row N1 - k1, or the row itself for k1 = 0 and N1/2)
+  // through LDS, the gradient of |X|^p and the inverse-split values C[k] and
+  // C[M - k], each pair computed by one of the two threads, and the row's
   // inverse DFT.  Partners are lanes of the same wave, and a wave's LDS
   // operations complete in order, so no barrier is needed inside.
   auto pass2_rows = [&](int nf) {
@@ -249,20 +249,30 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves(N1, N2)) void mel_backwa
     for (int j = 0; j < N2; ++j) row[j] = z[j];
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's rows are written
     __builtin_amdgcn_wave_barrier();
+    // Each pair (k, M - k) is computed once: this thread takes its bins
+    // k2 < hmine and sends C[M - k] to the mirrored slot (in the partner row,
+    // or its own row for the self-paired rows 0 and N1/2); the partner's pairs
+    // fill the rest of this row.
+    const bool r0 = (r == 0);
+    const int hmine = r0 ? N2 / 2 + 1 : (r <= N1 / 2 ? (N2 + 1) / 2 : N2 / 2);
+    constexpr int HMAX = N2 / 2 + 1;
     // zp[k2] = the mirror of bin r + N1*k2: row 0 -> its index (N2 - k2) % N2
     // (k2 = 0: bin M, i.e. Z[0]); other rows -> index N2 - 1 - k2 of the
     // partner row (the choice is made on the LDS address, not on registers)
-    const bool r0 = (r == 0);
-    float2 zp[N2];
+    float2 zp[HMAX];
+    float2* mdst[HMAX];
 #pragma unroll
-    for (int j = 0; j < N2; ++j) zp[j] = prow[r0 ? (N2 - j) % N2 : N2 - 1 - j];
+    for (int j = 0; j < HMAX; ++j) {
+      mdst[j] = const_cast<float2*>(prow) + (r0 ? (N2 - j) % N2 : N2 - 1 - j);
+      zp[j] = *mdst[j];
+    }
     // split twiddle exp(-2 pi i k/N), k = r + N1*k2: the table value of r times
     // the compile-time rotation exp(-2 pi i k2/(2 N2))
     const float2 w_r = a.tw_n[r];
     const float* dprow = dPt + f2 * K;
     const float* dk = dprow + r;        // dP[k]     = dk[N1*k2]
     const float* dm = dprow + (M - r);  // dP[M - k] = dm[-N1*k2]
-    static_for<0, N2>([&](auto k2c) {
+    static_for<0, HMAX>([&](auto k2c) {
       constexpr int k2 = decltype(k2c)::value;
       const float2 zk = z[k2];
       const float2 zm = zp[k2];
@@ -281,9 +291,21 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves(N1, N2)) void mel_backwa
       const float2 E = make_float2(hk.x + hm.x, hk.y - hm.y);   // H[k] + conj H[M-k]
       const float2 O = make_float2(hk.x - hm.x, hk.y + hm.y);   // H[k] - conj H[M-k]
       const float2 V = cmul(make_float2(w.x, -w.y), O);         // exp(+2 pi i k/N) O
-      z[k2] = make_float2(E.x - V.y, E.y + V.x);                // C[k] = E + i V
+      if (k2 < hmine) {
+        z[k2] = make_float2(E.x - V.y, E.y + V.x);              // C[k]   = E + i V
+        *mdst[k2] = make_float2(E.x + V.y, V.x - E.y);          // C[M-k] = conj(E - i V)
+      }
       if constexpr (k2 % kBwdPairGroup == kBwdPairGroup - 1) __builtin_amdgcn_sched_barrier(0);
     });
+    // the rest of this row: the values the partner (or this thread, as
+    // mirrors) wrote; every read of Z from LDS in this wave came first
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int j = 0; j < N2; ++j) {
+      const float2 t = row[j];
+      z[j] = j < hmine ? z[j] : t;
+    }
     // inverse N2-point DFT over k2 (conjugate, forward DFT, conjugate); the
     // partner's reads of this row were issued before these writes
 #pragma unroll
