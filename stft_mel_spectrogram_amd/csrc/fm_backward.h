@@ -103,7 +103,7 @@ template <int N1, int N2, int PMODE>
 __global__ __launch_bounds__(kBwdThreads, bwd_min_waves(N1, N2)) void mel_backward_kernel(BArgs a) {
   constexpr int M = N1 * N2;
   constexpr int K = M + 1;        // one-sided bins; odd: the dP tile's frame stride
-  constexpr int SY = exchange_stride(M);
+  constexpr int SY = bwd_exchange_stride(M);
   constexpr int DS = 2 * SY;      // float stride of a frame of frame gradients
   constexpr int NF = 2 * M;       // n_fft
   constexpr int NPAIR = N1 / 2;

@@ -75,6 +75,9 @@ constexpr int kMelStageFloats = 16 * 65;
 constexpr int kExchangePad = 4;
 constexpr int kPowerPad = 0;
 constexpr int exchange_stride(int half) { return half + kExchangePad; }
+// The backward's exchange buffer (its second pass walks single rows).
+constexpr int kBwdExchangePad = 4;
+constexpr int bwd_exchange_stride(int half) { return half + kBwdExchangePad; }
 constexpr int power_stride(int half) { return half + 1 + kPowerPad; }
 
 // Backward pass: the filters that touch one one-sided bin.  A triangular

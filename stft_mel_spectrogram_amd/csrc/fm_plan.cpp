@@ -120,7 +120,11 @@ int bwd_edge(const Plan& p) {
   return (p.center && p.pad_mode != FM_PAD_CONSTANT) ? p.pad_left + 1 : 0;
 }
 
-int bwd_grad_offset(const Plan& p, int chunk) { return tile_exchange_bytes(p, chunk) / 4; }
+int bwd_grad_offset(const Plan& p, int chunk) {
+  // after the exchange buffer Y[chunk][bwd_exchange_stride], 16-byte aligned
+  const long y = static_cast<long>(std::max(chunk, 1)) * bwd_exchange_stride(p.n_fft / 2) * 8;
+  return static_cast<int>((y + 15) / 16 * 4);
+}
 
 int bwd_acc_offset(const Plan& p, int chunk) {
   return bwd_grad_offset(p, chunk) + std::max(chunk, 1) * p.n_freqs;
