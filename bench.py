@@ -151,7 +151,7 @@ def sleep_rate(torch) -> float:
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(frames are independent: a batch would shard across GPUs with no exchange).",
               file=sys.stderr)
         sys.exit(2)
