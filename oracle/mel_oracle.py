@@ -381,7 +381,9 @@ def mel_spectrogram_vjp(x, grad_out, *, sample_rate: int = 16000, n_fft: int = 4
                         mel_scale: str = "htk", chunk: int = 1) -> np.ndarray:
     """f64 gradient of sum(grad_out * mel_spectrogram(x)) with respect to x.
 
-    The forward chain (padding, framing, window, one-sided DFT, |X|**power,
+    specux "Backends" page, section "Gradients": a spectrogram's gradient is
+    the analytic adjoint of the transform (checked there against float64
+    gradcheck); the flashmel 0.1.0 page itself is inference-only.  The forward chain (padding, framing, window, one-sided DFT, |X|**power,
     mel projection) is run again and each step is replaced by its adjoint, in
     reverse order: the transposed filterbank, power_gradient,
     dft_onesided_adjoint, the window, overlap-add of the frames, and the
