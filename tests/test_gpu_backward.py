@@ -96,6 +96,12 @@ CASES = [
     ("hop100_nfft2048_circ", 2, 9000, dict(sample_rate=22050, n_fft=2048, hop_length=100,
                                            n_mels=80, pad_mode="circular")),
     ("hop64_nfft4096", 1, 8192, dict(sample_rate=44100, n_fft=4096, hop_length=64, n_mels=128)),
+    # frames that do not overlap: samples between frames get a zero gradient
+    ("hop400_nfft400", 2, 9001, dict(n_fft=400, hop_length=400, n_mels=40)),
+    ("hop500_gaps", 2, 9001, dict(n_fft=400, hop_length=500, n_mels=40)),
+    ("hop1000_gaps_constant", 1, 9001, dict(n_fft=400, hop_length=1000, n_mels=40,
+                                            pad_mode="constant")),
+    ("hop1_nfft64", 1, 300, dict(n_fft=64, hop_length=1, n_mels=16)),
 ]
 
 

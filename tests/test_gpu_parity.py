@@ -112,6 +112,19 @@ def test_ragged_large_fft(n_fft, hop):
     assert_parity(run_gpu(x, **targs), oracle(x, **targs), f"{n_fft}/{hop}")
 
 
+@pytest.mark.parametrize("n_fft,hop,L,pad_mode,center", [
+    (400, 400, 9001, "reflect", True), (400, 500, 9001, "reflect", True),
+    (400, 1000, 9001, "constant", True), (400, 777, 9001, "reflect", False),
+    (64, 1, 300, "reflect", True), (128, 1, 257, "circular", True)])
+def test_hop_extremes(n_fft, hop, L, pad_mode, center):
+    """Frames that do not overlap (hop >= n_fft: samples between frames are
+    never read) and hop = 1 (every sample starts a frame)."""
+    x = np.random.default_rng(hop + L).standard_normal((2, L)).astype(np.float32)
+    targs = dict(sample_rate=16000, n_fft=n_fft, hop_length=hop, n_mels=24, pad_mode=pad_mode,
+                 center=center)
+    assert_parity(run_gpu(x, **targs), oracle(x, **targs), f"n_fft={n_fft} hop={hop}")
+
+
 OTHER_FFT = [(64, 16, 40), (64, 20, 8), (128, 32, 40), (256, 64, 64), (256, 100, 128),
              (512, 128, 80), (512, 100, 256), (4096, 1024, 128), (4096, 512, 40)]
 
