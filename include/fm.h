@@ -50,9 +50,11 @@ extern "C" {
 #define FM_NORM_NONE 0
 #define FM_NORM_SLANEY 1
 
-/* sample types: input float32 or int16 raw PCM scaled by 1/32768 (README
- * "Usage"); output float32 or float16 (README "Usage" out_dtype: the f32
- * result rounded to nearest at the store, beyond 65504 it becomes inf).    */
+/* sample types.  Input: float32, or int16 PCM that the kernel multiplies by
+ * 2^-15 as it loads it (README "Usage" lists both input types and that
+ * scale).  Output: float32, or float16 (README "Usage", out_dtype): the
+ * float32 result rounded to nearest at the store; values past 65504 become
+ * inf.                                                                     */
 #define FM_F32 0
 #define FM_I16 1
 #define FM_F16 2
@@ -141,6 +143,13 @@ int fm_plan_create_host(fm_plan** out, int sample_rate, int n_fft,
 /*
  * fm_forward -- enqueue one mel-spectrogram forward pass on `stream`.
  *
+ * The flashmel 0.1.0 page, README "Usage", defines the call: a batch of
+ * signals (..., time) in float32 or int16 on the GPU gives (..., n_mels,
+ * n_frames), e.g. [8, 480000] at hop 160 gives [8, 128, 3001]; README "How
+ * it works" puts the whole chain (padding as index arithmetic, window, real
+ * FFT, |X|^power, sparse mel projection) in one kernel launch.  Here the
+ * leading dimensions are flattened into `batch`.
+ *
  *   in     device pointer to [batch, length] samples, row-major, contiguous,
  *          of type in_dtype (FM_F32: float, FM_I16: int16_t).
  *   out    device pointer to [batch, n_mels, n_frames] elements of the plan's
@@ -190,7 +199,9 @@ int fm_backward(const fm_plan* plan, const float* in, int64_t batch, int64_t len
                 const float* grad_out, float* grad_in, void* stream);
 
 /*
- * fm_out_frames -- frames per signal for a given length (L = length + 2*pad):
+ * fm_out_frames -- frames per signal for a given length (L = length + 2*pad),
+ * the last dimension of fm_forward's output (README "Usage": the output
+ * shape (..., n_mels, n_frames), 480000 samples at hop 160 giving 3001):
  *   center: 1 + floor(L / hop) for even n_fft (generally
  *           1 + floor((L + 2*(n_fft/2) - n_fft) / hop));
  *   else:   1 + floor((L - n_fft) / hop).

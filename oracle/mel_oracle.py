@@ -126,34 +126,50 @@ def frame_signal(xp: np.ndarray, n_fft: int, hop: int) -> np.ndarray:
 def hann_window(win_length: int) -> np.ndarray:
     """Periodic Hann window w[n] = 0.5 - 0.5*cos(2*pi*n/win), n < win.
 
-    flashmel page, ``flashmel/filters.py`` make_window: periodic Hann of
-    length win_length.  The angle is reduced on integers (n mod win) before
-    the cosine.
+    flashmel page, ``flashmel/filters.py`` (window construction): a periodic
+    Hann window of length win_length.  The angle is reduced on integers
+    (n mod win) before the cosine.
     """
     n = np.arange(win_length, dtype=np.int64)
     return 0.5 - 0.5 * np.cos(2.0 * np.pi * (n % win_length) / win_length)
 
 
-def make_window(n_fft: int, win_length: int, normalized) -> np.ndarray:
-    """STFT window of length n_fft with the STFT normalisation folded in.
+def window_scale(hann: np.ndarray, normalized) -> float:
+    """Factor the STFT normalisation multiplies the window by.
 
-    flashmel page, ``flashmel/filters.py`` make_window: True or "window"
-    divides by sqrt(sum w^2); "frame_length" divides by sqrt(win_length);
-    a window shorter than n_fft is zero-padded centred, left=(n_fft-win)//2.
+    flashmel page, ``flashmel/filters.py`` (window construction): the
+    normalisation is folded into the window.  ``True`` or ``"window"`` makes
+    the window's energy 1 (divide by its Euclidean norm); ``"frame_length"``
+    divides by the square root of the window length; ``False``/``None``
+    leaves it unscaled.
+    """
+    if normalized is None or normalized is False:
+        return 1.0
+    if normalized is True or (isinstance(normalized, str) and normalized == "window"):
+        return 1.0 / float(np.sqrt(np.dot(hann, hann)))
+    if isinstance(normalized, str) and normalized == "frame_length":
+        return 1.0 / float(np.sqrt(len(hann)))
+    raise ValueError(f"unknown normalized={normalized!r}")
+
+
+def make_window(n_fft: int, win_length: int, normalized) -> np.ndarray:
+    """The length-n_fft analysis window, evaluated position by position.
+
+    flashmel page, ``flashmel/filters.py`` (window construction): a periodic
+    Hann window of win_length samples sits centred in the n_fft-sample frame,
+    its first sample at offset (n_fft - win_length) // 2, and is zero
+    elsewhere; the STFT normalisation (window_scale) is a constant factor.
     """
     if win_length > n_fft or win_length < 1:
         raise ValueError("need 1 <= win_length <= n_fft")
-    w = hann_window(win_length)
-    if normalized is True or normalized == "window":
-        w = w / np.sqrt(np.sum(w * w))
-    elif normalized == "frame_length":
-        w = w / np.sqrt(win_length)
-    elif normalized not in (False, None):
-        raise ValueError(f"unknown normalized={normalized!r}")
-    left = (n_fft - win_length) // 2
-    out = np.zeros(n_fft)
-    out[left:left + win_length] = w
-    return out
+    hann = hann_window(win_length)
+    scale = window_scale(hann, normalized)
+    offset = (n_fft - win_length) // 2
+    w = np.empty(n_fft)
+    for n in range(n_fft):
+        j = n - offset                      # index into the Hann window
+        w[n] = hann[j] * scale if 0 <= j < win_length else 0.0
+    return w
 
 
 # ---------------------------------------------------------------------------

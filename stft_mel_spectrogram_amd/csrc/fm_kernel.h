@@ -80,7 +80,11 @@ using f32x4 = float __attribute__((ext_vector_type(4)));
 // KS is the power tile's frame stride.  Both operands come from LDS (the
 // weights were copied there); blocks are
 // padded to whole groups of kMelStepGroup steps, so the step loop has no
-// tail.  Columns beyond the tile read its last frame and are not stored.
+// tail.  Columns beyond the last valid frame read that frame again and are
+// not stored, so no column reads a power row that was not written; a step
+// run may reach up to 15 floats past a row's last bin, into the next row
+// (times zero weights) or, after the last valid frame, into floats the
+// kernel zeroes.
 // Output (element type OT: float, or _Float16 rounded to nearest): with
 // STAGE the 16 x 16*NFB result goes through the wave's LDS staging area
 // `stg` and each filter row leaves in one contiguous streaming store (lane =
@@ -96,7 +100,7 @@ __device__ __forceinline__ void mel_blocks(const float* P, const float* WL, floa
   const int fr = lane & 15, kq = lane >> 4;
   int roff[NFB];
 #pragma unroll
-  for (int f = 0; f < NFB; ++f) roff[f] = min(16 * f + fr, G - 1) * KS + kq;
+  for (int f = 0; f < NFB; ++f) roff[f] = min(16 * f + fr, nvalid - 1) * KS + kq;
   for (int bi = bb; bi < be; ++bi) {
     const int kb = blk[4 * bi], ks = blk[4 * bi + 1], woff = blk[4 * bi + 2],
               mel0 = blk[4 * bi + 3];
@@ -493,8 +497,10 @@ __global__ __launch_bounds__((kThreads<N1, N2>), (kMinWavesPerSimd<N1, N2>)) voi
     // instruction, lane l's 16 bytes at l*16), landing while the split runs.
     for (int c = wave; c < a.w_chunks; c += NW)
       __builtin_amdgcn_global_load_lds(a.blk_w + c * 256 + lane * 4, P + a.w_lds + c * 256, 16, 0, 0);
-    // the mel stage may read a few floats past the power tile: keep them 0
-    if (tid < kMelTileOverrun) P[G * SP + tid] = 0.0f;
+    // the mel stage may read up to kMelTileOverrun - 1 floats past the last
+    // valid frame's row: keep them 0 (in a ragged last tile that is the
+    // unwritten row nvalid, else the slack after the tile)
+    if (tid < kMelTileOverrun) P[nvalid * SP + tid] = 0.0f;
     if (has) {
       float* prow = P + f2 * SP;
       if constexpr (SP > K) {

@@ -315,9 +315,9 @@ int build_host_plan(Plan& p, const fm_args& a) {
   // Blocks of 16 filters; each covers the union of its filters' bin runs,
   // rounded up to whole groups of 4-bin steps and shifted left if it would
   // run past the last bin.  When 4*steps exceeds n_freqs it starts at bin 0
-  // and reads at most 15 floats past a frame's row: the next frame's first
-  // bins (times zero weights), or, for the tile's last frame, floats the
-  // kernel zeroes.
+  // and reads at most 15 floats past a frame's row, all with zero weights:
+  // the next frame's first bins, or, after the last valid frame of a tile
+  // (full or ragged), floats the kernel zeroes before the mel stage.
   {
     const int K = p.n_freqs;
     const int nb = (n_mels + kMelBlock - 1) / kMelBlock;

@@ -22,12 +22,18 @@ def _require_gpu():
 
 
 def run_gpu(x_np, **targs):
+    """The HIP forward pass through the C ABI, written into an output
+    tensor filled with NaN first, so an element the kernel fails to write
+    cannot pass on a previous call's value left in reused memory."""
     from stft_mel_spectrogram_amd import MelSpectrogram
     _require_gpu()
     mel = MelSpectrogram(**targs)
     x = torch.from_numpy(np.ascontiguousarray(x_np)).to("cuda")
-    y = mel(x)
+    shape = tuple(x.shape[:-1]) + (mel.n_mels, mel.out_frames(x.shape[-1]))
+    out = torch.full(shape, float("nan"), dtype=mel.out_dtype, device="cuda")
+    y = mel(x, out=out)
     torch.cuda.synchronize()
+    assert y.data_ptr() == out.data_ptr()
     return y.cpu().numpy()
 
 
@@ -294,6 +300,29 @@ def test_forced_tile_sizes(monkeypatch, n_fft, tiles):
         assert_parity(run_gpu(x, **targs), ref, f"n_fft={n_fft} tile={g}")
         assert_parity_f16(run_gpu(x, out_dtype=torch.float16, **targs), ref, f"f16 n_fft={n_fft} tile={g}")
     monkeypatch.delenv("FM_TILE_FRAMES")
+
+
+@pytest.mark.parametrize("n_mels", [1, 8, 16])
+@pytest.mark.parametrize("tile", [0, 7, 33, 47])
+def test_few_mels_full_band_ragged_tiles(monkeypatch, n_mels, tile):
+    """n_fft 400 with at most 16 mels up to Nyquist: the one 16-filter block
+    spans every bin (52 four-bin steps over a 201-float row), so the mel
+    stage reads past each frame's row; in the last, ragged tile of a signal
+    those floats must be zero, not whatever the LDS held before.  Ragged
+    length, forced tile widths (0: the width the launch chooses), f32 and f16
+    output, and a first launch of a wide many-mel plan that leaves non-zero
+    LDS behind."""
+    rng = np.random.default_rng(100 + n_mels)
+    x = (rng.standard_normal((3, 16_321)) * 0.2).astype(np.float32)
+    # fill the LDS of every compute unit with large values first
+    run_gpu((rng.standard_normal((8, 48_000)) * 1e3).astype(np.float32), sample_rate=16000,
+            n_fft=400, hop_length=160, n_mels=256)
+    targs = dict(sample_rate=16000, n_fft=400, hop_length=160, n_mels=n_mels, f_max=8000.0)
+    ref = oracle(x, **targs)
+    if tile:
+        monkeypatch.setenv("FM_TILE_FRAMES", str(tile))
+    assert_parity(run_gpu(x, **targs), ref, f"mels={n_mels} tile={tile}")
+    assert_parity_f16(run_gpu(x, out_dtype=torch.float16, **targs), ref, f"f16 mels={n_mels} tile={tile}")
 
 
 def test_int16_odd_length_and_misaligned_input():

@@ -251,14 +251,29 @@ def test_empty_filters_counted_independently():
     assert empty == [0, 3, 6, 13]
 
 
-def test_slaney_norm_unit_area():
-    fpts = O.mel_corner_frequencies(0.0, 8000.0, 30, "slaney")
-    fb_peak = O.triangles(fpts[1:-1], fpts) * (2.0 / (fpts[2:] - fpts[:-2]))
-    # a triangle of base (f[m+2]-f[m]) and height 2/(f[m+2]-f[m]) has area 1
-    np.testing.assert_allclose(np.diag(fb_peak) * (fpts[2:] - fpts[:-2]) / 2, 1.0, rtol=1e-13)
-    fbn = O.mel_filterbank(201, 0.0, 8000.0, 30, 16000, norm="slaney", mel_scale="slaney")
-    fb = O.mel_filterbank(201, 0.0, 8000.0, 30, 16000, norm=None, mel_scale="slaney")
-    np.testing.assert_allclose(fbn, fb * (2.0 / (fpts[2:] - fpts[:-2]))[None, :], rtol=1e-15)
+@pytest.mark.parametrize("mel_scale,n_mels,f_min,f_max", [("slaney", 30, 0.0, 8000.0),
+                                                          ("htk", 40, 0.0, 8000.0),
+                                                          ("slaney", 64, 125.0, 7600.0)])
+def test_slaney_norm_unit_area(mel_scale, n_mels, f_min, f_max):
+    """norm="slaney" normalises every filter to unit area.  Pinned by
+    quadrature: the oracle's filterbank evaluated on a very fine bin grid
+    (n_fft = 2^21 at 16 kHz, bins 0.0076 Hz apart) and integrated with the
+    trapezoid rule gives area 1 for every filter, without restating the
+    normalising factor.  Each filter's peak times half its base (the corner
+    spacing) is 1 as well."""
+    sr, n_fft = 16000, 1 << 21
+    n_freqs = n_fft // 2 + 1
+    df = (sr // 2) / (n_freqs - 1)
+    fbn = O.mel_filterbank(n_freqs, f_min, f_max, n_mels, sr, norm="slaney", mel_scale=mel_scale)
+    area = df * (fbn[1:] + fbn[:-1]).sum(axis=0) / 2.0
+    np.testing.assert_allclose(area, 1.0, rtol=0, atol=2e-4)
+    fpts = O.mel_corner_frequencies(f_min, f_max, n_mels, mel_scale)
+    peak = fbn.max(axis=0)
+    np.testing.assert_allclose(peak * (fpts[2:] - fpts[:-2]) / 2.0, 1.0, rtol=0, atol=1e-3)
+    # without the norm the same filters peak at 1 and have area (base / 2)
+    fb = O.mel_filterbank(n_freqs, f_min, f_max, n_mels, sr, norm=None, mel_scale=mel_scale)
+    area_raw = df * (fb[1:] + fb[:-1]).sum(axis=0) / 2.0
+    np.testing.assert_allclose(area_raw, (fpts[2:] - fpts[:-2]) / 2.0, rtol=2e-4)
 
 
 # --------------------------------------------------------------------------- whole pipeline

@@ -7,6 +7,7 @@ for functions that are positively homogeneous of degree `power` in x.
 """
 import numpy as np
 import pytest
+import scipy.signal
 import torch
 
 from oracle import mel_oracle as O
@@ -71,9 +72,10 @@ def test_euler_identity(power, mode):
 def _torch_vjp(x, u, n_fft, hop, win_length, power, center, pad_mode, fb):
     """The same gradient through torch.stft's autograd in float64 (CPU)."""
     xt = torch.tensor(x, dtype=torch.float64, requires_grad=True)
-    w = torch.hann_window(win_length, periodic=True, dtype=torch.float64)
-    left = (n_fft - win_length) // 2
-    w = torch.nn.functional.pad(w, (left, n_fft - win_length - left))
+    # scipy's periodic Hann placed in the middle of an all-zero n_fft frame
+    w = torch.zeros(n_fft, dtype=torch.float64)
+    start = (n_fft - win_length) // 2
+    w[start:start + win_length] = torch.from_numpy(scipy.signal.get_window("hann", win_length))
     S = torch.stft(xt, n_fft, hop_length=hop, win_length=n_fft, window=w, center=center,
                    pad_mode=pad_mode, normalized=False, onesided=True, return_complex=True)
     P = S.abs() ** power                                       # [b, K, T]

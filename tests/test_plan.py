@@ -201,6 +201,41 @@ def test_mel_blocks_equal_the_csr_filterbank(name, over):
     assert max(cost) - min(cost) <= max(blocks[:, 1]) + 2
 
 
+# Floats the forward kernel zeroes after the last valid frame's power row
+# (the mel stage may read that far past a row).
+MEL_ROW_OVERRUN = 16
+
+
+@pytest.mark.parametrize("n_fft", [64, 128, 256, 400, 512, 1024, 2048, 4096])
+def test_mel_block_reads_stay_in_written_or_zeroed_floats(n_fft):
+    """For every n_mels 1..256 and f_max at or below Nyquist: a block's bin
+    run starts at bin >= 0 and ends at most MEL_ROW_OVERRUN - 1 floats past
+    the frame's last bin, and every weight on a bin past the row is 0.  The
+    kernel writes the power rows of the tile's valid frames and zeroes
+    MEL_ROW_OVERRUN floats after the last valid one, so in any tile (ragged
+    or full) the mel stage reads only written or zeroed floats, and what it
+    reads past a row is multiplied by 0."""
+    sr = 16000
+    K = n_fft // 2 + 1
+    worst = 0
+    for f_max in (sr / 2, 0.43 * sr):
+        for n_mels in range(1, 257):
+            p = N.Plan(device=False, sample_rate=sr, n_fft=n_fft, hop_length=n_fft // 4,
+                       n_mels=n_mels, f_max=f_max)
+            blocks, _, wts = p.mel_blocks()
+            for kb, ks, off, mel0 in blocks:
+                assert kb >= 0
+                end = kb + 4 * ks                       # one past the last bin read
+                assert end - K < MEL_ROW_OVERRUN, (n_fft, n_mels, f_max, kb, ks)
+                worst = max(worst, end - K)
+                if end > K:
+                    w = wts[off:off + 64 * ks].reshape(ks, 4, 16)   # [step, bin, filter]
+                    bins = kb + 4 * np.arange(ks)[:, None] + np.arange(4)[None, :]
+                    assert np.all(w[bins >= K] == 0.0), (n_fft, n_mels, f_max)
+    if n_fft == 400:
+        assert worst > 0          # this shape does read past its rows (few mels, f_max = sr/2)
+
+
 @pytest.mark.parametrize("n_fft", [64, 128, 256, 400, 512, 1024, 2048, 4096])
 def test_twiddles(n_fft):
     p = N.Plan(device=False, sample_rate=16000, n_fft=n_fft, hop_length=n_fft // 4, n_mels=40)
