@@ -225,12 +225,26 @@ typedef struct fm_plan_info {
   int pad, normalized, out_dtype;
   int nnz;          /* nonzero filterbank weights (CSR length)              */
   int w_max;        /* widest filter (bins)                                 */
-  int fft_n1, fft_n2; /* complex FFT of n_fft/2 = fft_n1 * fft_n2 points    */
-  int tile_frames;  /* frames per workgroup tile                            */
+  int fft_n1, fft_n2; /* complex FFT of n_fft/2 = fft_n1 * fft_n2 points of
+                       the split forward kernel and of the backward          */
+  int tile_frames;  /* frames per workgroup tile (paired: per chunk)        */
   int threads;      /* threads per workgroup                                */
   int lds_bytes;    /* dynamic LDS per workgroup                            */
   int has_device;   /* 1 if the plan owns device tables                     */
+  int forward_variant; /* FM_FWD_SPLIT or FM_FWD_PAIRED (see below)         */
 } fm_plan_info;
+
+/* Forward kernel variants.  SPLIT: each frame's real FFT through a complex
+ * FFT of n_fft/2 points and the real-spectrum split, one tile of frames per
+ * workgroup.  PAIRED: two frames per complex FFT of n_fft points (the
+ * pages' packing of two real frames into one complex transform, README "How
+ * it works"), persistent workgroups that walk their frames in chunks and load
+ * the next chunk while transforming the current one; built for n_fft = 400.
+ * A plan takes PAIRED where it is built and fits, SPLIT otherwise; the
+ * environment variable FM_FORWARD=split|paired, read at plan creation,
+ * forces one (for A/B measurements).                                      */
+#define FM_FWD_SPLIT 0
+#define FM_FWD_PAIRED 1
 
 int fm_plan_info_get(const fm_plan* plan, fm_plan_info* info);
 

@@ -25,9 +25,11 @@ SOURCES = ["fm_api.cpp", "fm_plan.cpp", "fm_launch.hip"]
 
 
 def sources() -> list:
-    """Host/ABI sources plus one fm_shape_<n1>x<n2>.hip per built FFT shape."""
+    """Host/ABI sources plus one fm_shape_<n1>x<n2>.hip per built FFT shape and
+    one fm_pair_<r>x<r>.hip per paired-kernel shape."""
     shapes = sorted(os.path.basename(f) for f in glob.glob(os.path.join(CSRC, "fm_shape_*.hip")))
-    return SOURCES + shapes
+    pairs = sorted(os.path.basename(f) for f in glob.glob(os.path.join(CSRC, "fm_pair_*.hip")))
+    return SOURCES + shapes + pairs
 
 # Packed-FP32 VALU forms are switched off for all device code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

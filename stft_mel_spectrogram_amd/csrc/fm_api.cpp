@@ -148,9 +148,11 @@ int fm_plan_info_get(const fm_plan* plan, fm_plan_info* info) {
   info->w_max = p.w_max;
   info->fft_n1 = p.fft.n1;
   info->fft_n2 = p.fft.n2;
-  info->tile_frames = p.tile_max;
-  info->threads = p.threads;
-  info->lds_bytes = p.lds_bytes;
+  const bool paired = p.fwd_variant == fm::kFwdPaired;
+  info->tile_frames = paired ? p.pair_chunk : p.tile_max;
+  info->threads = paired ? fm::kPairThreadsHost : p.threads;
+  info->lds_bytes = paired ? p.pair_lds_bytes : p.lds_bytes;
+  info->forward_variant = p.fwd_variant;
   info->has_device = p.has_device ? 1 : 0;
   return FM_OK;
 }

@@ -178,7 +178,56 @@ struct DftComposite {
   }
 };
 
+// R = A * B with gcd(A, B) = 1 (Good-Thomas prime-factor algorithm): the
+// input index n = (B*a + A*b) mod R and the output index k with k = ka
+// (mod A), k = kb (mod B) turn the DFT into A-point DFTs over a followed by
+// B-point DFTs over b with no twiddle factors between them, because
+// exp(-2 pi i n k / R) = exp(-2 pi i a ka / A) * exp(-2 pi i b kb / B).
+constexpr int mod_inverse(int x, int m) {
+  for (int y = 1; y < m; ++y)
+    if ((x * y) % m == 1) return y;
+  return 0;
+}
+template <int R, int A>
+struct DftPrimeFactor {
+  static constexpr int B = R / A;
+  static_assert(A * B == R && mod_inverse(B % A, A) > 0, "factors must be coprime");
+  static constexpr int CA = B * mod_inverse(B % A, A);  // 1 mod A, 0 mod B
+  static constexpr int CB = A * mod_inverse(A % B, B);  // 0 mod A, 1 mod B
+  __host__ __device__ __forceinline__ static void run(float2* v) {
+    float2 u[R];  // u[b*A + ka]
+    static_for<0, B>([&](auto bi) {
+      constexpr int b = decltype(bi)::value;
+      float2 t[A];
+      static_for<0, A>([&](auto ai) {
+        constexpr int a = decltype(ai)::value;
+        t[a] = v[(B * a + A * b) % R];
+      });
+      Dft<A>::run(t);
+      static_for<0, A>([&](auto ki) {
+        constexpr int ka = decltype(ki)::value;
+        u[b * A + ka] = t[ka];
+      });
+    });
+    static_for<0, A>([&](auto ki) {
+      constexpr int ka = decltype(ki)::value;
+      float2 s[B];
+      static_for<0, B>([&](auto bi) {
+        constexpr int b = decltype(bi)::value;
+        s[b] = u[b * A + ka];
+      });
+      Dft<B>::run(s);
+      static_for<0, B>([&](auto kbi) {
+        constexpr int kb = decltype(kbi)::value;
+        v[(ka * CA + kb * CB) % R] = s[kb];
+      });
+    });
+  }
+};
+
 template <> struct Dft<8> : DftComposite<8, 2> {};
+template <> struct Dft<10> : DftPrimeFactor<10, 2> {};
+template <> struct Dft<20> : DftPrimeFactor<20, 4> {};
 template <> struct Dft<16> : DftComposite<16, 4> {};
 template <> struct Dft<25> : DftComposite<25, 5> {};
 template <> struct Dft<32> : DftComposite<32, 4> {};

@@ -109,6 +109,20 @@ constexpr int bwd_chunk_cap(int n1, int n2, int threads) {
   return c < 64 ? c : 64;
 }
 
+// Forward kernel variants.
+constexpr int kFwdSplit = 0;
+constexpr int kFwdPaired = 1;
+// Paired kernel: R x R complex points per frame pair (n_fft = R*R); shapes
+// built into the library.
+constexpr int pair_radix_for(int n_fft) { return n_fft == 400 ? 20 : 0; }
+constexpr int kPairThreadsHost = 256;
+constexpr int kPairSpanFloatsHost = 4096;
+constexpr int kPairOutPitchHost = 36;
+// Layout of the paired kernel's LDS for radix r, chunks of `chunk` frames,
+// n_mels filters and `w_floats` mel weights; returns the total bytes (offsets
+// through the pointers: span buffer bytes, weights floats).
+int pair_lds_layout(int r, int chunk, int n_mels, long w_floats, int* span_b, int* w_f);
+
 // Threads per workgroup of an FFT shape.  n_fft = 2048 (32 x 32) tiles fill
 // the LDS of a CU on their own; 8 waves instead of 4 give the CU two waves
 // per SIMD and each pass-1 thread a single frame.
@@ -161,6 +175,17 @@ struct Plan {
   const void* d_mel_w = nullptr;  // float[nnz]
   const void* d_mel_tbl = nullptr;    // int32[8 + 4*n_blocks]: wave_beg, pad, blocks
   const void* d_blk_w = nullptr;      // float[blk_w.size()]
+  // forward kernel variant: FM_FWD_SPLIT (fm_kernel.h: complex FFT of n_fft/2
+  // points and the real split, one tile per workgroup) or FM_FWD_PAIRED
+  // (fm_pair.h: two frames per complex FFT of n_fft points, persistent
+  // workgroups walking their frames in chunks)
+  int fwd_variant = 0;
+  int pair_r = 0;              // paired: n_fft = pair_r * pair_r
+  int pair_chunk = 0;          // paired: frames per chunk at most (even)
+  int pair_lds_bytes = 0;      // paired: dynamic LDS per workgroup
+  int pair_span_lds = 0;       //   byte offset of the sample span buffer
+  int pair_w_lds = 0;          //   float offset of the mel weights
+  int pair_wg_per_cu = 1;      // paired: resident workgroups per CU (device)
   // backward
   std::vector<BinTap> taps;      // [n_fft/2 + 1]
   int bwd_chunk_max = 0;         // frames per backward pass at most
@@ -206,6 +231,9 @@ int64_t out_frames(const Plan& p, int64_t length);
 // Device side (fm_launch.hip).
 int upload_plan(Plan& p);
 void free_plan_device(Plan& p);
+// (paired kernel entry points, fm_pair_*.hip)
+template <int R>
+void* pair_kernel_for(int in_dtype, int pmode);
 int launch_forward(const Plan& p, const void* in, int in_dtype, int64_t batch,
                    int64_t length, void* out, void* stream);
 int launch_backward(const Plan& p, const float* in, int64_t batch, int64_t length,

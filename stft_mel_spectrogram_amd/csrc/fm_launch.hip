@@ -8,6 +8,7 @@
 #include <vector>
 
 #include "fm_backward.h"
+#include "fm_pair.h"
 
 namespace fm {
 
@@ -39,6 +40,11 @@ void* select_kernel(const Plan& p, int in_dtype, bool copy) {
   if (p.fft.n1 == A && p.fft.n2 == B) return kernel_for<A, B>(in_dtype, pm, copy);
   FM_FOR_EACH_SHAPE(FM_SELECT_SHAPE)
 #undef FM_SELECT_SHAPE
+  return nullptr;
+}
+
+void* select_pair_kernel(const Plan& p, int in_dtype) {
+  if (p.pair_r == 20) return pair_kernel_for<20>(in_dtype, power_mode(p));
   return nullptr;
 }
 
@@ -111,6 +117,19 @@ int upload_plan(Plan& p) {
     if (!k) return set_error(FM_E_UNSUPPORTED, "no kernel for this n_fft");
     e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, p.lds_bytes);
     if (e != hipSuccess) return hip_fail(e, "hipFuncSetAttribute");
+  }
+  // The paired kernel: LDS opt-in and residency.
+  if (p.fwd_variant == kFwdPaired) {
+    for (int dt : {FM_F32, FM_I16}) {
+      void* k = select_pair_kernel(p, dt);
+      if (!k) return set_error(FM_E_UNSUPPORTED, "no paired kernel for this n_fft");
+      e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, p.pair_lds_bytes);
+      if (e != hipSuccess) return hip_fail(e, "hipFuncSetAttribute (paired)");
+    }
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, select_pair_kernel(p, FM_F32), kPairThreads,
+                                                     p.pair_lds_bytes) == hipSuccess)
+      p.pair_wg_per_cu = std::max(1, n);
   }
   // Resident workgroups per CU for each tile size (registers and LDS).
   p.wg_per_cu.assign(p.tile_max + 1, 1);
@@ -201,6 +220,41 @@ int launch_forward(const Plan& p, const void* in, int in_dtype, int64_t batch, i
   hipError_t e = hipGetDevice(&cur);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
   if (cur != p.device) return set_error(FM_E_INVAL, "plan belongs to another device than the current one");
+  if (p.fwd_variant == kFwdPaired) {
+    if (length > (1 << 29)) return set_error(FM_E_INVAL, "problem too large for one launch (length <= 2^29)");
+    const int64_t total = batch * T;
+    const int64_t slots = static_cast<int64_t>(p.n_cu > 0 ? p.n_cu : 256) * p.pair_wg_per_cu;
+    const int64_t grid = std::min(total, slots);
+    PArgs a;
+    a.in = in;
+    a.out = out;
+    a.win = static_cast<const float*>(p.d_win2);
+    a.tw_n = static_cast<const float2*>(p.d_tw_n);
+    a.mel_tbl = static_cast<const int*>(p.d_mel_tbl);
+    a.blk_w = static_cast<const float*>(p.d_blk_w);
+    a.length = length;
+    a.in_elems = batch * length;
+    a.total = total;
+    a.n_frames = static_cast<int>(T);
+    a.hop = p.hop;
+    a.pad = p.pad_left + p.zpad;
+    a.zpad = p.zpad;
+    a.pad_mode = p.pad_mode;
+    a.n_mels = p.n_mels;
+    a.chunk = p.pair_chunk;
+    a.w_floats = static_cast<int>(p.blk_w.size());
+    a.out_f16 = p.out_dtype == FM_F16 ? 1 : 0;
+    a.half_power = static_cast<float>(p.power * 0.5);
+    a.span_lds = p.pair_span_lds;
+    a.w_lds = p.pair_w_lds;
+    void* k = select_pair_kernel(p, in_dtype);
+    if (!k) return set_error(FM_E_UNSUPPORTED, "no paired kernel for this n_fft");
+    void* args[] = {&a};
+    e = hipLaunchKernel(k, dim3(static_cast<unsigned>(grid)), dim3(kPairThreads), args,
+                        static_cast<size_t>(p.pair_lds_bytes), static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "kernel launch (paired)");
+    return FM_OK;
+  }
   const int G = choose_tile(p, batch, T);
   const int64_t tiles = (T + G - 1) / G;
   if (length > (1 << 29) || tiles * batch > INT32_MAX)

@@ -114,6 +114,23 @@ int tile_lds_bytes(const Plan& p, int frames) {
   return static_cast<int>(std::max<long>(pass1, after_fft));
 }
 
+int pair_lds_layout(int r, int chunk, int n_mels, long w_floats, int* span_b, int* w_f) {
+  const int nf = r * r;
+  // exchange buffer (pairs x (n_fft + 4) complex), which holds the tables at
+  // the start and each chunk's output tile (n_mels rounded up to 16 rows of
+  // kPairOutPitchHost floats) during the mel stage
+  const long y = static_cast<long>(kPairThreadsHost / r) * (nf + 4) * 8;
+  const long o = static_cast<long>((n_mels + 15) / 16 * 16) * kPairOutPitchHost * 4;
+  const long region = (std::max(std::max(y, o), 8L * nf) + 15) / 16 * 16;
+  // span buffer, later the power tile (chunk rows of n_fft/2 + 1 floats plus
+  // the zeroed overrun)
+  const long p_floats = static_cast<long>(chunk) * (nf / 2 + 1) + kMelTileOverrun;
+  const long span = (std::max<long>(kPairSpanFloatsHost, p_floats) * 4 + 15) / 16 * 16;
+  if (span_b) *span_b = static_cast<int>(region);
+  if (w_f) *w_f = static_cast<int>((region + span) / 4);
+  return static_cast<int>(region + span + 4 * w_floats);
+}
+
 int bwd_edge(const Plan& p) {
   // centre padding that copies signal samples hands gradients back to the
   // first and last n_fft/2 + 1 samples (constant padding copies none)
@@ -398,6 +415,29 @@ int build_host_plan(Plan& p, const fm_args& a) {
   int cmax = bwd_chunk_cap(fs.n1, fs.n2, kBwdThreads);
   while (cmax > 1 && bwd_lds_bytes(p, cmax) > 160 * 1024) --cmax;
   p.bwd_chunk_max = bwd_lds_bytes(p, cmax) <= 160 * 1024 ? cmax : 0;
+  // paired forward kernel where it is built and its chunks keep most of the
+  // workgroup busy: two full passes of R threads per frame pair need
+  // 2*floor(256/R) frames per chunk, whose samples ((chunk-1)*hop + n_fft,
+  // plus alignment slack) fit the span buffer; FM_FORWARD=split|paired
+  // overrides the choice (for A/B measurements)
+  p.fwd_variant = kFwdSplit;
+  p.pair_r = pair_radix_for(n_fft);
+  if (p.pair_r > 0 && p.w_in_lds) {
+    const int cmax = 2 * (kPairThreadsHost / p.pair_r);
+    int c = cmax;
+    while (c > 2 && static_cast<long>(c - 1) * hop_length + n_fft + 16 > kPairSpanFloatsHost) c -= 2;
+    const bool fits = static_cast<long>(c - 1) * hop_length + n_fft + 16 <= kPairSpanFloatsHost;
+    const int bytes = pair_lds_layout(p.pair_r, c, n_mels, static_cast<long>(p.blk_w.size()),
+                                      &p.pair_span_lds, &p.pair_w_lds);
+    p.pair_chunk = c;
+    p.pair_lds_bytes = bytes;
+    bool use = false;  // measured slower than the split kernel so far: opt-in only
+    if (const char* e = std::getenv("FM_FORWARD")) {
+      if (std::string(e) == "split") use = false;
+      if (std::string(e) == "paired" && fits && bytes <= 160 * 1024) use = true;
+    }
+    if (use) p.fwd_variant = kFwdPaired;
+  }
   p.tile_override = 0;
   p.bwd_chunk_override = 0;
   if (const char* e = std::getenv("FM_BWD_CHUNK")) {
