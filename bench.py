@@ -55,22 +55,48 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-copy-probe", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle sample")
+    ap.add_argument("--oracle-table", action="store_true",
+                    help="time only the oracle, on each of the five benchmark workloads (median "
+                         "of 3 bounded samples each); one JSON line per workload, no GPU use")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="measured HBM bytes per launch (from rocprofv3 --pmc), if present")
     return ap.parse_args()
 
 
+def host_cpu() -> dict:
+    """The host the oracle runs on: logical CPUs, CPU model, BLAS threads."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        threads = max([i.get("num_threads", 1) for i in blas] or [1])
+        lib = ",".join(sorted({f"{i.get('internal_api')} {i.get('version')}" for i in blas})) or None
+    except Exception:  # pragma: no cover
+        threads, lib = 1, None
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):  # pragma: no cover
+        affinity = None
+    return {"cpu_count": os.cpu_count(), "cpu_affinity": affinity, "cpu_model": model,
+            "blas_threads": int(threads), "blas": lib}
+
+
 def cpu_baseline(cfg: dict, budget_s: float, backward: bool = False) -> dict:
     """The oracle as it stands, on whole signals of the workload, repeated
     until about `budget_s` seconds of CPU work; frames/s (with `backward`,
-    the oracle's vector-Jacobian product)."""
+    the oracle's vector-Jacobian product).  `cores` is the number of BLAS
+    threads the oracle's products run on (the rest of it is one thread)."""
     from oracle import mel_oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()
-                       if i.get("user_api") == "blas"] or [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
+    host = host_cpu()
+    threads = host["blas_threads"]
     targs = W.transform_args(cfg)
     x = W.make_signal(W.workload(cfg["name"], batch=1))
     if backward:
@@ -94,7 +120,23 @@ def cpu_baseline(cfg: dict, budget_s: float, backward: bool = False) -> dict:
     return {"value": frames / dt, "unit": "frames/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{runs} x one {cfg['length']}-sample signal of the {cfg['name']} workload "
                       f"({'backward, ' if backward else ''}"
-                      f"{frames} frames, {dt:.1f} s, numpy f64 with BLAS threads)"}
+                      f"{frames} frames, {dt:.1f} s, numpy f64 with BLAS threads)",
+            **host}
+
+
+def oracle_table(budget_s: float) -> None:
+    """The oracle's forward rate on each of the five benchmark workloads:
+    three bounded samples each (whole signals, about `budget_s` seconds per
+    sample), the median printed as one JSON line per workload."""
+    for name in ("tiny", "whisper", "int16", "pow2", "large"):
+        cfg = W.workload(name)
+        runs = [cpu_baseline(cfg, budget_s) for _ in range(3)]
+        vals = sorted(r["value"] for r in runs)
+        print(json.dumps({"workload": name, "oracle_frames_per_s_median": vals[1],
+                          "runs": vals, "sample": runs[1]["sample"],
+                          **{k: runs[0][k] for k in ("cores", "cpu_count", "cpu_affinity",
+                                                      "cpu_model", "blas_threads", "blas")}}),
+              flush=True)
 
 
 def copy_probe(torch, dev, nbytes: int, reps: int = 50) -> dict:
@@ -150,6 +192,9 @@ def sleep_rate(torch) -> float:
 
 def main():
     args = parse()
+    if args.oracle_table:
+        oracle_table(args.cpu_seconds)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(frames are independent: a batch would shard across GPUs with no exchange).",

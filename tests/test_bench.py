@@ -30,9 +30,14 @@ def test_more_than_one_gpu_is_refused_before_any_gpu_work(argv, env):
 def test_cpu_baseline_object(backward):
     cfg = W.workload("tiny")
     res = bench.cpu_baseline(cfg, 0.05, backward=backward)
-    assert set(res) == {"value", "unit", "cores", "kind", "sample"}
+    assert set(res) == {"value", "unit", "cores", "kind", "sample", "cpu_count", "cpu_affinity",
+                        "cpu_model", "blas_threads", "blas"}
     assert res["unit"] == "frames/s" and res["kind"] == "oracle"
     assert res["value"] > 0 and isinstance(res["cores"], int) and res["cores"] >= 1
+    # the host is described: logical CPUs, model, and the BLAS threads the
+    # oracle's products use (which `cores` reports)
+    assert res["cpu_count"] == os.cpu_count() and res["cores"] == res["blas_threads"]
+    assert res["cpu_model"] is None or isinstance(res["cpu_model"], str)
     assert ("backward" in res["sample"]) == backward
     # frames counted are whole signals of the workload
     m = re.match(r"(\d+) x one (\d+)-sample signal", res["sample"])
