@@ -184,10 +184,20 @@ def _dft_basis(n_fft: int):
     The product n*k is reduced modulo N in exact integer arithmetic first, so
     each f64 angle is within one rounding of its true value.
     """
-    n = np.arange(n_fft, dtype=np.int64)[:, None]
     k = np.arange(n_fft // 2 + 1, dtype=np.int64)[None, :]
-    theta = 2.0 * np.pi * ((n * k) % n_fft) / n_fft
-    return np.cos(theta), np.sin(theta)
+    # only N distinct angles occur: evaluate each once and index by (n*k) mod N
+    # (the same f64 value per entry as evaluating the entry's own angle),
+    # filling the matrices a block of rows at a time
+    theta = 2.0 * np.pi * np.arange(n_fft, dtype=np.int64) / n_fft
+    cos_t, sin_t = np.cos(theta), np.sin(theta)
+    c = np.empty((n_fft, n_fft // 2 + 1))
+    s = np.empty_like(c)
+    for n0 in range(0, n_fft, 256):
+        n = np.arange(n0, min(n_fft, n0 + 256), dtype=np.int64)[:, None]
+        j = (n * k) % n_fft
+        c[n0:n0 + n.shape[0]] = cos_t[j]
+        s[n0:n0 + n.shape[0]] = sin_t[j]
+    return c, s
 
 
 def dft_onesided(frames: np.ndarray) -> np.ndarray:
@@ -199,6 +209,8 @@ def dft_onesided(frames: np.ndarray) -> np.ndarray:
     """
     n_fft = frames.shape[-1]
     c, s = _dft_basis(n_fft)
+    # (contiguous rows, so that the products run as BLAS matrix products)
+    frames = np.ascontiguousarray(frames)
     return frames @ c - 1j * (frames @ s)
 
 

@@ -121,7 +121,7 @@ def test_dft_matches_pure_python_brute_force(N):
         np.testing.assert_allclose(got[r], _brute_dft(f[r].tolist()), rtol=0, atol=1e-12)
 
 
-@pytest.mark.parametrize("N", [400, 1024, 2048])
+@pytest.mark.parametrize("N", [400, 1024, 2048, 16384])
 def test_dft_matches_numpy_rfft(N):
     f = np.random.default_rng(N).standard_normal((4, N))
     got = O.dft_onesided(f)
@@ -129,7 +129,7 @@ def test_dft_matches_numpy_rfft(N):
     assert np.max(np.abs(got - ref)) <= 1e-12 * np.max(np.abs(ref))
 
 
-@pytest.mark.parametrize("N", [16, 400, 2048])
+@pytest.mark.parametrize("N", [16, 400, 2048, 8192])
 def test_parseval_per_frame(N):
     f = np.random.default_rng(7).standard_normal((5, N))
     P = O.power_spectrum(O.dft_onesided(f), 2.0)
@@ -146,7 +146,8 @@ def test_power_one_is_sqrt_of_power_two():
 
 # --------------------------------------------------------------------------- tone closed form
 
-@pytest.mark.parametrize("N,sr,k0,n_mels", [(400, 16000, 25, 80), (1024, 16000, 70, 80)])
+@pytest.mark.parametrize("N,sr,k0,n_mels", [(400, 16000, 25, 80), (1024, 16000, 70, 80),
+                                            (16384, 44100, 1234, 256)])
 def test_pure_tone_closed_form(N, sr, k0, n_mels):
     """A*cos(2*pi*k0*n/N + phi) under a periodic Hann window gives |X[k0]| = A*N/4,
     |X[k0 +- 1]| = A*N/8 and 0 elsewhere in every interior frame, so the mel
@@ -162,7 +163,7 @@ def test_pure_tone_closed_form(N, sr, k0, n_mels):
     assert np.allclose(mag[:, k0 - 1], A * N / 8, rtol=1e-12)
     assert np.allclose(mag[:, k0 + 1], A * N / 8, rtol=1e-12)
     rest = np.delete(mag, [k0 - 1, k0, k0 + 1], axis=1)
-    assert rest.max() < 1e-9
+    assert rest.max() < 2e-11 * (A * N / 4)     # rounding only (phases grow with n)
     # whole pipeline, interior frames of the centred STFT
     y = O.mel_spectrogram(x, sample_rate=sr, n_fft=N, hop_length=hopw, n_mels=n_mels)
     fb = O.mel_filterbank(N // 2 + 1, 0.0, sr / 2, n_mels, sr)
