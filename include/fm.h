@@ -105,9 +105,8 @@ int fm_plan_create_args_host(fm_plan** out, const fm_args* args);
  * fm_plan_create -- build a plan on the CURRENT HIP device.
  *
  * Arguments are torchaudio MelSpectrogram's (README "Usage"):
- *   sample_rate > 0; n_fft 400 or a power of two from 64 to 4096 (others:
- *   FM_E_UNSUPPORTED; README "Usage" allows 400 and powers of two
- *   64..16384);
+ *   sample_rate > 0; n_fft 400 or a power of two from 64 to 16384 (others:
+ *   FM_E_UNSUPPORTED; README "Usage" allows exactly these);
  *   0 < win_length <= n_fft (a shorter window is zero-padded centred,
  *   flashmel/filters.py make_window); hop_length > 0;
  *   1 <= n_mels <= 256 (README "Usage");
@@ -190,7 +189,8 @@ int fm_forward(const fm_plan* plan, const void* in, int in_dtype,
  *   batch, length  as for fm_forward.
  *
  * Any hop: when more frames overlap one sample than one workgroup pass
- * holds, the workgroups take several passes.  FM_E_UNSUPPORTED only when the
+ * holds, the workgroups take several passes.  FM_E_UNSUPPORTED for n_fft
+ * 8192 and 16384 (no backward kernel is built for them), and when the
  * samples one workgroup owns (2 n_fft + 2 pad floats or so) do not fit its
  * LDS next to one frame's pass (a very large `pad`).  One kernel launch; no
  * allocation, no synchronisation.
@@ -231,7 +231,9 @@ typedef struct fm_plan_info {
   int threads;      /* threads per workgroup                                */
   int lds_bytes;    /* dynamic LDS per workgroup                            */
   int has_device;   /* 1 if the plan owns device tables                     */
-  int forward_variant; /* FM_FWD_SPLIT or FM_FWD_PAIRED (see below)         */
+  int forward_variant; /* FM_FWD_SPLIT, FM_FWD_PAIRED or FM_FWD_LARGE       */
+  int fft_n3;       /* FM_FWD_LARGE: n_fft/2 = fft_n1 * fft_n2 * fft_n3 (three
+                       passes); 0 otherwise                                  */
 } fm_plan_info;
 
 /* Forward kernel variants.  SPLIT: each frame's real FFT through a complex
@@ -239,12 +241,15 @@ typedef struct fm_plan_info {
  * workgroup.  PAIRED: two frames per complex FFT of n_fft points (the
  * pages' packing of two real frames into one complex transform, README "How
  * it works"), persistent workgroups that walk their frames in chunks and load
- * the next chunk while transforming the current one; built for n_fft = 400.
- * A plan takes PAIRED where it is built and fits, SPLIT otherwise; the
- * environment variable FM_FORWARD=split|paired, read at plan creation,
- * forces one (for A/B measurements).                                      */
+ * the next chunk while transforming the current one; built for n_fft = 400,
+ * taken only when the environment variable FM_FORWARD=paired is set at plan
+ * creation (measured slower than SPLIT; kept for A/B measurements).
+ * LARGE: n_fft 8192 and 16384, whose complex FFT of n_fft/2 points runs in
+ * three passes over one LDS buffer, one frame at a time per workgroup, with
+ * the mel projection over the CSR rows (these sizes have no backward).    */
 #define FM_FWD_SPLIT 0
 #define FM_FWD_PAIRED 1
+#define FM_FWD_LARGE 2
 
 int fm_plan_info_get(const fm_plan* plan, fm_plan_info* info);
 

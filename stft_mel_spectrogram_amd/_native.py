@@ -27,6 +27,7 @@ FM_I16 = 1
 FM_F16 = 2
 FM_FWD_SPLIT = 0
 FM_FWD_PAIRED = 1
+FM_FWD_LARGE = 2
 FM_NORMALIZED = {False: 0, None: 0, True: 1, "window": 1, "frame_length": 2}
 FM_OUT = {"f32": FM_F32, "f16": FM_F16}
 
@@ -43,7 +44,7 @@ class PlanInfo(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in (
         "n_fft", "win_length", "hop_length", "n_mels", "n_freqs", "pad", "normalized",
         "out_dtype", "nnz", "w_max", "fft_n1", "fft_n2", "tile_frames", "threads", "lds_bytes",
-        "has_device", "forward_variant")]
+        "has_device", "forward_variant", "fft_n3")]
 
 
 class Args(ctypes.Structure):

@@ -25,11 +25,12 @@ SOURCES = ["fm_api.cpp", "fm_plan.cpp", "fm_launch.hip"]
 
 
 def sources() -> list:
-    """Host/ABI sources plus one fm_shape_<n1>x<n2>.hip per built FFT shape and
-    one fm_pair_<r>x<r>.hip per paired-kernel shape."""
-    shapes = sorted(os.path.basename(f) for f in glob.glob(os.path.join(CSRC, "fm_shape_*.hip")))
-    pairs = sorted(os.path.basename(f) for f in glob.glob(os.path.join(CSRC, "fm_pair_*.hip")))
-    return SOURCES + shapes + pairs
+    """Host/ABI sources plus one fm_shape_<n1>x<n2>.hip per built FFT shape,
+    one fm_large_<a>x<c>x<d>.hip per large-FFT shape and one
+    fm_pair_<r>x<r>.hip per paired-kernel shape."""
+    def units(pattern):
+        return sorted(os.path.basename(f) for f in glob.glob(os.path.join(CSRC, pattern)))
+    return SOURCES + units("fm_shape_*.hip") + units("fm_large_*.hip") + units("fm_pair_*.hip")
 
 # Packed-FP32 VALU forms are switched off for all device code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

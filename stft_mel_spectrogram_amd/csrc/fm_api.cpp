@@ -148,6 +148,7 @@ int fm_plan_info_get(const fm_plan* plan, fm_plan_info* info) {
   info->w_max = p.w_max;
   info->fft_n1 = p.fft.n1;
   info->fft_n2 = p.fft.n2;
+  info->fft_n3 = p.fft.n3;
   const bool paired = p.fwd_variant == fm::kFwdPaired;
   info->tile_frames = paired ? p.pair_chunk : p.tile_max;
   info->threads = paired ? fm::kPairThreadsHost : p.threads;

@@ -112,6 +112,7 @@ constexpr int bwd_chunk_cap(int n1, int n2, int threads) {
 // Forward kernel variants.
 constexpr int kFwdSplit = 0;
 constexpr int kFwdPaired = 1;
+constexpr int kFwdLarge = 2;
 // Paired kernel: R x R complex points per frame pair (n_fft = R*R); shapes
 // built into the library.
 constexpr int pair_radix_for(int n_fft) { return n_fft == 400 ? 20 : 0; }
@@ -132,7 +133,16 @@ constexpr int threads_for(int n1, int n2) { return (n1 == 32 && n2 == 32) ? 512 
 // the real FFT (even samples as real part, odd samples as imaginary part).
 struct FftShape {
   int n1, n2;  // n_fft/2 = n1 * n2
+  int n3 = 0;  // three-pass shapes (the large-FFT kernel): n_fft/2 = n1 * n2 * n3
 };
+
+// Large-FFT kernel (fm_large.h): n_fft/2 = a * c * d complex points in three
+// register passes over one LDS buffer, c * d threads, one frame at a time.
+// LDS strides in complex values: d + 1 per c, an odd c (d + 1) + 1 per a.
+constexpr int large_threads(int c, int d) { return c * d; }
+constexpr int large_lds_bytes(int a, int c, int d) { return a * (c * (d + 1) + 1) * 8; }
+// Frames one large-kernel workgroup takes at most per launch.
+constexpr int kLargeTileMax = 1024;
 
 struct Plan {
   // transform arguments
@@ -176,9 +186,9 @@ struct Plan {
   const void* d_mel_tbl = nullptr;    // int32[8 + 4*n_blocks]: wave_beg, pad, blocks
   const void* d_blk_w = nullptr;      // float[blk_w.size()]
   // forward kernel variant: FM_FWD_SPLIT (fm_kernel.h: complex FFT of n_fft/2
-  // points and the real split, one tile per workgroup) or FM_FWD_PAIRED
-  // (fm_pair.h: two frames per complex FFT of n_fft points, persistent
-  // workgroups walking their frames in chunks)
+  // points and the real split, one tile per workgroup), FM_FWD_PAIRED
+  // (fm_pair.h: two frames per complex FFT of n_fft points) or FM_FWD_LARGE
+  // (fm_large.h: n_fft 8192 and 16384, three FFT passes, one frame at a time)
   int fwd_variant = 0;
   int pair_r = 0;              // paired: n_fft = pair_r * pair_r
   int pair_chunk = 0;          // paired: frames per chunk at most (even)
@@ -186,6 +196,7 @@ struct Plan {
   int pair_span_lds = 0;       //   byte offset of the sample span buffer
   int pair_w_lds = 0;          //   float offset of the mel weights
   int pair_wg_per_cu = 1;      // paired: resident workgroups per CU (device)
+  int large_wg_per_cu = 1;     // large-FFT kernel: resident workgroups per CU (device)
   // backward
   std::vector<BinTap> taps;      // [n_fft/2 + 1]
   int bwd_chunk_max = 0;         // frames per backward pass at most
@@ -234,6 +245,9 @@ void free_plan_device(Plan& p);
 // (paired kernel entry points, fm_pair_*.hip)
 template <int R>
 void* pair_kernel_for(int in_dtype, int pmode);
+// (large-FFT kernel entry points, fm_large_*.hip)
+template <int A, int C, int D>
+void* large_kernel_for(int in_dtype, int pmode);
 int launch_forward(const Plan& p, const void* in, int in_dtype, int64_t batch,
                    int64_t length, void* out, void* stream);
 int launch_backward(const Plan& p, const float* in, int64_t batch, int64_t length,

@@ -1,0 +1,6 @@
+// Large-FFT forward kernel, n_fft/2 = 16 x 16 x 32 (n_fft 16384).
+#include "fm_large.h"
+
+namespace fm {
+template void* large_kernel_for<16, 16, 32>(int, int);
+}  // namespace fm

@@ -8,6 +8,7 @@
 #include <vector>
 
 #include "fm_backward.h"
+#include "fm_large.h"
 #include "fm_pair.h"
 
 namespace fm {
@@ -43,6 +44,14 @@ void* select_kernel(const Plan& p, int in_dtype, bool copy) {
   return nullptr;
 }
 
+void* select_large_kernel(const Plan& p, int in_dtype) {
+  const int pm = power_mode(p);
+#define FM_SELECT_LARGE(A, C, D) \
+  if (p.fft.n1 == A && p.fft.n2 == C && p.fft.n3 == D) return large_kernel_for<A, C, D>(in_dtype, pm);
+  FM_FOR_EACH_LARGE_SHAPE(FM_SELECT_LARGE)
+#undef FM_SELECT_LARGE
+  return nullptr;
+}
 void* select_pair_kernel(const Plan& p, int in_dtype) {
   if (p.pair_r == 20) return pair_kernel_for<20>(in_dtype, power_mode(p));
   return nullptr;
@@ -111,6 +120,21 @@ int upload_plan(Plan& p) {
   p.d_mel_tbl = base + o_tbl;
   p.d_blk_w = base + o_bw;
   p.d_taps = base + o_taps;
+  // The large-FFT kernel: LDS opt-in and residency (no other kernel).
+  if (p.fwd_variant == kFwdLarge) {
+    for (int dt : {FM_F32, FM_I16}) {
+      void* k = select_large_kernel(p, dt);
+      if (!k) return set_error(FM_E_UNSUPPORTED, "no large-FFT kernel for this n_fft");
+      e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, p.lds_bytes);
+      if (e != hipSuccess) return hip_fail(e, "hipFuncSetAttribute (large)");
+    }
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, select_large_kernel(p, FM_F32), p.threads,
+                                                     p.lds_bytes) == hipSuccess)
+      p.large_wg_per_cu = std::max(1, n);
+    p.has_device = true;
+    return FM_OK;
+  }
   // Tiles above 64 KB of LDS need the per-kernel opt-in.
   for (int dt : {FM_F32, FM_I16}) {
     void* k = select_kernel(p, dt, use_tile_copy(p));
@@ -253,6 +277,47 @@ int launch_forward(const Plan& p, const void* in, int in_dtype, int64_t batch, i
     e = hipLaunchKernel(k, dim3(static_cast<unsigned>(grid)), dim3(kPairThreads), args,
                         static_cast<size_t>(p.pair_lds_bytes), static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "kernel launch (paired)");
+    return FM_OK;
+  }
+  if (p.fwd_variant == kFwdLarge) {
+    if (length > (1 << 29)) return set_error(FM_E_INVAL, "problem too large for one launch (length <= 2^29)");
+    // Frames per workgroup: the fewest that put every frame in the first
+    // round of resident workgroups (each walks its frames one at a time).
+    const int64_t slots = static_cast<int64_t>(p.n_cu > 0 ? p.n_cu : 256) * p.large_wg_per_cu;
+    int64_t g = p.tile_override > 0 ? p.tile_override : 1;
+    if (p.tile_override <= 0)
+      while (g < p.tile_max && batch * ((T + g - 1) / g) > slots) ++g;
+    const int64_t tiles = (T + g - 1) / g;
+    if (tiles * batch > INT32_MAX) return set_error(FM_E_INVAL, "problem too large for one launch");
+    LArgs a;
+    a.in = in;
+    a.out = out;
+    a.win2 = static_cast<const float2*>(p.d_win2);
+    a.tw_m = static_cast<const float2*>(p.d_tw_m);
+    a.tw_n = static_cast<const float2*>(p.d_tw_n);
+    a.rows = static_cast<const MelRow*>(p.d_rows);
+    a.mel_w = static_cast<const float*>(p.d_mel_w);
+    a.length = length;
+    a.n_frames = static_cast<int>(T);
+    a.hop = p.hop;
+    a.pad = p.pad_left + p.zpad;
+    a.zpad = p.zpad;
+    a.n_mels = p.n_mels;
+    a.tile = static_cast<int>(g);
+    a.tiles_per_signal = static_cast<int>(tiles);
+    a.pad_mode = p.pad_mode;
+    a.half_power = static_cast<float>(p.power * 0.5);
+    const size_t esz = (in_dtype == FM_I16) ? 2 : 4;
+    const uintptr_t ia = reinterpret_cast<uintptr_t>(in);
+    a.vec_ok = (ia % (2 * esz) == 0) && (length % 2 == 0) && (p.hop % 2 == 0) &&
+               ((p.pad_left + p.zpad) % 2 == 0);
+    a.out_f16 = p.out_dtype == FM_F16 ? 1 : 0;
+    void* k = select_large_kernel(p, in_dtype);
+    if (!k) return set_error(FM_E_UNSUPPORTED, "no large-FFT kernel for this n_fft");
+    void* args[] = {&a};
+    e = hipLaunchKernel(k, dim3(static_cast<unsigned>(tiles * batch)), dim3(p.threads), args,
+                        static_cast<size_t>(p.lds_bytes), static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "kernel launch (large)");
     return FM_OK;
   }
   const int G = choose_tile(p, batch, T);

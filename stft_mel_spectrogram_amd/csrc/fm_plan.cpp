@@ -78,6 +78,9 @@ bool fft_shape_for(int n_fft, FftShape* s) {
     case 1024: *s = {32, 16}; return true;  // 512 = 32 * 16 (radix 4*8, 4*4)
     case 2048: *s = {32, 32}; return true;  // 1024 = 32 * 32
     case 4096: *s = {64, 32}; return true;  // 2048 = 64 * 32 (radix 8*8, 4*8)
+    // three passes (the large-FFT kernel)
+    case 8192: *s = {16, 16, 16}; return true;   // 4096 = 16 * 16 * 16
+    case 16384: *s = {16, 16, 32}; return true;  // 8192 = 16 * 16 * 32
     default: return false;
   }
 }
@@ -224,7 +227,7 @@ int build_host_plan(Plan& p, const fm_args& a) {
   if (n_mels > 256) return set_error(FM_E_UNSUPPORTED, fmt("n_mels > 256 is not supported", n_mels));
   FftShape fs;
   if (!fft_shape_for(n_fft, &fs))
-    return set_error(FM_E_UNSUPPORTED, fmt("n_fft not built (supported: 400 and powers of two 64..4096)", n_fft));
+    return set_error(FM_E_UNSUPPORTED, fmt("n_fft not built (supported: 400 and powers of two 64..16384)", n_fft));
 
   p.sample_rate = sample_rate; p.n_fft = n_fft; p.win_length = win_length;
   p.hop = hop_length; p.n_mels = n_mels; p.f_min = f_min; p.f_max = f_max;
@@ -234,7 +237,7 @@ int build_host_plan(Plan& p, const fm_args& a) {
   p.n_freqs = n_fft / 2 + 1;
   p.pad_left = center ? n_fft / 2 : 0;
   p.fft = fs;
-  p.threads = threads_for(fs.n1, fs.n2);
+  p.threads = fs.n3 ? large_threads(fs.n2, fs.n3) : threads_for(fs.n1, fs.n2);
   const int M = n_fft / 2;
 
   // ---- window: periodic Hann of win_length, centred in n_fft, with the
@@ -399,6 +402,21 @@ int build_host_plan(Plan& p, const fm_args& a) {
     static_assert(kMelStepGroup * 64 % 256 == 0, "blocks must fill whole copy chunks");
   }
   // ---- tile geometry -------------------------------------------------------
+  if (fs.n3) {
+    // The large-FFT kernel holds one frame's exchange buffer and walks its
+    // tile frame by frame; it has no backward kernel.
+    p.tile_max = kLargeTileMax;
+    p.lds_bytes = large_lds_bytes(fs.n1, fs.n2, fs.n3);
+    p.bwd_chunk_max = 0;
+    p.fwd_variant = kFwdLarge;
+    p.tile_override = 0;
+    p.bwd_chunk_override = 0;
+    if (const char* e = std::getenv("FM_TILE_FRAMES")) {
+      int v = std::atoi(e);
+      if (v >= 1 && v <= p.tile_max) p.tile_override = v;
+    }
+    return FM_OK;
+  }
   // At most 64 frames per workgroup tile (four 16-frame column groups of
   // the mel stage's matrix products); the second FFT pass gives each thread
   // one pair of n2-point transforms; the tile's LDS (the exchange buffer, or

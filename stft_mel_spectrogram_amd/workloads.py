@@ -55,6 +55,15 @@ WORKLOADS = {
     "fft64": dict(batch=8, length=480000, dtype="f32", signal="noise", sigma=0.1, seed=10,
                   sample_rate=16000, n_fft=64, win_length=64, hop_length=16,
                   n_mels=24, f_min=0.0, f_max=8000.0, power=2.0),
+    # the pages' "huge" case (16384/4096, 256 mels, 44.1 kHz, batch 16; 10 s
+    # signals, the length its input + output bytes and time imply), and the
+    # same shape at n_fft 8192
+    "huge": dict(batch=16, length=441000, dtype="f32", signal="chirp", sigma=0.1, seed=11,
+                 sample_rate=44100, n_fft=16384, win_length=16384, hop_length=4096,
+                 n_mels=256, f_min=0.0, f_max=22050.0, power=2.0),
+    "fft8192": dict(batch=16, length=441000, dtype="f32", signal="chirp", sigma=0.1, seed=12,
+                    sample_rate=44100, n_fft=8192, win_length=8192, hop_length=2048,
+                    n_mels=256, f_min=0.0, f_max=22050.0, power=2.0),
 }
 
 # The arguments that define the transform (everything but the input recipe).

@@ -45,7 +45,7 @@ static void inspect(fm_plan* h) {
 }
 
 int main() {
-  const int n_ffts[] = {64, 128, 256, 400, 512, 1024, 2048, 4096};
+  const int n_ffts[] = {64, 128, 256, 400, 512, 1024, 2048, 4096, 8192, 16384};
   int made = 0, rejected = 0;
   for (int n_fft : n_ffts) {
     for (int wdiv : {1, 2}) {

@@ -236,7 +236,7 @@ def test_mel_block_reads_stay_in_written_or_zeroed_floats(n_fft):
         assert worst > 0          # this shape does read past its rows (few mels, f_max = sr/2)
 
 
-@pytest.mark.parametrize("n_fft", [64, 128, 256, 400, 512, 1024, 2048, 4096])
+@pytest.mark.parametrize("n_fft", [64, 128, 256, 400, 512, 1024, 2048, 4096, 8192, 16384])
 def test_twiddles(n_fft):
     p = N.Plan(device=False, sample_rate=16000, n_fft=n_fft, hop_length=n_fft // 4, n_mels=40)
     t = p.tables()
@@ -245,13 +245,13 @@ def test_twiddles(n_fft):
     np.testing.assert_allclose(t["tw_m"], np.exp(-2j * np.pi * j / M), rtol=0, atol=6e-8)
     np.testing.assert_allclose(t["tw_n"], np.exp(-2j * np.pi * j / n_fft), rtol=0, atol=6e-8)
     inf = p.info()
-    assert inf.fft_n1 * inf.fft_n2 == M
+    assert inf.fft_n1 * inf.fft_n2 * (inf.fft_n3 or 1) == M
 
 
 @pytest.mark.parametrize("L", [201, 202, 1000, 16000, 480000, 220500])
 def test_out_frames_closed_form(L):
     for n_fft, hop in ((64, 16), (256, 64), (400, 160), (512, 100), (1024, 256), (2048, 512),
-                       (4096, 1024)):
+                       (4096, 1024), (8192, 2048), (16384, 4096)):
         if L <= n_fft // 2:
             continue
         p = N.Plan(device=False, n_fft=n_fft, hop_length=hop, n_mels=40)
@@ -274,8 +274,34 @@ def test_geometry_fits_the_hardware():
         assert inf.has_device == 0
 
 
+@pytest.mark.parametrize("n_fft,shape", [(8192, (16, 16, 16)), (16384, (16, 16, 32))])
+def test_large_fft_geometry(n_fft, shape):
+    """n_fft 8192 and 16384 take the three-pass kernel: n_fft/2 = a*c*d
+    complex points, c*d threads (one pass-1 DFT each), one frame's exchange
+    buffer (strides d+1 per c and c(d+1)+1 per a, complex) in LDS, which
+    also holds the frame's power row."""
+    for n_mels in (1, 128, 256):
+        p = N.Plan(device=False, sample_rate=44100, n_fft=n_fft, hop_length=n_fft // 4,
+                   n_mels=n_mels, f_max=22050.0)
+        inf = p.info()
+        a, c, d = shape
+        assert (inf.fft_n1, inf.fft_n2, inf.fft_n3) == shape and a * c * d == n_fft // 2
+        assert inf.forward_variant == N.FM_FWD_LARGE
+        assert inf.threads == c * d and inf.threads % 64 == 0 and inf.threads <= 1024
+        assert inf.lds_bytes == a * (c * (d + 1) + 1) * 8 <= 160 * 1024
+        assert inf.lds_bytes >= 4 * (n_fft // 2 + 1)          # the power row fits
+        assert n_mels <= inf.threads                          # one thread per filter
+        # the largest position the passes touch is inside the buffer
+        assert ((a - 1) * (c * (d + 1) + 1) + (c - 1) * (d + 1) + d - 1) * 8 < inf.lds_bytes
+    # every bin position (ka, kc, kd) maps to a distinct buffer slot
+    pos = {(ka * (c * (d + 1) + 1) + kc * (d + 1) + kd) for ka in range(a) for kc in range(c)
+           for kd in range(d)}
+    assert len(pos) == n_fft // 2
+
+
 BAD = [
-    (dict(n_fft=8192, hop_length=2048, f_max=8000.0), N.FM_E_UNSUPPORTED),
+    (dict(n_fft=32768, hop_length=8192, f_max=8000.0), N.FM_E_UNSUPPORTED),
+    (dict(n_fft=2000, hop_length=500), N.FM_E_UNSUPPORTED),
     (dict(n_fft=300), N.FM_E_UNSUPPORTED),
     (dict(n_mels=257), N.FM_E_UNSUPPORTED),
     (dict(f_min=8000.0, f_max=8000.0), N.FM_E_INVAL),
