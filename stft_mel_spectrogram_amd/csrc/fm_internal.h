@@ -138,9 +138,13 @@ struct FftShape {
 
 // Large-FFT kernel (fm_large.h): n_fft/2 = a * c * d complex points in three
 // register passes over one LDS buffer, c * d threads, one frame at a time.
-// LDS strides in complex values: d + 1 per c, an odd c (d + 1) + 1 per a.
+// LDS strides in complex values: d + 1 per c, an odd c (d + 1) + 1 per a;
+// the CSR mel weights (nnz floats, in 16-byte pieces) follow the buffer.
 constexpr int large_threads(int c, int d) { return c * d; }
-constexpr int large_lds_bytes(int a, int c, int d) { return a * (c * (d + 1) + 1) * 8; }
+constexpr int large_exchange_bytes(int a, int c, int d) { return a * (c * (d + 1) + 1) * 8; }
+constexpr int large_lds_bytes(int a, int c, int d, int nnz) {
+  return large_exchange_bytes(a, c, d) + (nnz + 3) / 4 * 16;
+}
 // Frames one large-kernel workgroup takes at most per launch.
 constexpr int kLargeTileMax = 1024;
 

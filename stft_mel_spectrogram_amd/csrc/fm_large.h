@@ -22,7 +22,8 @@
 // then per bin k the real split X[k] = (Z[k] + conj Z[M-k])
 // - i W_N^k (Z[k] - conj Z[M-k]) and |X|^p into a power row (aliasing the
 // buffer), and the mel projection of that row, one thread per filter over
-// its CSR run of nonzero weights.  Each pass writes back the positions it
+// its CSR run of nonzero weights (copied into LDS behind the buffer once per
+// workgroup).  Each pass writes back the positions it
 // read, so one buffer serves all three; its strides (D + 1 per c, an odd
 // C (D + 1) + 1 per a) keep every pass and the split's reads of consecutive
 // bins free of LDS bank conflicts.
@@ -53,6 +54,8 @@ struct LArgs {
   float half_power;      // power / 2
   int vec_ok;            // interior frames may use paired (2-sample) loads
   int out_f16;           // 1: the output is float16
+  int w16;               // mel weights in 16-byte pieces (nnz rounded up to 4 floats)
+  int w_lds;             // LDS byte offset of the weights (after the exchange buffer)
 };
 
 // LDS strides of the exchange buffer (in complex values).
@@ -65,6 +68,25 @@ template <int A, int C, int D>
 constexpr int kLargeThreads = C * D;
 
 namespace {
+
+// The A sample pairs z[B q + b] (q < A) of the frame starting at `base`
+// (relative to x[0]) for pass-1 thread b: paired loads inside the signal,
+// the padding index map at its edges.
+template <int A, int B, typename InT>
+__device__ __forceinline__ void large_frame_samples(float2 (&v)[A], const InT* x, int base, int L,
+                                                    int b, int vec_ok, int zpad, int pad_mode) {
+  if (vec_ok && base >= 0 && base + 2 * A * B <= L) {
+#pragma unroll
+    for (int q = 0; q < A; ++q) v[q] = load_pair_raw(x, base + 2 * (B * q + b));
+  } else {
+#pragma unroll
+    for (int q = 0; q < A; ++q) {
+      const int i = base + 2 * (B * q + b);
+      v[q] = make_float2(padded_sample_raw(x, i, L, zpad, pad_mode),
+                         padded_sample_raw(x, i + 1, L, zpad, pad_mode));
+    }
+  }
+}
 
 template <int A, int C, int D, typename InT, int PMODE>
 __global__ __launch_bounds__((kLargeThreads<A, C, D>), 2) void mel_forward_large_kernel(LArgs a) {
@@ -89,9 +111,38 @@ __global__ __launch_bounds__((kLargeThreads<A, C, D>), 2) void mel_forward_large
   const int nvalid = min(G, a.n_frames - t0);
   const InT* x = static_cast<const InT*>(a.in) + static_cast<long long>(sig) * L;
   const long long obase = (static_cast<long long>(sig) * a.n_mels) * a.n_frames + t0;
+  const float* WL = reinterpret_cast<const float*>(lds + a.w_lds);  // mel weights in LDS
 
-  // pass-1 role: b = tid = D*c1 + d1
-  const int c1 = tid / D, d1 = tid - (tid / D) * D;
+  // The mel weights go to LDS once (direct global -> LDS loads, 16 bytes
+  // per lane), landing while the first frame loads and transforms.
+  {
+    const int wave = tid >> 6, lane = tid & 63;
+    for (int c = wave; c * 64 < a.w16; c += NT / 64) {
+      const int q = c * 64 + lane;
+      if (q < a.w16)
+        __builtin_amdgcn_global_load_lds(a.mel_w + 4 * q, lds + a.w_lds + c * 1024, 16, 0, 0);
+    }
+  }
+
+  // Each thread keeps its pass-1 window values and twiddles W_M^(b ka) and
+  // its pass-2 twiddles W_M^(A d kc) in registers for the whole tile.  Where
+  // the registers allow (D <= 16; the 32-point third pass of the other shape
+  // needs them), frame f + 1's samples load while frame f is transformed.
+  constexpr bool kPrefetch = D <= 16;
+  constexpr bool kOneP2 = (A * D == NT);  // one pass-2 item per thread
+  const int c1 = tid / D, d1 = tid - (tid / D) * D;  // pass-1 role: b = tid = D*c1 + d1
+  float2 win[A], tw1[A];
+  float2 tw2[kOneP2 ? C : 1];
+#pragma unroll
+  for (int q = 0; q < A; ++q) {
+    const float2 w = a.win2[B * q + tid];
+    win[q] = make_float2(w.x * kSampleScale<InT>, w.y * kSampleScale<InT>);
+    tw1[q] = a.tw_m[tid * q];
+  }
+  if constexpr (kOneP2) {
+#pragma unroll
+    for (int kc = 0; kc < C; ++kc) tw2[kc] = a.tw_m[A * d1 * kc];
+  }
   // this thread's filter (the mel stage), read once
   MelRow row{0, 0, 0, 0};
   if (tid < a.n_mels) row = a.rows[tid];
@@ -101,33 +152,31 @@ __global__ __launch_bounds__((kLargeThreads<A, C, D>), 2) void mel_forward_large
   CFloat* twn_s = (CFloat*)(a.tw_n);
   const float hp = a.half_power;
 
+  float2 nxt[kPrefetch ? A : 1];
+  if constexpr (kPrefetch)
+    large_frame_samples<A, B>(nxt, x, t0 * a.hop - a.pad, L, tid, a.vec_ok, a.zpad, a.pad_mode);
+
   for (int f = 0; f < nvalid; ++f) {
     // ---- pass 1: samples, window, A-point DFTs, twiddles ------------------
     {
       float2 v[A];
-      const int base = (t0 + f) * a.hop - a.pad;
-      if (a.vec_ok && base >= 0 && base + 2 * M <= L) {
+      if constexpr (kPrefetch) {
 #pragma unroll
-        for (int q = 0; q < A; ++q) v[q] = load_pair_raw(x, base + 2 * (B * q + tid));
+        for (int q = 0; q < A; ++q) v[q] = nxt[q];
+        if (f + 1 < nvalid)
+          large_frame_samples<A, B>(nxt, x, (t0 + f + 1) * a.hop - a.pad, L, tid, a.vec_ok, a.zpad,
+                                    a.pad_mode);
       } else {
-#pragma unroll
-        for (int q = 0; q < A; ++q) {
-          const int i = base + 2 * (B * q + tid);
-          v[q] = make_float2(padded_sample_raw(x, i, L, a.zpad, a.pad_mode),
-                             padded_sample_raw(x, i + 1, L, a.zpad, a.pad_mode));
-        }
+        large_frame_samples<A, B>(v, x, (t0 + f) * a.hop - a.pad, L, tid, a.vec_ok, a.zpad,
+                                  a.pad_mode);
       }
 #pragma unroll
-      for (int q = 0; q < A; ++q) {
-        float2 w = a.win2[B * q + tid];
-        w = make_float2(w.x * kSampleScale<InT>, w.y * kSampleScale<InT>);
-        v[q] = make_float2(v[q].x * w.x, v[q].y * w.y);
-      }
+      for (int q = 0; q < A; ++q) v[q] = make_float2(v[q].x * win[q].x, v[q].y * win[q].y);
       Dft<A>::run(v);
       float2* yp = Y + RC * c1 + d1;
       yp[0] = v[0];
 #pragma unroll
-      for (int ka = 1; ka < A; ++ka) yp[RA * ka] = cmul(v[ka], a.tw_m[tid * ka]);
+      for (int ka = 1; ka < A; ++ka) yp[RA * ka] = cmul(v[ka], tw1[ka]);
     }
     __syncthreads();
     // ---- pass 2: C-point DFTs over c, twiddles W_B^(d kc) = W_M^(A d kc) ---
@@ -140,7 +189,8 @@ __global__ __launch_bounds__((kLargeThreads<A, C, D>), 2) void mel_forward_large
       Dft<C>::run(u);
       yp[0] = u[0];
 #pragma unroll
-      for (int kc = 1; kc < C; ++kc) yp[RC * kc] = cmul(u[kc], a.tw_m[A * d * kc]);
+      for (int kc = 1; kc < C; ++kc)
+        yp[RC * kc] = cmul(u[kc], kOneP2 ? tw2[kOneP2 ? kc : 0] : a.tw_m[A * d * kc]);
     }
     __syncthreads();
     // ---- pass 3: D-point DFTs over d -------------------------------------
@@ -180,11 +230,12 @@ __global__ __launch_bounds__((kLargeThreads<A, C, D>), 2) void mel_forward_large
 #pragma unroll
     for (int j = 0; j < KPT; ++j) P[tid + NT * j] = pw[j];
     if (tid == 0) P[M] = p_nyq;
+    if (f == 0) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the weight copies have landed
     __syncthreads();
     // ---- mel projection: thread m over its CSR run ------------------------
     if (tid < a.n_mels) {
       const float* pr = P + row.first;
-      const float* wr = a.mel_w + row.off;
+      const float* wr = WL + row.off;
       float acc = 0.0f;
       for (int j = 0; j < row.len; ++j) acc = fmaf(pr[j], wr[j], acc);
       const long long o = obase + static_cast<long long>(tid) * a.n_frames + f;

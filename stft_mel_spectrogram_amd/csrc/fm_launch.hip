@@ -312,6 +312,8 @@ int launch_forward(const Plan& p, const void* in, int in_dtype, int64_t batch, i
     a.vec_ok = (ia % (2 * esz) == 0) && (length % 2 == 0) && (p.hop % 2 == 0) &&
                ((p.pad_left + p.zpad) % 2 == 0);
     a.out_f16 = p.out_dtype == FM_F16 ? 1 : 0;
+    a.w16 = (p.nnz + 3) / 4;
+    a.w_lds = large_exchange_bytes(p.fft.n1, p.fft.n2, p.fft.n3);
     void* k = select_large_kernel(p, in_dtype);
     if (!k) return set_error(FM_E_UNSUPPORTED, "no large-FFT kernel for this n_fft");
     void* args[] = {&a};

@@ -406,7 +406,9 @@ int build_host_plan(Plan& p, const fm_args& a) {
     // The large-FFT kernel holds one frame's exchange buffer and walks its
     // tile frame by frame; it has no backward kernel.
     p.tile_max = kLargeTileMax;
-    p.lds_bytes = large_lds_bytes(fs.n1, fs.n2, fs.n3);
+    p.lds_bytes = large_lds_bytes(fs.n1, fs.n2, fs.n3, p.nnz);
+    if (p.lds_bytes > 160 * 1024)
+      return set_error(FM_E_UNSUPPORTED, "mel filterbank too large for the LDS of one workgroup");
     p.bwd_chunk_max = 0;
     p.fwd_variant = kFwdLarge;
     p.tile_override = 0;

@@ -288,11 +288,12 @@ def test_large_fft_geometry(n_fft, shape):
         assert (inf.fft_n1, inf.fft_n2, inf.fft_n3) == shape and a * c * d == n_fft // 2
         assert inf.forward_variant == N.FM_FWD_LARGE
         assert inf.threads == c * d and inf.threads % 64 == 0 and inf.threads <= 1024
-        assert inf.lds_bytes == a * (c * (d + 1) + 1) * 8 <= 160 * 1024
-        assert inf.lds_bytes >= 4 * (n_fft // 2 + 1)          # the power row fits
+        ybytes = a * (c * (d + 1) + 1) * 8                   # exchange buffer (complex)
+        assert inf.lds_bytes == ybytes + 16 * (-(-inf.nnz // 4)) <= 160 * 1024   # + CSR weights
+        assert ybytes >= 4 * (n_fft // 2 + 1)                 # the power row fits the buffer
         assert n_mels <= inf.threads                          # one thread per filter
         # the largest position the passes touch is inside the buffer
-        assert ((a - 1) * (c * (d + 1) + 1) + (c - 1) * (d + 1) + d - 1) * 8 < inf.lds_bytes
+        assert ((a - 1) * (c * (d + 1) + 1) + (c - 1) * (d + 1) + d - 1) * 8 < ybytes
     # every bin position (ka, kc, kd) maps to a distinct buffer slot
     pos = {(ka * (c * (d + 1) + 1) + kc * (d + 1) + kd) for ka in range(a) for kc in range(c)
            for kd in range(d)}
