@@ -221,10 +221,16 @@ void default_args(fm_args* a);
 // pass 1 followed by the pass-1 tables where tables_in_lds), which later
 // holds the power tile, its zeroed overrun floats, (from float
 // tile_weights_offset) the mel block weights and, for wide tiles, the 4
-// waves' output staging areas right after them.
+// waves' output staging areas right after them; behind all of that (byte
+// tile_twiddles_offset), where twiddles_in_lds, the split twiddles W_N^k,
+// k < n_fft/2.
 int tile_exchange_bytes(const Plan& p, int frames);
 int tile_weights_offset(const Plan& p, int frames);
 int tile_tables_offset(const Plan& p, int frames);  // bytes; pass-1 tables in LDS
+// Split twiddles W_N^k copied into LDS (complex FFTs of 1024 points or more;
+// smaller ones hold them in registers or read them from L2).
+constexpr bool twiddles_in_lds(int m) { return m >= 1024; }
+int tile_twiddles_offset(const Plan& p, int frames);  // bytes; split twiddles in LDS
 int tile_lds_bytes(const Plan& p, int frames);
 
 // LDS layout of a backward pass of `chunk` frames (floats from the start):

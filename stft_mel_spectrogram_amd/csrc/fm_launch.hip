@@ -355,6 +355,7 @@ int launch_forward(const Plan& p, const void* in, int in_dtype, int64_t batch, i
   a.w_lds = tile_weights_offset(p, G);
   a.out_f16 = p.out_dtype == FM_F16 ? 1 : 0;
   a.tab_lds = tile_tables_offset(p, G);
+  a.twn_lds = tile_twiddles_offset(p, G);
 
   void* k = select_kernel(p, in_dtype, use_tile_copy(p));
   if (!k) return set_error(FM_E_UNSUPPORTED, "no kernel for this n_fft");

@@ -108,13 +108,18 @@ int tile_weights_offset(const Plan& p, int frames) {
 
 int tile_tables_offset(const Plan& p, int frames) { return tile_exchange_bytes(p, frames); }
 
-int tile_lds_bytes(const Plan& p, int frames) {
+int tile_twiddles_offset(const Plan& p, int frames) {
   const long tables = tables_in_lds(p.fft.n1, p.n_fft / 2) ? 16L * (p.n_fft / 2) : 0;
   const long pass1 = tile_tables_offset(p, frames) + tables;
   const long stage = frames >= kMelStageMinFrames ? kMelWaves * kMelStageFloats : 0;
   const long weights = p.w_in_lds ? static_cast<long>(p.blk_w.size()) : 0;
   const long after_fft = (static_cast<long>(tile_weights_offset(p, frames)) + weights + stage) * 4;
-  return static_cast<int>(std::max<long>(pass1, after_fft));
+  return static_cast<int>((std::max<long>(pass1, after_fft) + 15) / 16 * 16);
+}
+
+int tile_lds_bytes(const Plan& p, int frames) {
+  const long twiddles = twiddles_in_lds(p.n_fft / 2) ? 8L * (p.n_fft / 2) : 0;
+  return static_cast<int>(tile_twiddles_offset(p, frames) + twiddles);
 }
 
 int pair_lds_layout(int r, int chunk, int n_mels, long w_floats, int* span_b, int* w_f) {
