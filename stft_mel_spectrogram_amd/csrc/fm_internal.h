@@ -65,16 +65,19 @@ constexpr int kMelStageMinFrames = 33;
 // Staging floats per wave: 16 filters x (64 frames + 1 pad).
 constexpr int kMelStageFloats = 16 * 65;
 
-// LDS frame strides of a tile, padded against bank conflicts: the exchange
-// buffer Y holds each frame's n_fft/2 complex values at a stride of
-// n_fft/2 + kExchangePad, the power tile P each frame's n_fft/2 + 1 bins at
-// a stride of n_fft/2 + 1 + kPowerPad (the pad floats are kept at zero).
-// A pad of 4 complex values keeps rows 16-byte aligned (paired 64-bit LDS
-// accesses) and spreads the frames of a wave over the 64 banks; the odd
-// power-tile stride needs none.
+// LDS strides of a tile, padded against bank conflicts.  The exchange
+// buffer Y holds a frame's n1 rows of n2 complex values (row k1 written by
+// the first pass, read whole by one second-pass thread).  A frame's second-
+// pass threads read their rows in step, so rows of an even length would put
+// them on the same banks (n2 = 32: 64 floats apart, 16 threads on one bank);
+// even rows are therefore padded to n2 + 1 complex values.  Frames follow at
+// a stride of n1 * row + kExchangePad (a pad of 4 complex values spreads the
+// frames of a wave over the 64 banks).  The power tile P holds each frame's
+// n_fft/2 + 1 bins at a stride of n_fft/2 + 1 + kPowerPad (odd: no pad).
 constexpr int kExchangePad = 4;
 constexpr int kPowerPad = 0;
-constexpr int exchange_stride(int half) { return half + kExchangePad; }
+constexpr int exchange_row(int n2) { return n2 % 2 == 0 ? n2 + 1 : n2; }
+constexpr int exchange_stride(int n1, int n2) { return n1 * exchange_row(n2) + kExchangePad; }
 // The backward's exchange buffer (its second pass walks single rows).
 constexpr int kBwdExchangePad = 4;
 constexpr int bwd_exchange_stride(int half) { return half + kBwdExchangePad; }

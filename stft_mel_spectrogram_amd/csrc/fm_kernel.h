@@ -18,7 +18,8 @@
 //              X[k] = (Z[k] + conj Z[M-k]) - i W_N^k (Z[k] - conj Z[M-k])
 //           (window pre-scaled by 1/2) and |X|^p need no further exchange.
 // The power tile P[f][k] (odd frame stride n_fft/2+1) reuses the exchange
-// buffer (frame stride n_fft/2 + 4 complex values).  The mel projection is
+// buffer (rows of N2 complex values, padded to N2 + 1 where N2 is even;
+// frames 4 complex values apart beyond their rows).  The mel projection is
 // a block-sparse product on the matrix cores: 16 filters x 16 frames per
 // v_mfma_f32_16x16x4f32, over only the bins each block of filters touches.
 #pragma once
@@ -284,7 +285,8 @@ template <int N1, int N2, typename InT, int PMODE, bool COPY>
 __global__ __launch_bounds__((kThreads<N1, N2>), (kMinWavesPerSimd<N1, N2>)) void mel_forward_kernel(KArgs a) {
   constexpr int M = N1 * N2;
   constexpr int K = M + 1;        // one-sided bins
-  constexpr int SY = exchange_stride(M);  // LDS frame strides (padded)
+  constexpr int RS = exchange_row(N2);         // LDS row and frame strides (padded)
+  constexpr int SY = exchange_stride(N1, N2);
   constexpr int SP = power_stride(M);
   constexpr int NF = 2 * M;       // n_fft
   constexpr int NPAIR = N1 / 2;   // pass-2 threads per frame
@@ -390,7 +392,7 @@ __global__ __launch_bounds__((kThreads<N1, N2>), (kMinWavesPerSimd<N1, N2>)) voi
         yrow[0] = v[0];
 #pragma unroll
         for (int k1 = 1; k1 < N1; ++k1)
-          yrow[k1 * N2] = cmul(v[k1], kHoist ? twv[kHoist ? k1 : 0]
+          yrow[k1 * RS] = cmul(v[k1], kHoist ? twv[kHoist ? k1 : 0]
                                              : (kTabLds ? tab_tw[n2 * k1] : a.tw_m[n2 * k1]));
       };
       if constexpr (kHoist) {
@@ -497,8 +499,8 @@ __global__ __launch_bounds__((kThreads<N1, N2>), (kMinWavesPerSimd<N1, N2>)) voi
       }
       const int ka = p;
       const int kb = (p == 0) ? N1 / 2 : N1 - p;
-      const float2* ra = Y + f2 * SY + ka * N2;
-      const float2* rb = Y + f2 * SY + kb * N2;
+      const float2* ra = Y + f2 * SY + ka * RS;
+      const float2* rb = Y + f2 * SY + kb * RS;
 #pragma unroll
       for (int j = 0; j < N2; ++j) {
         za[j] = ra[j];

@@ -95,7 +95,7 @@ std::string fmt(const char* what, double v) {
 
 int tile_exchange_bytes(const Plan& p, int frames) {
   // complex exchange buffer Y[frames][exchange_stride]
-  const long y = static_cast<long>(std::max(frames, 1)) * exchange_stride(p.n_fft / 2) * 8;
+  const long y = static_cast<long>(std::max(frames, 1)) * exchange_stride(p.fft.n1, p.fft.n2) * 8;
   return static_cast<int>((y + 15) / 16 * 16);
 }
 
