@@ -178,6 +178,9 @@ struct Plan {
   std::vector<MelRow> rows;   // [n_mels]
   std::vector<float> mel_w;   // [nnz]
   std::vector<float> tw_m;    // [2*M] exp(-2 pi i j / M), M = n_fft/2
+  std::vector<float> tw_p;    // [2*M] first-pass twiddles in the order the pass reads
+                              // them: entry k1*n2 + j = tw_m entry (j*k1) mod M
+                              // (two-pass shapes; zero for the three-pass ones)
   std::vector<float> tw_n;    // [2*M] exp(-2 pi i k / n_fft)
   // device
   bool has_device = false;
@@ -186,6 +189,7 @@ struct Plan {
   std::vector<int> wg_per_cu;  // [tile frames] resident workgroups per CU
   void* d_block = nullptr;     // one allocation holding every table
   const void* d_win2 = nullptr;   // float2[M] : 0.5*(w[2m], w[2m+1])
+  const void* d_tw_p = nullptr;   // float2[M] (right behind d_win2)
   const void* d_tw_m = nullptr;   // float2[M]
   const void* d_tw_n = nullptr;   // float2[M]
   const void* d_rows = nullptr;   // MelRow[n_mels]

@@ -39,7 +39,9 @@ struct KArgs {
   const void* in;
   void* out;            // [B, n_mels, n_frames] float or _Float16
   const float2* win2;   // [M]  0.5*(w[2m], w[2m+1])
-  const float2* tw_m;   // [M]  exp(-2 pi i j / M)
+  const float2* tw_m;   // [M]  first-pass twiddles exp(-2 pi i n2 k1 / M),
+                        //      entry k1*N2 + n2 (consecutive threads, consecutive
+                        //      entries)
   const float2* tw_n;   // [M]  exp(-2 pi i k / N)
   long long length;     // samples per signal
   int n_frames;         // frames per signal
@@ -301,6 +303,7 @@ __global__ __launch_bounds__((kThreads<N1, N2>), (kMinWavesPerSimd<N1, N2>)) voi
   float2* Y = reinterpret_cast<float2*>(lds);  // Y[f][k1][n2]
   float* P = reinterpret_cast<float*>(lds);    // P[f][k], aliases Y
   // pass-1 tables copied behind Y (kTabLds): window pairs, then twiddles
+  // (both in the order of KArgs)
   const float2* tab_win = reinterpret_cast<const float2*>(lds + a.tab_lds);
   const float2* tab_tw = tab_win + M;
 
@@ -358,7 +361,7 @@ __global__ __launch_bounds__((kThreads<N1, N2>), (kMinWavesPerSimd<N1, N2>)) voi
         }
         twv[0] = make_float2(1.0f, 0.0f);
 #pragma unroll
-        for (int k1 = 1; k1 < N1; ++k1) twv[k1] = a.tw_m[n2 * k1];
+        for (int k1 = 1; k1 < N1; ++k1) twv[k1] = a.tw_m[N2 * k1 + n2];
       }
       auto fetch = [&](int f, float2 (&s)[N1]) {
         const int base = (t0 + f) * a.hop - a.pad;
@@ -393,7 +396,7 @@ __global__ __launch_bounds__((kThreads<N1, N2>), (kMinWavesPerSimd<N1, N2>)) voi
 #pragma unroll
         for (int k1 = 1; k1 < N1; ++k1)
           yrow[k1 * RS] = cmul(v[k1], kHoist ? twv[kHoist ? k1 : 0]
-                                             : (kTabLds ? tab_tw[n2 * k1] : a.tw_m[n2 * k1]));
+                                             : (kTabLds ? tab_tw[N2 * k1 + n2] : a.tw_m[N2 * k1 + n2]));
       };
       if constexpr (kHoist) {
         // Every frame of this thread is loaded before any is computed.  A

@@ -74,7 +74,8 @@ int upload_plan(Plan& p) {
   // each 256-byte aligned
   auto al = [](size_t n) { return (n + 255) / 256 * 256; };
   const size_t o_win = 0;
-  const size_t o_twm = o_win + al(M * sizeof(float2));
+  const size_t o_twp = o_win + al(M * sizeof(float2));
+  const size_t o_twm = o_twp + al(M * sizeof(float2));
   const size_t o_twn = o_twm + al(M * sizeof(float2));
   const size_t o_rows = o_twn + al(M * sizeof(float2));
   const size_t o_w = o_rows + al(p.n_mels * sizeof(MelRow));
@@ -82,12 +83,13 @@ int upload_plan(Plan& p) {
   const size_t o_bw = o_tbl + al((8 + 4 * p.blocks.size()) * sizeof(int32_t));
   const size_t o_taps = o_bw + al(std::max<size_t>(p.blk_w.size(), 1) * sizeof(float));
   const size_t total = o_taps + al(p.taps.size() * sizeof(BinTap));
-  // the kernels copy win2 and tw_m as one block of 16*M bytes
-  if (o_twm != o_win + static_cast<size_t>(M) * sizeof(float2) && tables_in_lds(p.fft.n1, M))
+  // the kernels copy win2 and tw_p as one block of 16*M bytes
+  if (o_twp != o_win + static_cast<size_t>(M) * sizeof(float2) && tables_in_lds(p.fft.n1, M))
     return set_error(FM_E_HIP, "internal: pass-1 tables are not contiguous");
   std::vector<unsigned char> host(total, 0);
   float* win2 = reinterpret_cast<float*>(host.data() + o_win);
   for (int j = 0; j < p.n_fft; ++j) win2[j] = 0.5f * p.window[j];  // exact scaling
+  std::copy(p.tw_p.begin(), p.tw_p.end(), reinterpret_cast<float*>(host.data() + o_twp));
   std::copy(p.tw_m.begin(), p.tw_m.end(), reinterpret_cast<float*>(host.data() + o_twm));
   std::copy(p.tw_n.begin(), p.tw_n.end(), reinterpret_cast<float*>(host.data() + o_twn));
   std::copy(p.rows.begin(), p.rows.end(), reinterpret_cast<MelRow*>(host.data() + o_rows));
@@ -113,6 +115,7 @@ int upload_plan(Plan& p) {
   unsigned char* base = static_cast<unsigned char*>(d);
   p.d_block = d;
   p.d_win2 = base + o_win;
+  p.d_tw_p = base + o_twp;
   p.d_tw_m = base + o_twm;
   p.d_tw_n = base + o_twn;
   p.d_rows = base + o_rows;
@@ -333,7 +336,7 @@ int launch_forward(const Plan& p, const void* in, int in_dtype, int64_t batch, i
   a.in = in;
   a.out = out;
   a.win2 = static_cast<const float2*>(p.d_win2);
-  a.tw_m = static_cast<const float2*>(p.d_tw_m);
+  a.tw_m = static_cast<const float2*>(p.d_tw_p);
   a.tw_n = static_cast<const float2*>(p.d_tw_n);
   a.length = length;
   a.n_frames = static_cast<int>(T);

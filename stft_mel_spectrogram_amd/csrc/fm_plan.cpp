@@ -335,6 +335,17 @@ int build_host_plan(Plan& p, const fm_args& a) {
     p.tw_n[2 * j] = static_cast<float>(c);
     p.tw_n[2 * j + 1] = static_cast<float>(-s);
   }
+  // the first pass's twiddles exp(-2 pi i n2 k1 / M) in [k1][n2] order, so
+  // that the threads of a pass (consecutive n2) read consecutive entries
+  p.tw_p.assign(2 * M, 0.0f);
+  if (fs.n3 == 0) {
+    for (int k1 = 0; k1 < fs.n1; ++k1)
+      for (int n2 = 0; n2 < fs.n2; ++n2) {
+        const int e = (n2 * k1) % M;
+        p.tw_p[2 * (k1 * fs.n2 + n2)] = p.tw_m[2 * e];
+        p.tw_p[2 * (k1 * fs.n2 + n2) + 1] = p.tw_m[2 * e + 1];
+      }
+  }
 
   // ---- mel blocks ----------------------------------------------------------
   // Blocks of 16 filters; each covers the union of its filters' bin runs,
