@@ -378,3 +378,18 @@ def test_build_rejects_kernels_that_use_scratch():
     ])
     assert scratch_users(remarks) == [("_Z4kern2v", 12), ("_Z4kern3v", 8)]
     assert scratch_users("") == []
+
+
+def test_forward_variant_choice(monkeypatch):
+    """n_fft 400 takes the split kernel unless FM_FORWARD=paired (read at plan
+    creation); n_fft 8192 and 16384 always take the three-pass kernel."""
+    p = N.Plan(device=False, sample_rate=16000, n_fft=400, hop_length=160, n_mels=128)
+    assert p.info().forward_variant == N.FM_FWD_SPLIT
+    monkeypatch.setenv("FM_FORWARD", "paired")
+    p = N.Plan(device=False, sample_rate=16000, n_fft=400, hop_length=160, n_mels=128)
+    assert p.info().forward_variant == N.FM_FWD_PAIRED
+    p = N.Plan(device=False, sample_rate=16000, n_fft=512, hop_length=160, n_mels=80)
+    assert p.info().forward_variant == N.FM_FWD_SPLIT       # not built for other sizes
+    p = N.Plan(device=False, sample_rate=44100, n_fft=16384, hop_length=4096, n_mels=256,
+               f_max=22050.0)
+    assert p.info().forward_variant == N.FM_FWD_LARGE
