@@ -25,8 +25,8 @@
 // its CSR run of nonzero weights (copied into LDS behind the buffer once per
 // workgroup).  Each pass writes back the positions it
 // read, so one buffer serves all three; its strides (D + 1 per c, an odd
-// C (D + 1) + 1 per a) keep every pass and the split's reads of consecutive
-// bins free of LDS bank conflicts.
+// C (D + 1) + 1 per a) put the threads of a pass, and the split's reads of
+// consecutive bins, on distinct banks or at most two to a bank.
 #pragma once
 
 #include "fm_kernel.h"
@@ -58,9 +58,9 @@ struct LArgs {
   int w_lds;             // LDS byte offset of the weights (after the exchange buffer)
 };
 
-// LDS strides of the exchange buffer (in complex values).
+// LDS strides of the exchange buffer (in complex values): per c and per a.
 template <int C, int D>
-constexpr int kLargeRowC = D + 1;
+constexpr int kLargeRowC = D + 1;  // (C unused: both strides take the shape)
 template <int C, int D>
 constexpr int kLargeRowA = C * (D + 1) + 1;
 
