@@ -152,7 +152,7 @@ def window_scale(hann: np.ndarray, normalized) -> float:
     raise ValueError(f"unknown normalized={normalized!r}")
 
 
-def make_window(n_fft: int, win_length: int, normalized) -> np.ndarray:
+def analysis_window(n_fft: int, win_length: int, normalized) -> np.ndarray:
     """The length-n_fft analysis window, evaluated position by position.
 
     flashmel page, ``flashmel/filters.py`` (window construction): a periodic
@@ -338,7 +338,7 @@ def mel_spectrogram(x, *, sample_rate: int = 16000, n_fft: int = 400,
     xf = to_float64(x)
     lead = xf.shape[:-1]
     xf = xf.reshape(-1, xf.shape[-1])
-    window = make_window(n_fft, win_length, normalized)
+    window = analysis_window(n_fft, win_length, normalized)
     fb = mel_filterbank(n_fft // 2 + 1, f_min, f_max, n_mels, sample_rate, norm, mel_scale)
     outs = []
     for s in range(0, xf.shape[0], max(1, chunk)):
@@ -432,7 +432,7 @@ def mel_spectrogram_vjp(x, grad_out, *, sample_rate: int = 16000, n_fft: int = 4
     L = xf.shape[-1]
     xf = xf.reshape(-1, L)
     g = np.asarray(grad_out, dtype=np.float64).reshape((xf.shape[0],) + np.shape(grad_out)[-2:])
-    window = make_window(n_fft, win_length, normalized)
+    window = analysis_window(n_fft, win_length, normalized)
     fb = mel_filterbank(n_fft // 2 + 1, f_min, f_max, n_mels, sample_rate, norm, mel_scale)
     outs = []
     for s in range(0, xf.shape[0], max(1, chunk)):

@@ -91,13 +91,13 @@ def test_hann_closed_form_sums(n):
 
 
 def test_window_centring_and_normalisation():
-    w = O.make_window(16, 10, False)
+    w = O.analysis_window(16, 10, False)
     assert np.all(w[:3] == 0) and np.all(w[13:] == 0)   # left = (16-10)//2 = 3
     np.testing.assert_allclose(w[3:13], scipy.signal.get_window("hann", 10), atol=1e-15)
-    wn = O.make_window(16, 10, "window")
+    wn = O.analysis_window(16, 10, "window")
     assert abs((wn * wn).sum() - 1.0) < 1e-14
-    assert O.make_window(16, 10, True).tolist() == wn.tolist()
-    wf = O.make_window(16, 10, "frame_length")
+    assert O.analysis_window(16, 10, True).tolist() == wn.tolist()
+    wf = O.analysis_window(16, 10, "frame_length")
     np.testing.assert_allclose(wf * math.sqrt(10), w, atol=1e-15)
 
 

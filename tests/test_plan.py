@@ -50,7 +50,7 @@ def host_plan(cfg, **kw):
 def test_window_matches_oracle(name):
     cfg = W.WORKLOADS[name]
     t = host_plan(cfg).tables()
-    ref = O.make_window(cfg["n_fft"], cfg["win_length"], False)
+    ref = O.analysis_window(cfg["n_fft"], cfg["win_length"], False)
     np.testing.assert_allclose(t["window"], ref, rtol=1.2e-7, atol=1e-30)
 
 
@@ -59,7 +59,7 @@ def test_window_matches_oracle(name):
 def test_window_normalisation_matches_oracle(normalized, win):
     p = N.Plan(device=False, n_fft=400, win_length=win, hop_length=100, n_mels=40,
                normalized=normalized)
-    np.testing.assert_allclose(p.tables()["window"], O.make_window(400, win, normalized),
+    np.testing.assert_allclose(p.tables()["window"], O.analysis_window(400, win, normalized),
                                rtol=1.2e-7, atol=1e-30)
     assert p.info().normalized == (2 if normalized == "frame_length" else 1)
 
@@ -109,7 +109,7 @@ def test_raw_args_validation():
 
 def test_window_shorter_than_nfft_is_centred():
     p = N.Plan(device=False, sample_rate=16000, n_fft=400, win_length=300, hop_length=100, n_mels=40)
-    np.testing.assert_allclose(p.tables()["window"], O.make_window(400, 300, False), rtol=1.2e-7, atol=1e-30)
+    np.testing.assert_allclose(p.tables()["window"], O.analysis_window(400, 300, False), rtol=1.2e-7, atol=1e-30)
 
 
 @pytest.mark.parametrize("name", ["tiny", "whisper", "pow2", "large"])
