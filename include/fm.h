@@ -209,6 +209,23 @@ int fm_backward(const fm_plan* plan, const float* in, int64_t batch, int64_t len
  */
 int64_t fm_out_frames(const fm_plan* plan, int64_t length);
 
+/*
+ * fm_forward_config -- how fm_forward runs a call of `batch` signals of
+ * `length` samples on this plan, without running it: *variant = the kernel
+ * (FM_FWD_SPLIT, FM_FWD_ROWS, FM_FWD_PAIRED or FM_FWD_LARGE; never
+ * FM_FWD_AUTO), *tile_frames = frames per workgroup tile (PAIRED: frames per
+ * chunk at most), *workgroups = workgroups launched (0 for batch 0).  The
+ * choice depends on the device the plan was created on (its compute units
+ * and the kernels' residency); a host-only plan assumes 256 compute units
+ * and one resident workgroup per unit.  Any output pointer may be NULL.
+ * Returns FM_OK, FM_E_INVAL (NULL plan, batch < 0) or the negative code of
+ * an invalid length (as fm_out_frames).  Operation-wise this is a host-side
+ * query of the launch geometry behind the pages' one-launch forward pass
+ * (flashmel 0.1.0 README "How it works").
+ */
+int fm_forward_config(const fm_plan* plan, int64_t batch, int64_t length, int* variant,
+                      int* tile_frames, int64_t* workgroups);
+
 /* fm_plan_destroy -- free the plan and its device tables.  NULL is a no-op. */
 int fm_plan_destroy(fm_plan* plan);
 
@@ -228,10 +245,12 @@ typedef struct fm_plan_info {
   int fft_n1, fft_n2; /* complex FFT of n_fft/2 = fft_n1 * fft_n2 points of
                        the split forward kernel and of the backward          */
   int tile_frames;  /* frames per workgroup tile (paired: per chunk)        */
-  int threads;      /* threads per workgroup                                */
+  int threads;      /* threads per workgroup (FM_FWD_AUTO: of the split
+                       kernel; the row kernel runs 512)                    */
   int lds_bytes;    /* dynamic LDS per workgroup                            */
   int has_device;   /* 1 if the plan owns device tables                     */
-  int forward_variant; /* FM_FWD_SPLIT, FM_FWD_PAIRED or FM_FWD_LARGE       */
+  int forward_variant; /* FM_FWD_SPLIT, FM_FWD_PAIRED, FM_FWD_LARGE,
+                          FM_FWD_ROWS or FM_FWD_AUTO                       */
   int fft_n3;       /* FM_FWD_LARGE: n_fft/2 = fft_n1 * fft_n2 * fft_n3 (three
                        passes); 0 otherwise                                  */
 } fm_plan_info;
@@ -246,10 +265,21 @@ typedef struct fm_plan_info {
  * creation (measured slower than SPLIT; kept for A/B measurements).
  * LARGE: n_fft 8192 and 16384, whose complex FFT of n_fft/2 points runs in
  * three passes over one LDS buffer, one frame at a time per workgroup, with
- * the mel projection over the CSR rows (these sizes have no backward).    */
+ * the mel projection over the CSR rows (these sizes have no backward).
+ * ROWS: the SPLIT chain with 512-thread workgroups whose second FFT pass
+ * gives each of a frame's 8 rows of n_fft/16 points its own thread (the
+ * mirrored row's values exchanged between lanes); built for n_fft = 400.
+ * AUTO (the default for n_fft = 400): ROWS or SPLIT chosen per call, SPLIT
+ * only for calls whose tiles fill more than 7/8 of one round of resident
+ * workgroups (fm_forward_config reports the choice); FM_FORWARD=rows or
+ * FM_FORWARD=split at plan creation forces one of them.  ROWS and SPLIT
+ * compute the same operations in the same order: their outputs are
+ * identical.                                                             */
 #define FM_FWD_SPLIT 0
 #define FM_FWD_PAIRED 1
 #define FM_FWD_LARGE 2
+#define FM_FWD_ROWS 3
+#define FM_FWD_AUTO 4
 
 int fm_plan_info_get(const fm_plan* plan, fm_plan_info* info);
 

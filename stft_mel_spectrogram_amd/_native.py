@@ -28,6 +28,8 @@ FM_F16 = 2
 FM_FWD_SPLIT = 0
 FM_FWD_PAIRED = 1
 FM_FWD_LARGE = 2
+FM_FWD_ROWS = 3
+FM_FWD_AUTO = 4
 FM_NORMALIZED = {False: 0, None: 0, True: 1, "window": 1, "frame_length": 2}
 FM_OUT = {"f32": FM_F32, "f16": FM_F16}
 
@@ -75,6 +77,8 @@ def _load() -> ctypes.CDLL:
         "fm_forward": (I, [P, P, I, I64, I64, P, P]),
         "fm_backward": (I, [P, P, I64, I64, P, P, P]),
         "fm_out_frames": (I64, [P, I64]),
+        "fm_forward_config": (I, [P, I64, I64, ctypes.POINTER(I), ctypes.POINTER(I),
+                                  ctypes.POINTER(I64)]),
         "fm_plan_destroy": (I, [P]),
         "fm_strerror": (ctypes.c_char_p, [I]),
         "fm_last_error": (ctypes.c_char_p, []),
@@ -152,6 +156,13 @@ class Plan:
 
     def out_frames(self, length: int) -> int:
         return check(lib.fm_out_frames(self.handle, int(length)))
+
+    def forward_config(self, batch: int, length: int):
+        """(variant, tile_frames, workgroups) that fm_forward takes for this call."""
+        v, t, w = ctypes.c_int(), ctypes.c_int(), ctypes.c_int64()
+        check(lib.fm_forward_config(self.handle, int(batch), int(length), ctypes.byref(v),
+                                    ctypes.byref(t), ctypes.byref(w)))
+        return v.value, t.value, w.value
 
     def tables(self):
         """Host tables as numpy arrays (window, first, len, off, weights, tw_m, tw_n)."""

@@ -116,6 +116,12 @@ constexpr int bwd_chunk_cap(int n1, int n2, int threads) {
 constexpr int kFwdSplit = 0;
 constexpr int kFwdPaired = 1;
 constexpr int kFwdLarge = 2;
+constexpr int kFwdRows = 3;
+constexpr int kFwdAuto = 4;  // ROWS or SPLIT, chosen per call (choose_forward)
+// Row-per-thread kernel (fm_rows.h): threads per workgroup; built for
+// n_fft = 400 (8 x 25).
+constexpr int kRowsThreadsHost = 512;
+constexpr bool has_rows_kernel(int n1, int n2) { return n1 == 8 && n2 == 25; }
 // Paired kernel: R x R complex points per frame pair (n_fft = R*R); shapes
 // built into the library.
 constexpr int pair_radix_for(int n_fft) { return n_fft == 400 ? 20 : 0; }
@@ -197,10 +203,13 @@ struct Plan {
   const void* d_mel_tbl = nullptr;    // int32[8 + 4*n_blocks]: wave_beg, pad, blocks
   const void* d_blk_w = nullptr;      // float[blk_w.size()]
   // forward kernel variant: FM_FWD_SPLIT (fm_kernel.h: complex FFT of n_fft/2
-  // points and the real split, one tile per workgroup), FM_FWD_PAIRED
-  // (fm_pair.h: two frames per complex FFT of n_fft points) or FM_FWD_LARGE
-  // (fm_large.h: n_fft 8192 and 16384, three FFT passes, one frame at a time)
+  // points and the real split, one tile per workgroup), FM_FWD_ROWS
+  // (fm_rows.h: the same with one second-pass thread per row), FM_FWD_AUTO
+  // (one of those two per call), FM_FWD_PAIRED (fm_pair.h: two frames per
+  // complex FFT of n_fft points) or FM_FWD_LARGE (fm_large.h: n_fft 8192 and
+  // 16384, three FFT passes, one frame at a time)
   int fwd_variant = 0;
+  std::vector<int> rows_wg_per_cu;  // [tile frames] resident row-kernel workgroups per CU
   int pair_r = 0;              // paired: n_fft = pair_r * pair_r
   int pair_chunk = 0;          // paired: frames per chunk at most (even)
   int pair_lds_bytes = 0;      // paired: dynamic LDS per workgroup
@@ -265,6 +274,17 @@ void* pair_kernel_for(int in_dtype, int pmode);
 // (large-FFT kernel entry points, fm_large_*.hip)
 template <int A, int C, int D>
 void* large_kernel_for(int in_dtype, int pmode);
+// (row-per-thread kernel entry points, fm_shape_8x25.hip)
+template <int N2>
+void* rows_kernel_for(int in_dtype, int pmode);
+// How a forward call of `batch` signals of T frames runs: kernel variant
+// (never kFwdAuto), frames per tile (paired: per chunk) and workgroups.
+struct FwdChoice {
+  int variant = kFwdSplit;
+  int tile = 1;
+  int64_t workgroups = 0;
+};
+FwdChoice choose_forward(const Plan& p, int64_t batch, int64_t T);
 int launch_forward(const Plan& p, const void* in, int in_dtype, int64_t batch,
                    int64_t length, void* out, void* stream);
 int launch_backward(const Plan& p, const float* in, int64_t batch, int64_t length,

@@ -10,6 +10,7 @@
 #include "fm_backward.h"
 #include "fm_large.h"
 #include "fm_pair.h"
+#include "fm_rows.h"
 
 namespace fm {
 
@@ -51,6 +52,9 @@ void* select_large_kernel(const Plan& p, int in_dtype) {
   FM_FOR_EACH_LARGE_SHAPE(FM_SELECT_LARGE)
 #undef FM_SELECT_LARGE
   return nullptr;
+}
+void* select_rows_kernel(const Plan& p, int in_dtype) {
+  return has_rows_kernel(p.fft.n1, p.fft.n2) ? rows_kernel_for<25>(in_dtype, power_mode(p)) : nullptr;
 }
 void* select_pair_kernel(const Plan& p, int in_dtype) {
   if (p.pair_r == 20) return pair_kernel_for<20>(in_dtype, power_mode(p));
@@ -167,6 +171,22 @@ int upload_plan(Plan& p) {
         p.wg_per_cu[g] = std::max(1, n);
     }
   }
+  // The row kernel (same LDS layout): opt-in and residency.
+  if (p.fwd_variant == kFwdRows || p.fwd_variant == kFwdAuto) {
+    for (int dt : {FM_F32, FM_I16}) {
+      void* k = select_rows_kernel(p, dt);
+      if (!k) return set_error(FM_E_UNSUPPORTED, "no row kernel for this n_fft");
+      e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, p.lds_bytes);
+      if (e != hipSuccess) return hip_fail(e, "hipFuncSetAttribute (rows)");
+    }
+    p.rows_wg_per_cu.assign(p.tile_max + 1, 1);
+    void* k = select_rows_kernel(p, FM_F32);
+    for (int g = (p.tile_max + 1) / 2; g <= p.tile_max; ++g) {
+      int n = 0;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k, kRowsThreadsHost, tile_lds_bytes(p, g)) == hipSuccess)
+        p.rows_wg_per_cu[g] = std::max(1, n);
+    }
+  }
   // The backward kernel of the plan's power mode: LDS opt-in and residency.
   p.bwd_wg_per_cu.assign(p.bwd_chunk_max + 1, 1);
   if (p.bwd_chunk_max > 0) {
@@ -196,43 +216,6 @@ void free_plan_device(Plan& p) {
   p.has_device = false;
 }
 
-namespace {
-
-// Frames per tile for this call.  Rounds of resident workgroups times the
-// time of one workgroup, which grows with its pass-1 rounds (frames per
-// thread) on top of a fixed part (pass 2, split, mel) worth about 3 of them;
-// ties go to smaller tiles (more compute units busy for small calls).
-// Measured: n_fft 2048 x 64 signals picks 16 frames (7 rounds of 1 per CU:
-// 127 us) where "fewest frames on the busiest CU" picked 12 (9 rounds:
-// 160 us); the whisper shape keeps 47.  Calls with fewer tiles than CUs
-// then shrink the tile while every tile still gets a CU of its own
-// (1 x 16000 samples: 1-frame tiles, 8.2 us, against 10.0 us with 32-frame
-// tiles; below that point, in calls of several rounds, the model above does
-// not rank small tiles reliably and they measured slower).
-int choose_tile(const Plan& p, int64_t batch, int64_t T) {
-  if (p.tile_override > 0) return p.tile_override;
-  const int ncu = p.n_cu > 0 ? p.n_cu : 256;
-  const int slots = std::max(1, p.threads / p.fft.n2);  // frames per pass-1 round
-  int best = p.tile_max;
-  int64_t best_cost = INT64_MAX;
-  for (int g = (p.tile_max + 1) / 2; g <= p.tile_max; ++g) {
-    const int64_t tiles = batch * ((T + g - 1) / g);
-    const int occ = (g < static_cast<int>(p.wg_per_cu.size()) && p.wg_per_cu[g] > 0) ? p.wg_per_cu[g] : 1;
-    const int64_t rounds = (tiles + static_cast<int64_t>(ncu) * occ - 1) / (static_cast<int64_t>(ncu) * occ);
-    const int64_t cost = rounds * ((g + slots - 1) / slots + 3);
-    if (cost < best_cost) {
-      best_cost = cost;
-      best = g;
-    }
-  }
-  // A call that leaves CUs idle takes smaller tiles, down to one per CU.
-  if (batch * ((T + best - 1) / best) < ncu) {
-    while (best > 1 && batch * ((T + best - 2) / (best - 1)) <= ncu) --best;
-  }
-  return best;
-}
-
-}  // namespace
 
 int launch_forward(const Plan& p, const void* in, int in_dtype, int64_t batch, int64_t length,
                    void* out, void* stream) {
@@ -247,11 +230,11 @@ int launch_forward(const Plan& p, const void* in, int in_dtype, int64_t batch, i
   hipError_t e = hipGetDevice(&cur);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
   if (cur != p.device) return set_error(FM_E_INVAL, "plan belongs to another device than the current one");
-  if (p.fwd_variant == kFwdPaired) {
+  const FwdChoice c = choose_forward(p, batch, T);
+  if (c.variant == kFwdPaired) {
     if (length > (1 << 29)) return set_error(FM_E_INVAL, "problem too large for one launch (length <= 2^29)");
     const int64_t total = batch * T;
-    const int64_t slots = static_cast<int64_t>(p.n_cu > 0 ? p.n_cu : 256) * p.pair_wg_per_cu;
-    const int64_t grid = std::min(total, slots);
+    const int64_t grid = c.workgroups;
     PArgs a;
     a.in = in;
     a.out = out;
@@ -282,14 +265,9 @@ int launch_forward(const Plan& p, const void* in, int in_dtype, int64_t batch, i
     if (e != hipSuccess) return hip_fail(e, "kernel launch (paired)");
     return FM_OK;
   }
-  if (p.fwd_variant == kFwdLarge) {
+  if (c.variant == kFwdLarge) {
     if (length > (1 << 29)) return set_error(FM_E_INVAL, "problem too large for one launch (length <= 2^29)");
-    // Frames per workgroup: the fewest that put every frame in the first
-    // round of resident workgroups (each walks its frames one at a time).
-    const int64_t slots = static_cast<int64_t>(p.n_cu > 0 ? p.n_cu : 256) * p.large_wg_per_cu;
-    int64_t g = p.tile_override > 0 ? p.tile_override : 1;
-    if (p.tile_override <= 0)
-      while (g < p.tile_max && batch * ((T + g - 1) / g) > slots) ++g;
+    const int64_t g = c.tile;
     const int64_t tiles = (T + g - 1) / g;
     if (tiles * batch > INT32_MAX) return set_error(FM_E_INVAL, "problem too large for one launch");
     LArgs a;
@@ -325,7 +303,8 @@ int launch_forward(const Plan& p, const void* in, int in_dtype, int64_t batch, i
     if (e != hipSuccess) return hip_fail(e, "kernel launch (large)");
     return FM_OK;
   }
-  const int G = choose_tile(p, batch, T);
+  const bool rows = c.variant == kFwdRows;
+  const int G = c.tile;
   const int64_t tiles = (T + G - 1) / G;
   if (length > (1 << 29) || tiles * batch > INT32_MAX)
     return set_error(FM_E_INVAL, "problem too large for one launch (length <= 2^29, tiles < 2^31)");
@@ -360,11 +339,11 @@ int launch_forward(const Plan& p, const void* in, int in_dtype, int64_t batch, i
   a.tab_lds = tile_tables_offset(p, G);
   a.twn_lds = tile_twiddles_offset(p, G);
 
-  void* k = select_kernel(p, in_dtype, use_tile_copy(p));
+  void* k = rows ? select_rows_kernel(p, in_dtype) : select_kernel(p, in_dtype, use_tile_copy(p));
   if (!k) return set_error(FM_E_UNSUPPORTED, "no kernel for this n_fft");
   void* args[] = {&a};
-  e = hipLaunchKernel(k, dim3(static_cast<unsigned>(n_tiles)), dim3(p.threads), args,
-                      static_cast<size_t>(lds), static_cast<hipStream_t>(stream));
+  e = hipLaunchKernel(k, dim3(static_cast<unsigned>(n_tiles)), dim3(rows ? kRowsThreadsHost : p.threads),
+                      args, static_cast<size_t>(lds), static_cast<hipStream_t>(stream));
   // (the launch's own status only: hipGetLastError would also report, and
   // clear, an unrelated earlier failure on the caller's thread)
   if (e != hipSuccess) return hip_fail(e, "kernel launch");

@@ -469,10 +469,19 @@ int build_host_plan(Plan& p, const fm_args& a) {
     p.pair_lds_bytes = bytes;
     bool use = false;  // measured slower than the split kernel so far: opt-in only
     if (const char* e = std::getenv("FM_FORWARD")) {
-      if (std::string(e) == "split") use = false;
       if (std::string(e) == "paired" && fits && bytes <= 160 * 1024) use = true;
     }
     if (use) p.fwd_variant = kFwdPaired;
+  }
+  // Row-per-thread kernel where it is built (its second pass needs one
+  // thread per row of every frame of a tile): chosen per call by default,
+  // FM_FORWARD=rows or split forces one of the two (for A/B measurements).
+  if (p.fwd_variant == kFwdSplit && has_rows_kernel(fs.n1, fs.n2) && tmax * fs.n1 <= kRowsThreadsHost) {
+    p.fwd_variant = kFwdAuto;
+    if (const char* e = std::getenv("FM_FORWARD")) {
+      if (std::string(e) == "rows") p.fwd_variant = kFwdRows;
+      if (std::string(e) == "split") p.fwd_variant = kFwdSplit;
+    }
   }
   p.tile_override = 0;
   p.bwd_chunk_override = 0;
@@ -485,6 +494,99 @@ int build_host_plan(Plan& p, const fm_args& a) {
     if (v >= 1 && v <= tmax) p.tile_override = v;
   }
   return FM_OK;
+}
+
+namespace {
+
+// Resident workgroups per CU for a tile of g frames (1 where unknown: host
+// plans, or sizes the device pass did not measure).
+int occupancy(const std::vector<int>& tab, int g) {
+  return (g < static_cast<int>(tab.size()) && tab[g] > 0) ? tab[g] : 1;
+}
+
+// Frames per tile for a tile-per-workgroup kernel of `threads` threads with
+// residency table `occ`.  Rounds of resident workgroups times the time of
+// one workgroup, which grows with its pass-1 rounds (frames per thread) on
+// top of a fixed part (pass 2, split, mel) worth about 3 of them; ties go to
+// smaller tiles (more compute units busy for small calls).  Measured: n_fft
+// 2048 x 64 signals picks 16 frames (7 rounds of 1 per CU: 127 us) where
+// "fewest frames on the busiest CU" picked 12 (9 rounds: 160 us); the
+// whisper shape keeps 47.  Calls with fewer tiles than CUs then shrink the
+// tile while every tile still gets a CU of its own (1 x 16000 samples:
+// 1-frame tiles, 8.2 us, against 10.0 us with 32-frame tiles; below that
+// point, in calls of several rounds, the model above does not rank small
+// tiles reliably and they measured slower).
+int choose_tile(const Plan& p, int64_t batch, int64_t T, int threads, const std::vector<int>& occ) {
+  if (p.tile_override > 0) return p.tile_override;
+  const int64_t ncu = p.n_cu > 0 ? p.n_cu : 256;
+  const int slots = std::max(1, threads / p.fft.n2);  // frames per pass-1 round
+  int best = p.tile_max;
+  int64_t best_cost = INT64_MAX;
+  for (int g = (p.tile_max + 1) / 2; g <= p.tile_max; ++g) {
+    const int64_t tiles = batch * ((T + g - 1) / g);
+    const int64_t per_round = ncu * occupancy(occ, g);
+    const int64_t rounds = (tiles + per_round - 1) / per_round;
+    const int64_t cost = rounds * ((g + slots - 1) / slots + 3);
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = g;
+    }
+  }
+  // A call that leaves CUs idle takes smaller tiles, down to one per CU.
+  if (batch * ((T + best - 1) / best) < ncu) {
+    while (best > 1 && batch * ((T + best - 2) / (best - 1)) <= ncu) --best;
+  }
+  return best;
+}
+
+}  // namespace
+
+// Kernel and tiling of one forward call.  Between the split and the row
+// kernel (FM_FWD_AUTO plans) the row kernel is taken, except for calls whose
+// split tiles fill more than 7/8 of one round of resident workgroups: there
+// every CU runs two tiles whose phases proceed in lockstep, the second pass
+// is bound by the SIMDs' issue rate rather than by one thread's chain of
+// dependent operations, and the split kernel measured about 1% faster
+// (whisper shape, 8 x 480000 samples: 16.78 against 16.98 us per launch).
+// Everywhere else the row kernel measured 1-17% faster (1 x 16000: 6.7
+// against 8.1 us; 32 x 480000: 60.5 against 62.7 us).
+FwdChoice choose_forward(const Plan& p, int64_t batch, int64_t T) {
+  FwdChoice c;
+  const int64_t ncu = p.n_cu > 0 ? p.n_cu : 256;
+  const int64_t nb = std::max<int64_t>(batch, 1);
+  if (p.fwd_variant == kFwdPaired) {
+    c.variant = kFwdPaired;
+    c.tile = p.pair_chunk;
+    c.workgroups = std::min(batch * T, ncu * p.pair_wg_per_cu);
+    return c;
+  }
+  if (p.fwd_variant == kFwdLarge) {
+    // the fewest frames per workgroup that put every frame in the first
+    // round of resident workgroups (each walks its frames one at a time)
+    const int64_t slots = ncu * p.large_wg_per_cu;
+    int64_t g = p.tile_override > 0 ? p.tile_override : 1;
+    if (p.tile_override <= 0)
+      while (g < p.tile_max && nb * ((T + g - 1) / g) > slots) ++g;
+    c.variant = kFwdLarge;
+    c.tile = static_cast<int>(g);
+    c.workgroups = batch * ((T + g - 1) / g);
+    return c;
+  }
+  c.variant = kFwdSplit;
+  c.tile = choose_tile(p, nb, T, p.threads, p.wg_per_cu);
+  c.workgroups = batch * ((T + c.tile - 1) / c.tile);
+  bool rows = p.fwd_variant == kFwdRows;
+  if (p.fwd_variant == kFwdAuto) {
+    const int64_t tiles = nb * ((T + c.tile - 1) / c.tile);
+    const int64_t slots = ncu * occupancy(p.wg_per_cu, c.tile);
+    rows = !(8 * tiles > 7 * slots && tiles <= slots);
+  }
+  if (rows) {
+    c.variant = kFwdRows;
+    c.tile = choose_tile(p, nb, T, kRowsThreadsHost, p.rows_wg_per_cu);
+    c.workgroups = batch * ((T + c.tile - 1) / c.tile);
+  }
+  return c;
 }
 
 }  // namespace fm

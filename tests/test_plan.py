@@ -381,10 +381,13 @@ def test_build_rejects_kernels_that_use_scratch():
 
 
 def test_forward_variant_choice(monkeypatch):
-    """n_fft 400 takes the split kernel unless FM_FORWARD=paired (read at plan
-    creation); n_fft 8192 and 16384 always take the three-pass kernel."""
+    """n_fft 400 chooses between the split and the row kernel per call unless
+    FM_FORWARD=paired, rows or split (read at plan creation); other sizes up to
+    4096 take the split kernel; n_fft 8192 and 16384 always take the three-pass
+    kernel."""
+    monkeypatch.delenv("FM_FORWARD", raising=False)
     p = N.Plan(device=False, sample_rate=16000, n_fft=400, hop_length=160, n_mels=128)
-    assert p.info().forward_variant == N.FM_FWD_SPLIT
+    assert p.info().forward_variant == N.FM_FWD_AUTO
     monkeypatch.setenv("FM_FORWARD", "paired")
     p = N.Plan(device=False, sample_rate=16000, n_fft=400, hop_length=160, n_mels=128)
     assert p.info().forward_variant == N.FM_FWD_PAIRED
@@ -393,3 +396,55 @@ def test_forward_variant_choice(monkeypatch):
     p = N.Plan(device=False, sample_rate=44100, n_fft=16384, hop_length=4096, n_mels=256,
                f_max=22050.0)
     assert p.info().forward_variant == N.FM_FWD_LARGE
+    monkeypatch.setenv("FM_FORWARD", "rows")
+    p = N.Plan(device=False, sample_rate=16000, n_fft=400, hop_length=160, n_mels=128)
+    assert p.info().forward_variant == N.FM_FWD_ROWS and p.info().threads == 512
+    p = N.Plan(device=False, sample_rate=16000, n_fft=1024, hop_length=256, n_mels=80)
+    assert p.info().forward_variant == N.FM_FWD_SPLIT and p.info().threads == 256
+    monkeypatch.setenv("FM_FORWARD", "split")
+    p = N.Plan(device=False, sample_rate=16000, n_fft=400, hop_length=160, n_mels=128)
+    assert p.info().forward_variant == N.FM_FWD_SPLIT and p.info().threads == 256
+
+
+def test_forward_config(monkeypatch):
+    """The per-call choice of an n_fft-400 plan: the row kernel, except for
+    calls whose split tiles fill more than 7/8 of one round of resident
+    workgroups (a host-only plan assumes 256 compute units, one workgroup
+    each); the workgroup count is batch x tiles per signal."""
+    monkeypatch.delenv("FM_FORWARD", raising=False)
+    monkeypatch.delenv("FM_TILE_FRAMES", raising=False)
+    p = N.Plan(device=False, sample_rate=16000, n_fft=400, hop_length=160, n_mels=128)
+    assert p.info().forward_variant == N.FM_FWD_AUTO and p.info().threads == 256
+    T = p.out_frames(480000)
+    assert T == 3001
+    v, g, wg = p.forward_config(4, 480000)          # 4 x 64 tiles of 47 = one full round
+    assert (v, g, wg) == (N.FM_FWD_SPLIT, 47, 256)
+    v, g, wg = p.forward_config(8, 480000)          # two rounds
+    assert v == N.FM_FWD_ROWS and wg == 8 * -(-T // g)
+    v, g, wg = p.forward_config(1, 16000)           # fewer tiles than compute units
+    assert v == N.FM_FWD_ROWS and g == 1 and wg == 101
+    for batch in (1, 2, 3, 5, 8, 16, 64):
+        for L in (16000, 160000, 480000):
+            v, g, wg = p.forward_config(batch, L)
+            T = p.out_frames(L)
+            tiles = batch * -(-T // g)
+            assert wg == tiles and 1 <= g <= p.info().tile_frames
+            vs, gs, ws = N.Plan(device=False, sample_rate=16000, n_fft=400, hop_length=160,
+                                n_mels=128).forward_config(batch, L)
+            split_fill = ws / 256
+            assert (v == N.FM_FWD_SPLIT) == (7 / 8 < split_fill <= 1), (batch, L, v, split_fill)
+    assert p.forward_config(0, 480000)[2] == 0
+    with pytest.raises(N.FmError):
+        p.forward_config(-1, 480000)
+    monkeypatch.setenv("FM_FORWARD", "split")
+    ps = N.Plan(device=False, sample_rate=16000, n_fft=400, hop_length=160, n_mels=128)
+    monkeypatch.setenv("FM_FORWARD", "rows")
+    pr = N.Plan(device=False, sample_rate=16000, n_fft=400, hop_length=160, n_mels=128)
+    for batch in (1, 4, 8):
+        assert ps.forward_config(batch, 480000)[0] == N.FM_FWD_SPLIT
+        assert pr.forward_config(batch, 480000)[0] == N.FM_FWD_ROWS
+    monkeypatch.delenv("FM_FORWARD")
+    pl = N.Plan(device=False, sample_rate=44100, n_fft=16384, hop_length=4096, n_mels=256,
+                f_max=22050.0)
+    v, g, wg = pl.forward_config(16, 441000)
+    assert v == N.FM_FWD_LARGE and wg == 16 * -(-pl.out_frames(441000) // g)
