@@ -107,13 +107,15 @@ int fm_backward(const fm_plan* plan, const float* in, int64_t batch, int64_t len
   return fm::launch_backward(plan->p, in, batch, length, grad_out, grad_in, stream);
 }
 
-int fm_forward_config(const fm_plan* plan, int64_t batch, int64_t length, int* variant,
-                      int* tile_frames, int64_t* workgroups) {
+int fm_forward_config(const fm_plan* plan, int in_dtype, int64_t batch, int64_t length,
+                      int* variant, int* tile_frames, int64_t* workgroups) {
   if (!plan) return fm::set_error(FM_E_INVAL, "plan must not be NULL");
+  if (in_dtype != FM_F32 && in_dtype != FM_I16)
+    return fm::set_error(FM_E_INVAL, "in_dtype must be FM_F32 or FM_I16");
   if (batch < 0) return fm::set_error(FM_E_INVAL, "batch must be >= 0");
   const int64_t T = fm::out_frames(plan->p, length);
   if (T < 0) return static_cast<int>(T);
-  const fm::FwdChoice c = fm::choose_forward(plan->p, batch, T);
+  const fm::FwdChoice c = fm::choose_forward(plan->p, in_dtype, batch, T);
   if (variant) *variant = c.variant;
   if (tile_frames) *tile_frames = c.tile;
   if (workgroups) *workgroups = c.workgroups;
@@ -165,7 +167,7 @@ int fm_plan_info_get(const fm_plan* plan, fm_plan_info* info) {
   const bool paired = p.fwd_variant == fm::kFwdPaired;
   info->tile_frames = paired ? p.pair_chunk : p.tile_max;
   info->threads = paired ? fm::kPairThreadsHost
-                         : (p.fwd_variant == fm::kFwdRows ? fm::kRowsThreadsHost : p.threads);
+                         : (p.fwd_variant == fm::kFwdRows ? fm::kRowsThreads : p.threads);
   info->lds_bytes = paired ? p.pair_lds_bytes : p.lds_bytes;
   info->forward_variant = p.fwd_variant;
   info->has_device = p.has_device ? 1 : 0;

@@ -118,10 +118,13 @@ constexpr int kFwdPaired = 1;
 constexpr int kFwdLarge = 2;
 constexpr int kFwdRows = 3;
 constexpr int kFwdAuto = 4;  // ROWS or SPLIT, chosen per call (choose_forward)
-// Row-per-thread kernel (fm_rows.h): threads per workgroup; built for
-// n_fft = 400 (8 x 25).
-constexpr int kRowsThreadsHost = 512;
-constexpr bool has_rows_kernel(int n1, int n2) { return n1 == 8 && n2 == 25; }
+// Row layout of the split kernel (fm_kernel.h, ROWS): threads per workgroup
+// (one second-pass thread per row: N1 per frame, 64 frames at N1 = 8), and
+// waves per SIMD it is built for: four (two tiles per CU, <= 128 registers)
+// where its rows are short and its pass 1 keeps samples in registers, else two.
+constexpr int kRowsThreads = 512;
+constexpr int kRowsMaxN1 = 32;  // built for n1 <= 32 (fm_kernel.h kRowsCapable)
+constexpr int rows_waves_per_simd(int n1, int n2) { return (n1 <= 16 && n2 <= 25) ? 4 : 2; }
 // Paired kernel: R x R complex points per frame pair (n_fft = R*R); shapes
 // built into the library.
 constexpr int pair_radix_for(int n_fft) { return n_fft == 400 ? 20 : 0; }
@@ -204,7 +207,7 @@ struct Plan {
   const void* d_blk_w = nullptr;      // float[blk_w.size()]
   // forward kernel variant: FM_FWD_SPLIT (fm_kernel.h: complex FFT of n_fft/2
   // points and the real split, one tile per workgroup), FM_FWD_ROWS
-  // (fm_rows.h: the same with one second-pass thread per row), FM_FWD_AUTO
+  // (fm_kernel.h with one second-pass thread per row), FM_FWD_AUTO
   // (one of those two per call), FM_FWD_PAIRED (fm_pair.h: two frames per
   // complex FFT of n_fft points) or FM_FWD_LARGE (fm_large.h: n_fft 8192 and
   // 16384, three FFT passes, one frame at a time)
@@ -274,17 +277,15 @@ void* pair_kernel_for(int in_dtype, int pmode);
 // (large-FFT kernel entry points, fm_large_*.hip)
 template <int A, int C, int D>
 void* large_kernel_for(int in_dtype, int pmode);
-// (row-per-thread kernel entry points, fm_shape_8x25.hip)
-template <int N2>
-void* rows_kernel_for(int in_dtype, int pmode);
-// How a forward call of `batch` signals of T frames runs: kernel variant
-// (never kFwdAuto), frames per tile (paired: per chunk) and workgroups.
+// How a forward call of `batch` signals of T frames of input type in_dtype
+// runs: kernel variant (never kFwdAuto), frames per tile (paired: per
+// chunk) and workgroups.
 struct FwdChoice {
   int variant = kFwdSplit;
   int tile = 1;
   int64_t workgroups = 0;
 };
-FwdChoice choose_forward(const Plan& p, int64_t batch, int64_t T);
+FwdChoice choose_forward(const Plan& p, int in_dtype, int64_t batch, int64_t T);
 int launch_forward(const Plan& p, const void* in, int in_dtype, int64_t batch,
                    int64_t length, void* out, void* stream);
 int launch_backward(const Plan& p, const float* in, int64_t batch, int64_t length,

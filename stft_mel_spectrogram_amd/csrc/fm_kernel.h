@@ -268,31 +268,37 @@ __device__ __forceinline__ void split_pair(float* pk, float* pm, float2 zk, floa
   *pm = power_of<PMODE>(fmaf(bx, bx, by * by), hp);
 }
 
-// Two waves per SIMD (<= 256 registers each): two workgroups per compute
-// unit wherever two tiles fit the LDS, or one workgroup of 8 waves
-// (n_fft = 2048, whose tile takes the whole LDS); n_fft = 4096 runs one wave
-// per SIMD.
-template <int N1, int N2>
-constexpr int kMinWavesPerSimd = (N1 * N2 <= 1024) ? 2 : 1;
-template <int N1, int N2>
-constexpr int kThreads = threads_for(N1, N2);
+// Pair layout: two waves per SIMD (<= 256 registers each): two workgroups
+// per compute unit wherever two tiles fit the LDS, or one workgroup of 8
+// waves (n_fft = 2048, whose tile takes the whole LDS); n_fft = 4096 runs one
+// wave per SIMD.  Row layout (ROWS): 8 waves, four per SIMD (<= 128
+// registers: two tiles per CU) where the second pass's rows are short, else
+// two per SIMD.
+template <int N1, int N2, bool ROWS>
+constexpr int kMinWavesPerSimd = ROWS ? rows_waves_per_simd(N1, N2) : ((N1 * N2 <= 1024) ? 2 : 1);
+template <int N1, int N2, bool ROWS>
+constexpr int kThreads = ROWS ? kRowsThreads : threads_for(N1, N2);
 
 // Shapes whose pass-1 threads hold all their samples in registers (N1 <= 8)
 // and load two or more frames each can copy a tile's samples into LDS first
 // (COPY variant, chosen per call); the others only gather.
 template <int N1, int N2>
 constexpr bool kCopyCapable = (N1 <= 8) && (N2 >= 8);
+// The row layout is built up to N1 = 32: at N1 = 64 its 512 threads leave
+// each wave 256 registers, which the 64-point first pass overflows.
+template <int N1, int N2>
+constexpr bool kRowsCapable = N1 <= kRowsMaxN1;
 
-template <int N1, int N2, typename InT, int PMODE, bool COPY>
-__global__ __launch_bounds__((kThreads<N1, N2>), (kMinWavesPerSimd<N1, N2>)) void mel_forward_kernel(KArgs a) {
+template <int N1, int N2, typename InT, int PMODE, bool COPY, bool ROWS>
+__global__ __launch_bounds__((kThreads<N1, N2, ROWS>), (kMinWavesPerSimd<N1, N2, ROWS>)) void mel_forward_kernel(KArgs a) {
   constexpr int M = N1 * N2;
   constexpr int K = M + 1;        // one-sided bins
   constexpr int RS = exchange_row(N2);         // LDS row and frame strides (padded)
   constexpr int SY = exchange_stride(N1, N2);
   constexpr int SP = power_stride(M);
   constexpr int NF = 2 * M;       // n_fft
-  constexpr int NPAIR = N1 / 2;   // pass-2 threads per frame
-  constexpr int NT = kThreads<N1, N2>;  // threads of the workgroup
+  constexpr int NPAIR = N1 / 2;   // pass-2 threads per frame (pair layout)
+  constexpr int NT = kThreads<N1, N2, ROWS>;  // threads of the workgroup
   constexpr int NW = NT / 64;           // waves
   constexpr int SLOTS = NT / N2;  // frames per pass-1 round (one thread per n2)
   constexpr bool kHoist = N1 <= 8;   // window and twiddles in registers, all of
@@ -314,9 +320,10 @@ __global__ __launch_bounds__((kThreads<N1, N2>), (kMinWavesPerSimd<N1, N2>)) voi
   // pass-1 role of this thread: fixed n2, frames slot, slot+SLOTS, ...
   const int n2 = tid % N2;
   const int slot = tid / N2;
-  // pass-2 role: frame f2, pair p of first-pass outputs
-  const int f2 = tid / NPAIR;
-  const int p = tid - f2 * NPAIR;
+  // pass-2 role: frame f2, and pair p of first-pass output rows (row p
+  // itself in the row layout)
+  const int f2 = ROWS ? tid / N1 : tid / NPAIR;
+  const int p = ROWS ? tid - f2 * N1 : tid - f2 * NPAIR;
   // mel role: wave -> its list of filter blocks
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
@@ -477,87 +484,146 @@ __global__ __launch_bounds__((kThreads<N1, N2>), (kMinWavesPerSimd<N1, N2>)) voi
     }
     __syncthreads();
 
-    // ---- pass 2: paired N2-point DFTs, real split, power -> P (aliases Y) --
+    // ---- pass 2: N2-point DFTs, real split, power -> P (aliases Y) --
     const bool has = f2 < nvalid;
-    // Unified split schedule: lanes with p != 0 pair bins p + N1*k2 (row p)
-    // with M - that (row N1 - p); lanes with p == 0 own the self-paired rows 0
-    // and N1/2 and walk the same N2 iterations with their rows permuted
-    // (k2 < CA: row 0's pairs, k2 >= CA: row N1/2's), plus one extra pair.
-    // One instruction stream for every lane: no divergent branches.
-    constexpr int CA = N2 / 2 + 1;        // row 0 pairs of the p == 0 lanes
-    constexpr int D2 = N1 / 2 - N1 * CA;  // bin offset of row N1/2's pairs there
-    constexpr int JX = N2 - CA;           // index of row N1/2's extra pair
-    const bool p0 = (p == 0);
-    const int off_lo = p;                 // bin = off + N1*k2 for k2 < CA
-    const int off_hi = p0 ? D2 : p;       // ... and for k2 >= CA
-    float2 za[N2], zb[N2], wv[kTwPrefetch ? N2 + 1 : 1];
-    auto tw_at = [&](int idx, int k) -> float2 {
-      return kTwPrefetch ? wv[kTwPrefetch ? idx : 0] : (kTwLds ? twn_l[k] : a.tw_n[k]);
-    };
-    if (has) {
-      if constexpr (kTwPrefetch) {  // split twiddles load under the DFTs
+    if constexpr (ROWS) {
+      // Row layout: thread (f2, k1 = p) transforms row k1 alone.  The split
+      // of bin k = k1 + N1*j needs Z[M - k], which lies in row N1 - k1 at
+      // index N2-1-j (row 0: itself, index (N2-j) mod N2; row N1/2: itself,
+      // index N2-1-j).  A frame's N1 threads are N1 consecutive lanes of one
+      // wave, so the mirrored values come from the partner lane
+      // (ds_bpermute).  Rows k1 and N1-k1 share their N2 bin pairs: k1 <
+      // N1/2 takes ceil(N2/2) of them, N1-k1 the other floor(N2/2); row
+      // N1/2 has ceil(N2/2) pairs, row 0 floor(N2/2) + 1 (bin 0 with bin M).
+      constexpr int CH = (N2 + 1) / 2;
+      constexpr int CF = N2 / 2;
+      constexpr int CP = CF + 1;  // most pairs of any thread (row 0)
+      const int k1 = p;
+      float2 za[N2], wv[kTwPrefetch ? CP : 1];
+      auto tw_at = [&](int idx, int k) -> float2 {
+        return kTwPrefetch ? wv[kTwPrefetch ? idx : 0] : (kTwLds ? twn_l[k] : a.tw_n[k]);
+      };
+      if (has) {
+        if constexpr (kTwPrefetch) {  // split twiddles load under the DFT
 #pragma unroll
-        for (int k2 = 0; k2 < N2; ++k2) wv[k2] = a.tw_n[(k2 < CA ? off_lo : off_hi) + N1 * k2];
-        wv[N2] = a.tw_n[N1 / 2 + N1 * JX];
+          for (int j = 0; j < CP; ++j) wv[j] = a.tw_n[k1 + N1 * j];  // k1 + N1*j < M
+        }
+        const float2* ra = Y + f2 * SY + k1 * RS;
+#pragma unroll
+        for (int j = 0; j < N2; ++j) za[j] = ra[j];
+        Dft<N2>::run(za);
       }
-      const int ka = p;
-      const int kb = (p == 0) ? N1 / 2 : N1 - p;
-      const float2* ra = Y + f2 * SY + ka * RS;
-      const float2* rb = Y + f2 * SY + kb * RS;
+      // pv[j] = the partner row's Z at index N2-1-j (every lane takes part;
+      // a frame's lanes all have the same `has`)
+      const int partner = ((lane & ~(N1 - 1)) | ((N1 - k1) & (N1 - 1))) * 4;
+      float2 pv[CH];
 #pragma unroll
-      for (int j = 0; j < N2; ++j) {
-        za[j] = ra[j];
-        zb[j] = rb[j];
-      }
-      Dft<N2>::run(za);
-      Dft<N2>::run(zb);
-    }
-    // (the twiddle copies have landed: a wave without samples to load in
-    // pass 1 has not waited for its loads yet)
-    if constexpr (kTwLds) __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    // Every read of the exchange buffer is done: stream the mel weights into
-    // LDS behind the power tile (direct global -> LDS loads, 1 KB per wave
-    // instruction, lane l's 16 bytes at l*16), landing while the split runs.
-    for (int c = wave; c < a.w_chunks; c += NW)
-      __builtin_amdgcn_global_load_lds(a.blk_w + c * 256 + lane * 4, P + a.w_lds + c * 256, 16, 0, 0);
-    // the mel stage may read up to kMelTileOverrun - 1 floats past the last
-    // valid frame's row: keep them 0 (in a ragged last tile that is the
-    // unwritten row nvalid, else the slack after the tile)
-    if (tid < kMelTileOverrun) P[nvalid * SP + tid] = 0.0f;
-    if (has) {
-      float* prow = P + f2 * SP;
-      if constexpr (SP > K) {
-        if (p == 0) {
+      for (int j = 0; j < CH; ++j)
+        pv[j] = make_float2(
+            __int_as_float(__builtin_amdgcn_ds_bpermute(partner, __float_as_int(za[N2 - 1 - j].x))),
+            __int_as_float(__builtin_amdgcn_ds_bpermute(partner, __float_as_int(za[N2 - 1 - j].y))));
+      if constexpr (kTwLds) __builtin_amdgcn_s_waitcnt(0);  // the twiddle copies have landed
+      __syncthreads();
+      // every read of the exchange buffer is done: weights into LDS behind
+      // the power tile while the split runs, and the mel stage's overrun
+      for (int c = wave; c < a.w_chunks; c += NW)
+        __builtin_amdgcn_global_load_lds(a.blk_w + c * 256 + lane * 4, P + a.w_lds + c * 256, 16, 0, 0);
+      if (tid < kMelTileOverrun) P[nvalid * SP + tid] = 0.0f;
+      static_assert(SP == K, "power rows without a pad to clear");
+      if (has) {
+        float* prow = P + f2 * SP;
+        const float hp = a.half_power;
+        const int lim = k1 == 0 ? CP : (k1 <= N1 / 2 ? CH : CF);
 #pragma unroll
-          for (int j = K; j < SP; ++j) prow[j] = 0.0f;  // row pad
+        for (int j = 0; j < CP; ++j) {
+          if (j < lim) {
+            const float2 zm = k1 == 0 ? (j == 0 ? za[0] : pv[j - 1]) : pv[j < CH ? j : CH - 1];
+            const int k = k1 + N1 * j;
+            split_pair<PMODE>(prow + k, prow + (M - k), za[j], zm, tw_at(j, k), hp);
+          }
         }
       }
-      const float hp = a.half_power;
-      // bin k = off + N1*k2 and its mirror M - k, as per-lane bases plus
-      // compile-time (non-negative) offsets
-      float* pk_lo = prow + off_lo;
-      float* pk_hi = prow + off_hi;
-      float* pm_lo = prow + (M - off_lo - N1 * (N2 - 1));
-      float* pm_hi = prow + (M - off_hi - N1 * (N2 - 1));
+    } else {
+      // Unified split schedule: lanes with p != 0 pair bins p + N1*k2 (row p)
+      // with M - that (row N1 - p); lanes with p == 0 own the self-paired rows 0
+      // and N1/2 and walk the same N2 iterations with their rows permuted
+      // (k2 < CA: row 0's pairs, k2 >= CA: row N1/2's), plus one extra pair.
+      // One instruction stream for every lane: no divergent branches.
+      constexpr int CA = N2 / 2 + 1;        // row 0 pairs of the p == 0 lanes
+      constexpr int D2 = N1 / 2 - N1 * CA;  // bin offset of row N1/2's pairs there
+      constexpr int JX = N2 - CA;           // index of row N1/2's extra pair
+      const bool p0 = (p == 0);
+      const int off_lo = p;                 // bin = off + N1*k2 for k2 < CA
+      const int off_hi = p0 ? D2 : p;       // ... and for k2 >= CA
+      float2 za[N2], zb[N2], wv[kTwPrefetch ? N2 + 1 : 1];
+      auto tw_at = [&](int idx, int k) -> float2 {
+        return kTwPrefetch ? wv[kTwPrefetch ? idx : 0] : (kTwLds ? twn_l[k] : a.tw_n[k]);
+      };
+      if (has) {
+        if constexpr (kTwPrefetch) {  // split twiddles load under the DFTs
 #pragma unroll
-      for (int k2 = 0; k2 < N2; ++k2) {
-        float2 zk, zm;
-        if (k2 < CA) {
-          zk = za[k2];
-          zm = p0 ? za[(N2 - k2) % N2] : zb[N2 - 1 - k2];
-        } else {
-          zk = p0 ? zb[k2 - CA] : za[k2];
-          zm = p0 ? zb[N2 - 1 - (k2 - CA)] : zb[N2 - 1 - k2];
+          for (int k2 = 0; k2 < N2; ++k2) wv[k2] = a.tw_n[(k2 < CA ? off_lo : off_hi) + N1 * k2];
+          wv[N2] = a.tw_n[N1 / 2 + N1 * JX];
         }
-        const int k = (k2 < CA ? off_lo : off_hi) + N1 * k2;
-        float* pk = (k2 < CA ? pk_lo : pk_hi) + N1 * k2;
-        float* pm = (k2 < CA ? pm_lo : pm_hi) + N1 * (N2 - 1 - k2);
-        split_pair<PMODE>(pk, pm, zk, zm, tw_at(k2, k), hp);
+        const int ka = p;
+        const int kb = (p == 0) ? N1 / 2 : N1 - p;
+        const float2* ra = Y + f2 * SY + ka * RS;
+        const float2* rb = Y + f2 * SY + kb * RS;
+#pragma unroll
+        for (int j = 0; j < N2; ++j) {
+          za[j] = ra[j];
+          zb[j] = rb[j];
+        }
+        Dft<N2>::run(za);
+        Dft<N2>::run(zb);
       }
-      if (p0) {
-        constexpr int k = N1 / 2 + N1 * JX;
-        split_pair<PMODE>(prow + k, prow + (M - k), zb[JX], zb[N2 - 1 - JX], tw_at(N2, k), hp);
+      // (the twiddle copies have landed: a wave without samples to load in
+      // pass 1 has not waited for its loads yet)
+      if constexpr (kTwLds) __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      // Every read of the exchange buffer is done: stream the mel weights into
+      // LDS behind the power tile (direct global -> LDS loads, 1 KB per wave
+      // instruction, lane l's 16 bytes at l*16), landing while the split runs.
+      for (int c = wave; c < a.w_chunks; c += NW)
+        __builtin_amdgcn_global_load_lds(a.blk_w + c * 256 + lane * 4, P + a.w_lds + c * 256, 16, 0, 0);
+      // the mel stage may read up to kMelTileOverrun - 1 floats past the last
+      // valid frame's row: keep them 0 (in a ragged last tile that is the
+      // unwritten row nvalid, else the slack after the tile)
+      if (tid < kMelTileOverrun) P[nvalid * SP + tid] = 0.0f;
+      if (has) {
+        float* prow = P + f2 * SP;
+        if constexpr (SP > K) {
+          if (p == 0) {
+#pragma unroll
+            for (int j = K; j < SP; ++j) prow[j] = 0.0f;  // row pad
+          }
+        }
+        const float hp = a.half_power;
+        // bin k = off + N1*k2 and its mirror M - k, as per-lane bases plus
+        // compile-time (non-negative) offsets
+        float* pk_lo = prow + off_lo;
+        float* pk_hi = prow + off_hi;
+        float* pm_lo = prow + (M - off_lo - N1 * (N2 - 1));
+        float* pm_hi = prow + (M - off_hi - N1 * (N2 - 1));
+#pragma unroll
+        for (int k2 = 0; k2 < N2; ++k2) {
+          float2 zk, zm;
+          if (k2 < CA) {
+            zk = za[k2];
+            zm = p0 ? za[(N2 - k2) % N2] : zb[N2 - 1 - k2];
+          } else {
+            zk = p0 ? zb[k2 - CA] : za[k2];
+            zm = p0 ? zb[N2 - 1 - (k2 - CA)] : zb[N2 - 1 - k2];
+          }
+          const int k = (k2 < CA ? off_lo : off_hi) + N1 * k2;
+          float* pk = (k2 < CA ? pk_lo : pk_hi) + N1 * k2;
+          float* pm = (k2 < CA ? pm_lo : pm_hi) + N1 * (N2 - 1 - k2);
+          split_pair<PMODE>(pk, pm, zk, zm, tw_at(k2, k), hp);
+        }
+        if (p0) {
+          constexpr int k = N1 / 2 + N1 * JX;
+          split_pair<PMODE>(prow + k, prow + (M - k), zb[JX], zb[N2 - 1 - JX], tw_at(N2, k), hp);
+        }
       }
     }
     __builtin_amdgcn_s_waitcnt(0);  // the weight copies have landed in LDS
@@ -599,31 +665,41 @@ __global__ __launch_bounds__((kThreads<N1, N2>), (kMinWavesPerSimd<N1, N2>)) voi
 }  // namespace
 
 // Kernel entry of one FFT shape for an input type, a power mode (0: p = 2,
-// 1: p = 1, 2: general p) and the tile-copy variant (only for shapes that
-// support it); instantiated in fm_shape_<N1>x<N2>.hip.
+// 1: p = 1, 2: general p), the tile-copy variant (only for shapes that
+// support it) and the second pass's layout (rows: one thread per row, 512
+// threads; else one per pair of rows); instantiated in fm_shape_<N1>x<N2>.hip.
 template <int N1, int N2>
-void* kernel_for(int in_dtype, int pmode, bool copy) {
-  auto pick = [](auto in_tag, auto copy_tag, int pm) -> void* {
+void* kernel_for(int in_dtype, int pmode, bool copy, bool rows) {
+  auto pick = [](auto in_tag, auto copy_tag, auto rows_tag, int pm) -> void* {
     using InT = decltype(in_tag);
     constexpr bool C = decltype(copy_tag)::value;
-    if (pm == 0) return reinterpret_cast<void*>(&mel_forward_kernel<N1, N2, InT, 0, C>);
-    if (pm == 1) return reinterpret_cast<void*>(&mel_forward_kernel<N1, N2, InT, 1, C>);
-    return reinterpret_cast<void*>(&mel_forward_kernel<N1, N2, InT, 2, C>);
+    constexpr bool R = decltype(rows_tag)::value;
+    if (pm == 0) return reinterpret_cast<void*>(&mel_forward_kernel<N1, N2, InT, 0, C, R>);
+    if (pm == 1) return reinterpret_cast<void*>(&mel_forward_kernel<N1, N2, InT, 1, C, R>);
+    return reinterpret_cast<void*>(&mel_forward_kernel<N1, N2, InT, 2, C, R>);
+  };
+  auto by_layout = [&](auto in_tag, auto copy_tag) -> void* {
+    if constexpr (kRowsCapable<N1, N2>) {
+      if (rows) return pick(in_tag, copy_tag, std::true_type{}, pmode);
+    } else {
+      if (rows) return nullptr;
+    }
+    return pick(in_tag, copy_tag, std::false_type{}, pmode);
   };
   using Yes = std::integral_constant<bool, kCopyCapable<N1, N2>>;
   using No = std::false_type;
   if (copy && kCopyCapable<N1, N2>) {
-    if (in_dtype == FM_I16) return pick(int16_t{}, Yes{}, pmode);
-    return pick(float{}, Yes{}, pmode);
+    if (in_dtype == FM_I16) return by_layout(int16_t{}, Yes{});
+    return by_layout(float{}, Yes{});
   }
-  if (in_dtype == FM_I16) return pick(int16_t{}, No{}, pmode);
-  return pick(float{}, No{}, pmode);
+  if (in_dtype == FM_I16) return by_layout(int16_t{}, No{});
+  return by_layout(float{}, No{});
 }
 
 // Shapes built into the library (n_fft/2 = N1 * N2).
 #define FM_FOR_EACH_SHAPE(X) \
   X(8, 4) X(8, 8) X(8, 16) X(8, 25) X(16, 16) X(32, 16) X(32, 32) X(64, 32)
-#define FM_DECLARE_SHAPE(A, B) extern template void* kernel_for<A, B>(int, int, bool);
+#define FM_DECLARE_SHAPE(A, B) extern template void* kernel_for<A, B>(int, int, bool, bool);
 FM_FOR_EACH_SHAPE(FM_DECLARE_SHAPE)
 #undef FM_DECLARE_SHAPE
 

@@ -10,7 +10,6 @@
 #include "fm_backward.h"
 #include "fm_large.h"
 #include "fm_pair.h"
-#include "fm_rows.h"
 
 namespace fm {
 
@@ -36,10 +35,10 @@ void* select_backward_kernel(const Plan& p) {
   return nullptr;
 }
 
-void* select_kernel(const Plan& p, int in_dtype, bool copy) {
+void* select_kernel(const Plan& p, int in_dtype, bool copy, bool rows) {
   const int pm = power_mode(p);
 #define FM_SELECT_SHAPE(A, B) \
-  if (p.fft.n1 == A && p.fft.n2 == B) return kernel_for<A, B>(in_dtype, pm, copy);
+  if (p.fft.n1 == A && p.fft.n2 == B) return kernel_for<A, B>(in_dtype, pm, copy, rows);
   FM_FOR_EACH_SHAPE(FM_SELECT_SHAPE)
 #undef FM_SELECT_SHAPE
   return nullptr;
@@ -54,7 +53,7 @@ void* select_large_kernel(const Plan& p, int in_dtype) {
   return nullptr;
 }
 void* select_rows_kernel(const Plan& p, int in_dtype) {
-  return has_rows_kernel(p.fft.n1, p.fft.n2) ? rows_kernel_for<25>(in_dtype, power_mode(p)) : nullptr;
+  return select_kernel(p, in_dtype, use_tile_copy(p), true);
 }
 void* select_pair_kernel(const Plan& p, int in_dtype) {
   if (p.pair_r == 20) return pair_kernel_for<20>(in_dtype, power_mode(p));
@@ -144,7 +143,7 @@ int upload_plan(Plan& p) {
   }
   // Tiles above 64 KB of LDS need the per-kernel opt-in.
   for (int dt : {FM_F32, FM_I16}) {
-    void* k = select_kernel(p, dt, use_tile_copy(p));
+    void* k = select_kernel(p, dt, use_tile_copy(p), false);
     if (!k) return set_error(FM_E_UNSUPPORTED, "no kernel for this n_fft");
     e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, p.lds_bytes);
     if (e != hipSuccess) return hip_fail(e, "hipFuncSetAttribute");
@@ -164,7 +163,7 @@ int upload_plan(Plan& p) {
   }
   // Resident workgroups per CU for each tile size (registers and LDS).
   p.wg_per_cu.assign(p.tile_max + 1, 1);
-  if (void* k = select_kernel(p, FM_F32, use_tile_copy(p))) {
+  if (void* k = select_kernel(p, FM_F32, use_tile_copy(p), false)) {
     for (int g = (p.tile_max + 1) / 2; g <= p.tile_max; ++g) {
       int n = 0;
       if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k, p.threads, tile_lds_bytes(p, g)) == hipSuccess)
@@ -175,7 +174,7 @@ int upload_plan(Plan& p) {
   if (p.fwd_variant == kFwdRows || p.fwd_variant == kFwdAuto) {
     for (int dt : {FM_F32, FM_I16}) {
       void* k = select_rows_kernel(p, dt);
-      if (!k) return set_error(FM_E_UNSUPPORTED, "no row kernel for this n_fft");
+      if (!k) return set_error(FM_E_UNSUPPORTED, "no row-layout kernel for this n_fft");
       e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, p.lds_bytes);
       if (e != hipSuccess) return hip_fail(e, "hipFuncSetAttribute (rows)");
     }
@@ -183,7 +182,7 @@ int upload_plan(Plan& p) {
     void* k = select_rows_kernel(p, FM_F32);
     for (int g = (p.tile_max + 1) / 2; g <= p.tile_max; ++g) {
       int n = 0;
-      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k, kRowsThreadsHost, tile_lds_bytes(p, g)) == hipSuccess)
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k, kRowsThreads, tile_lds_bytes(p, g)) == hipSuccess)
         p.rows_wg_per_cu[g] = std::max(1, n);
     }
   }
@@ -230,7 +229,7 @@ int launch_forward(const Plan& p, const void* in, int in_dtype, int64_t batch, i
   hipError_t e = hipGetDevice(&cur);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
   if (cur != p.device) return set_error(FM_E_INVAL, "plan belongs to another device than the current one");
-  const FwdChoice c = choose_forward(p, batch, T);
+  const FwdChoice c = choose_forward(p, in_dtype, batch, T);
   if (c.variant == kFwdPaired) {
     if (length > (1 << 29)) return set_error(FM_E_INVAL, "problem too large for one launch (length <= 2^29)");
     const int64_t total = batch * T;
@@ -339,10 +338,10 @@ int launch_forward(const Plan& p, const void* in, int in_dtype, int64_t batch, i
   a.tab_lds = tile_tables_offset(p, G);
   a.twn_lds = tile_twiddles_offset(p, G);
 
-  void* k = rows ? select_rows_kernel(p, in_dtype) : select_kernel(p, in_dtype, use_tile_copy(p));
+  void* k = select_kernel(p, in_dtype, use_tile_copy(p), rows);
   if (!k) return set_error(FM_E_UNSUPPORTED, "no kernel for this n_fft");
   void* args[] = {&a};
-  e = hipLaunchKernel(k, dim3(static_cast<unsigned>(n_tiles)), dim3(rows ? kRowsThreadsHost : p.threads),
+  e = hipLaunchKernel(k, dim3(static_cast<unsigned>(n_tiles)), dim3(rows ? kRowsThreads : p.threads),
                       args, static_cast<size_t>(lds), static_cast<hipStream_t>(stream));
   // (the launch's own status only: hipGetLastError would also report, and
   // clear, an unrelated earlier failure on the caller's thread)

@@ -473,10 +473,11 @@ int build_host_plan(Plan& p, const fm_args& a) {
     }
     if (use) p.fwd_variant = kFwdPaired;
   }
-  // Row-per-thread kernel where it is built (its second pass needs one
-  // thread per row of every frame of a tile): chosen per call by default,
-  // FM_FORWARD=rows or split forces one of the two (for A/B measurements).
-  if (p.fwd_variant == kFwdSplit && has_rows_kernel(fs.n1, fs.n2) && tmax * fs.n1 <= kRowsThreadsHost) {
+  // Row layout of the second pass (one thread per row of every frame of a
+  // tile, so at most kRowsThreads / n1 frames): chosen per call
+  // (choose_forward); FM_FORWARD=rows or split forces one layout (for A/B
+  // measurements).
+  if (p.fwd_variant == kFwdSplit && fs.n1 <= kRowsMaxN1 && tmax * fs.n1 <= kRowsThreads) {
     p.fwd_variant = kFwdAuto;
     if (const char* e = std::getenv("FM_FORWARD")) {
       if (std::string(e) == "rows") p.fwd_variant = kFwdRows;
@@ -541,16 +542,28 @@ int choose_tile(const Plan& p, int64_t batch, int64_t T, int threads, const std:
 
 }  // namespace
 
-// Kernel and tiling of one forward call.  Between the split and the row
-// kernel (FM_FWD_AUTO plans) the row kernel is taken, except for calls whose
-// split tiles fill more than 7/8 of one round of resident workgroups: there
-// every CU runs two tiles whose phases proceed in lockstep, the second pass
-// is bound by the SIMDs' issue rate rather than by one thread's chain of
-// dependent operations, and the split kernel measured about 1% faster
-// (whisper shape, 8 x 480000 samples: 16.78 against 16.98 us per launch).
-// Everywhere else the row kernel measured 1-17% faster (1 x 16000: 6.7
-// against 8.1 us; 32 x 480000: 60.5 against 62.7 us).
-FwdChoice choose_forward(const Plan& p, int64_t batch, int64_t T) {
+// Kernel and tiling of one forward call.  FM_FWD_AUTO plans choose the
+// second pass's layout per call, from same-box A/B measurements of the two
+// (identical outputs):
+// - n_fft 2048 (32 x 32): rows always.  The pair layout leaves half of its
+//   512 threads idle in pass 2 at the 14-17-frame tiles that fit the LDS;
+//   rows measured 8-11% faster from 1 to 128 signals of 220500 samples
+//   (64 signals: 94.1 against 103.1 us).
+// - n_fft 400 (8 x 25): rows, except for float32 calls whose pair-layout
+//   tiles fill more than 7/8 of one round of resident workgroups.  There
+//   every CU runs two tiles whose phases proceed in lockstep, the second
+//   pass is bound by the SIMDs' issue rate rather than by one thread's chain
+//   of dependent operations, and the pair layout measured about 1% faster
+//   (8 x 480000: 16.78 against 16.98 us per launch); elsewhere rows measured
+//   1-17% faster (1 x 16000: 6.7 against 8.1 us; 32 x 480000: 60.5 against
+//   62.7 us), int16 input included at 8 x 480000 (17.10 against 17.42 us).
+// - the other shapes built with both layouts: rows when its workgroups fit
+//   one per compute unit (the latency-bound calls: n_fft 1024, 16 x 32768:
+//   13.7 against 14.5 us; n_fft 512, 1 x 480000: 9.1 against 9.7 us); the
+//   pair layout for larger calls, where its workgroups share the CUs with
+//   fewer barriers per frame (n_fft 1024, 32 x 32768: 17.3 against 24.1 us;
+//   n_fft 256, 4 x 480000: 13.3 against 13.7 us).
+FwdChoice choose_forward(const Plan& p, int in_dtype, int64_t batch, int64_t T) {
   FwdChoice c;
   const int64_t ncu = p.n_cu > 0 ? p.n_cu : 256;
   const int64_t nb = std::max<int64_t>(batch, 1);
@@ -575,16 +588,25 @@ FwdChoice choose_forward(const Plan& p, int64_t batch, int64_t T) {
   c.variant = kFwdSplit;
   c.tile = choose_tile(p, nb, T, p.threads, p.wg_per_cu);
   c.workgroups = batch * ((T + c.tile - 1) / c.tile);
+  if (p.fwd_variant != kFwdRows && p.fwd_variant != kFwdAuto) return c;
+  const int rows_tile = choose_tile(p, nb, T, kRowsThreads, p.rows_wg_per_cu);
+  const int64_t rows_tiles = nb * ((T + rows_tile - 1) / rows_tile);
   bool rows = p.fwd_variant == kFwdRows;
   if (p.fwd_variant == kFwdAuto) {
-    const int64_t tiles = nb * ((T + c.tile - 1) / c.tile);
-    const int64_t slots = ncu * occupancy(p.wg_per_cu, c.tile);
-    rows = !(8 * tiles > 7 * slots && tiles <= slots);
+    if (p.fft.n1 == 32 && p.fft.n2 == 32) {
+      rows = true;
+    } else if (p.fft.n1 == 8 && p.fft.n2 == 25) {
+      const int64_t tiles = nb * ((T + c.tile - 1) / c.tile);
+      const int64_t slots = ncu * occupancy(p.wg_per_cu, c.tile);
+      rows = in_dtype != FM_F32 || !(8 * tiles > 7 * slots && tiles <= slots);
+    } else {
+      rows = rows_tiles <= ncu;
+    }
   }
   if (rows) {
     c.variant = kFwdRows;
-    c.tile = choose_tile(p, nb, T, kRowsThreadsHost, p.rows_wg_per_cu);
-    c.workgroups = batch * ((T + c.tile - 1) / c.tile);
+    c.tile = rows_tile;
+    c.workgroups = batch * ((T + rows_tile - 1) / rows_tile);
   }
   return c;
 }

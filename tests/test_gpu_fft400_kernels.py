@@ -135,8 +135,9 @@ def test_auto_choice_equals_both_kernels(batch, L, monkeypatch):
 
 def test_auto_choice_on_the_device():
     """On the device (256 compute units, two resident tiles of 47 frames per
-    unit) the 8 x 480000 call fills one round and takes the split kernel;
-    one 16000-sample signal and 16 x 480000 take the row kernel."""
+    unit) the float32 8 x 480000 call fills one round and takes the split
+    kernel; its int16 form, one 16000-sample signal and 16 x 480000 take the
+    row kernel."""
     import os
     from stft_mel_spectrogram_amd import MelSpectrogram
     from stft_mel_spectrogram_amd._native import FM_FWD_ROWS, FM_FWD_SPLIT
@@ -149,5 +150,6 @@ def test_auto_choice_on_the_device():
     if n_cu != 256:
         pytest.skip(f"device with {n_cu} compute units")
     assert mel.plan.forward_config(8, 480000) == (FM_FWD_SPLIT, 47, 512)
+    assert mel.plan.forward_config(8, 480000, 1)[0] == FM_FWD_ROWS   # int16 input
     assert mel.plan.forward_config(1, 16000)[0] == FM_FWD_ROWS
     assert mel.plan.forward_config(16, 480000)[0] == FM_FWD_ROWS

@@ -381,10 +381,10 @@ def test_build_rejects_kernels_that_use_scratch():
 
 
 def test_forward_variant_choice(monkeypatch):
-    """n_fft 400 chooses between the split and the row kernel per call unless
-    FM_FORWARD=paired, rows or split (read at plan creation); other sizes up to
-    4096 take the split kernel; n_fft 8192 and 16384 always take the three-pass
-    kernel."""
+    """n_fft 64 ... 2048 choose between the pair and the row layout per call
+    unless FM_FORWARD=rows or split (n_fft 400 also paired) is set at plan
+    creation; n_fft 4096 takes the pair layout; n_fft 8192 and 16384 always
+    take the three-pass kernel."""
     monkeypatch.delenv("FM_FORWARD", raising=False)
     p = N.Plan(device=False, sample_rate=16000, n_fft=400, hop_length=160, n_mels=128)
     assert p.info().forward_variant == N.FM_FWD_AUTO
@@ -392,14 +392,23 @@ def test_forward_variant_choice(monkeypatch):
     p = N.Plan(device=False, sample_rate=16000, n_fft=400, hop_length=160, n_mels=128)
     assert p.info().forward_variant == N.FM_FWD_PAIRED
     p = N.Plan(device=False, sample_rate=16000, n_fft=512, hop_length=160, n_mels=80)
-    assert p.info().forward_variant == N.FM_FWD_SPLIT       # not built for other sizes
+    assert p.info().forward_variant == N.FM_FWD_AUTO        # paired: not built for other sizes
     p = N.Plan(device=False, sample_rate=44100, n_fft=16384, hop_length=4096, n_mels=256,
                f_max=22050.0)
     assert p.info().forward_variant == N.FM_FWD_LARGE
+    monkeypatch.delenv("FM_FORWARD")
+    for n_fft in (64, 128, 256, 512, 1024, 2048):
+        p = N.Plan(device=False, sample_rate=16000, n_fft=n_fft, hop_length=n_fft // 4, n_mels=40)
+        assert p.info().forward_variant == N.FM_FWD_AUTO, n_fft
+    p = N.Plan(device=False, sample_rate=16000, n_fft=4096, hop_length=1024, n_mels=80)
+    assert p.info().forward_variant == N.FM_FWD_SPLIT
     monkeypatch.setenv("FM_FORWARD", "rows")
     p = N.Plan(device=False, sample_rate=16000, n_fft=400, hop_length=160, n_mels=128)
     assert p.info().forward_variant == N.FM_FWD_ROWS and p.info().threads == 512
-    p = N.Plan(device=False, sample_rate=16000, n_fft=1024, hop_length=256, n_mels=80)
+    for n_fft in (64, 128, 256, 512, 1024, 2048):   # the row layout is built up to n1 = 32
+        p = N.Plan(device=False, sample_rate=16000, n_fft=n_fft, hop_length=n_fft // 4, n_mels=40)
+        assert p.info().forward_variant == N.FM_FWD_ROWS and p.info().threads == 512, n_fft
+    p = N.Plan(device=False, sample_rate=16000, n_fft=4096, hop_length=1024, n_mels=80)
     assert p.info().forward_variant == N.FM_FWD_SPLIT and p.info().threads == 256
     monkeypatch.setenv("FM_FORWARD", "split")
     p = N.Plan(device=False, sample_rate=16000, n_fft=400, hop_length=160, n_mels=128)
@@ -419,6 +428,7 @@ def test_forward_config(monkeypatch):
     assert T == 3001
     v, g, wg = p.forward_config(4, 480000)          # 4 x 64 tiles of 47 = one full round
     assert (v, g, wg) == (N.FM_FWD_SPLIT, 47, 256)
+    assert p.forward_config(4, 480000, N.FM_I16)[0] == N.FM_FWD_ROWS   # int16: rows
     v, g, wg = p.forward_config(8, 480000)          # two rounds
     assert v == N.FM_FWD_ROWS and wg == 8 * -(-T // g)
     v, g, wg = p.forward_config(1, 16000)           # fewer tiles than compute units
@@ -436,6 +446,8 @@ def test_forward_config(monkeypatch):
     assert p.forward_config(0, 480000)[2] == 0
     with pytest.raises(N.FmError):
         p.forward_config(-1, 480000)
+    with pytest.raises(N.FmError):
+        p.forward_config(1, 480000, 7)
     monkeypatch.setenv("FM_FORWARD", "split")
     ps = N.Plan(device=False, sample_rate=16000, n_fft=400, hop_length=160, n_mels=128)
     monkeypatch.setenv("FM_FORWARD", "rows")
@@ -444,6 +456,23 @@ def test_forward_config(monkeypatch):
         assert ps.forward_config(batch, 480000)[0] == N.FM_FWD_SPLIT
         assert pr.forward_config(batch, 480000)[0] == N.FM_FWD_ROWS
     monkeypatch.delenv("FM_FORWARD")
+    # n_fft 2048: always rows; the other sizes: rows while its workgroups fit
+    # one per compute unit
+    p2 = N.Plan(device=False, sample_rate=22050, n_fft=2048, hop_length=512, n_mels=128)
+    for batch in (1, 64, 512):
+        assert p2.forward_config(batch, 220500)[0] == N.FM_FWD_ROWS
+    monkeypatch.setenv("FM_FORWARD", "rows")
+    forced = {n: N.Plan(device=False, sample_rate=16000, n_fft=n, hop_length=n // 4, n_mels=40)
+              for n in (64, 256, 512, 1024)}
+    monkeypatch.delenv("FM_FORWARD")
+    for n, pf in forced.items():
+        pa = N.Plan(device=False, sample_rate=16000, n_fft=n, hop_length=n // 4, n_mels=40)
+        for batch, L in ((1, 16000), (1, 480000), (8, 480000), (16, 32768), (64, 32768)):
+            v, g, wg = pa.forward_config(batch, L)
+            _, gr, wgr = pf.forward_config(batch, L)
+            assert (v == N.FM_FWD_ROWS) == (wgr <= 256), (n, batch, L, v, wgr)
+            if v == N.FM_FWD_ROWS:
+                assert (g, wg) == (gr, wgr)
     pl = N.Plan(device=False, sample_rate=44100, n_fft=16384, hop_length=4096, n_mels=256,
                 f_max=22050.0)
     v, g, wg = pl.forward_config(16, 441000)
