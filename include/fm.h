@@ -211,21 +211,20 @@ int64_t fm_out_frames(const fm_plan* plan, int64_t length);
 
 /*
  * fm_forward_config -- how fm_forward runs a call of `batch` signals of
- * `length` samples of type in_dtype (FM_F32 or FM_I16) on this plan, without
- * running it: *variant = the kernel
+ * `length` samples on this plan, without running it: *variant = the kernel
  * (FM_FWD_SPLIT, FM_FWD_ROWS, FM_FWD_PAIRED or FM_FWD_LARGE; never
  * FM_FWD_AUTO), *tile_frames = frames per workgroup tile (PAIRED: frames per
  * chunk at most), *workgroups = workgroups launched (0 for batch 0).  The
  * choice depends on the device the plan was created on (its compute units
  * and the kernels' residency); a host-only plan assumes 256 compute units
  * and one resident workgroup per unit.  Any output pointer may be NULL.
- * Returns FM_OK, FM_E_INVAL (NULL plan, another in_dtype, batch < 0) or the
- * negative code of an invalid length (as fm_out_frames).  Operation-wise this is a host-side
+ * Returns FM_OK, FM_E_INVAL (NULL plan, batch < 0) or the negative code of
+ * an invalid length (as fm_out_frames).  Operation-wise this is a host-side
  * query of the launch geometry behind the pages' one-launch forward pass
  * (flashmel 0.1.0 README "How it works").
  */
-int fm_forward_config(const fm_plan* plan, int in_dtype, int64_t batch, int64_t length,
-                      int* variant, int* tile_frames, int64_t* workgroups);
+int fm_forward_config(const fm_plan* plan, int64_t batch, int64_t length, int* variant,
+                      int* tile_frames, int64_t* workgroups);
 
 /* fm_plan_destroy -- free the plan and its device tables.  NULL is a no-op. */
 int fm_plan_destroy(fm_plan* plan);
@@ -272,9 +271,7 @@ typedef struct fm_plan_info {
  * row's values exchanged between lanes); built for n_fft 64 ... 2048.
  * AUTO (the default for n_fft 64 ... 2048): ROWS or SPLIT chosen per call
  * from the call's size (fm_forward_config reports the choice):
- * n_fft 2048 always ROWS; n_fft 400 ROWS unless the input is float32 and
- * SPLIT's tiles fill more than 7/8 of one round of resident workgroups; the
- * other sizes ROWS when its
+ * n_fft 400 and 2048 always ROWS; the other sizes ROWS when its
  * workgroups number at most the device's compute units.  FM_FORWARD=rows or
  * FM_FORWARD=split at plan creation forces one of them.  ROWS and SPLIT
  * compute the same operations in the same order: their outputs are

@@ -77,7 +77,7 @@ def _load() -> ctypes.CDLL:
         "fm_forward": (I, [P, P, I, I64, I64, P, P]),
         "fm_backward": (I, [P, P, I64, I64, P, P, P]),
         "fm_out_frames": (I64, [P, I64]),
-        "fm_forward_config": (I, [P, I, I64, I64, ctypes.POINTER(I), ctypes.POINTER(I),
+        "fm_forward_config": (I, [P, I64, I64, ctypes.POINTER(I), ctypes.POINTER(I),
                                   ctypes.POINTER(I64)]),
         "fm_plan_destroy": (I, [P]),
         "fm_strerror": (ctypes.c_char_p, [I]),
@@ -157,11 +157,11 @@ class Plan:
     def out_frames(self, length: int) -> int:
         return check(lib.fm_out_frames(self.handle, int(length)))
 
-    def forward_config(self, batch: int, length: int, in_dtype: int = FM_F32):
+    def forward_config(self, batch: int, length: int):
         """(variant, tile_frames, workgroups) that fm_forward takes for this call."""
         v, t, w = ctypes.c_int(), ctypes.c_int(), ctypes.c_int64()
-        check(lib.fm_forward_config(self.handle, int(in_dtype), int(batch), int(length),
-                                    ctypes.byref(v), ctypes.byref(t), ctypes.byref(w)))
+        check(lib.fm_forward_config(self.handle, int(batch), int(length), ctypes.byref(v),
+                                    ctypes.byref(t), ctypes.byref(w)))
         return v.value, t.value, w.value
 
     def tables(self):

@@ -107,15 +107,13 @@ int fm_backward(const fm_plan* plan, const float* in, int64_t batch, int64_t len
   return fm::launch_backward(plan->p, in, batch, length, grad_out, grad_in, stream);
 }
 
-int fm_forward_config(const fm_plan* plan, int in_dtype, int64_t batch, int64_t length,
-                      int* variant, int* tile_frames, int64_t* workgroups) {
+int fm_forward_config(const fm_plan* plan, int64_t batch, int64_t length, int* variant,
+                      int* tile_frames, int64_t* workgroups) {
   if (!plan) return fm::set_error(FM_E_INVAL, "plan must not be NULL");
-  if (in_dtype != FM_F32 && in_dtype != FM_I16)
-    return fm::set_error(FM_E_INVAL, "in_dtype must be FM_F32 or FM_I16");
   if (batch < 0) return fm::set_error(FM_E_INVAL, "batch must be >= 0");
   const int64_t T = fm::out_frames(plan->p, length);
   if (T < 0) return static_cast<int>(T);
-  const fm::FwdChoice c = fm::choose_forward(plan->p, in_dtype, batch, T);
+  const fm::FwdChoice c = fm::choose_forward(plan->p, batch, T);
   if (variant) *variant = c.variant;
   if (tile_frames) *tile_frames = c.tile;
   if (workgroups) *workgroups = c.workgroups;

@@ -125,6 +125,10 @@ constexpr int kFwdAuto = 4;  // ROWS or SPLIT, chosen per call (choose_forward)
 constexpr int kRowsThreads = 512;
 constexpr int kRowsMaxN1 = 32;  // built for n1 <= 32 (fm_kernel.h kRowsCapable)
 constexpr int rows_waves_per_simd(int n1, int n2) { return (n1 <= 16 && n2 <= 25) ? 4 : 2; }
+// Shapes whose pass-1 threads hold all their samples in registers (n1 <= 8)
+// and load two or more frames each can copy a tile's samples into LDS first
+// (fm_kernel.h's COPY variant, chosen per call); the others only gather.
+constexpr bool copy_capable(int n1, int n2) { return n1 <= 8 && n2 >= 8; }
 // Paired kernel: R x R complex points per frame pair (n_fft = R*R); shapes
 // built into the library.
 constexpr int pair_radix_for(int n_fft) { return n_fft == 400 ? 20 : 0; }
@@ -277,15 +281,16 @@ void* pair_kernel_for(int in_dtype, int pmode);
 // (large-FFT kernel entry points, fm_large_*.hip)
 template <int A, int C, int D>
 void* large_kernel_for(int in_dtype, int pmode);
-// How a forward call of `batch` signals of T frames of input type in_dtype
-// runs: kernel variant (never kFwdAuto), frames per tile (paired: per
-// chunk) and workgroups.
+// How a forward call of `batch` signals of T frames runs: kernel variant
+// (never kFwdAuto), frames per tile (paired: per chunk), workgroups, and
+// whether tiles copy their sample span into LDS first (COPY variant).
 struct FwdChoice {
   int variant = kFwdSplit;
   int tile = 1;
   int64_t workgroups = 0;
+  bool copy = false;
 };
-FwdChoice choose_forward(const Plan& p, int in_dtype, int64_t batch, int64_t T);
+FwdChoice choose_forward(const Plan& p, int64_t batch, int64_t T);
 int launch_forward(const Plan& p, const void* in, int in_dtype, int64_t batch,
                    int64_t length, void* out, void* stream);
 int launch_backward(const Plan& p, const float* in, int64_t batch, int64_t length,

@@ -279,11 +279,10 @@ constexpr int kMinWavesPerSimd = ROWS ? rows_waves_per_simd(N1, N2) : ((N1 * N2 
 template <int N1, int N2, bool ROWS>
 constexpr int kThreads = ROWS ? kRowsThreads : threads_for(N1, N2);
 
-// Shapes whose pass-1 threads hold all their samples in registers (N1 <= 8)
-// and load two or more frames each can copy a tile's samples into LDS first
-// (COPY variant, chosen per call); the others only gather.
+// Shapes that can copy a tile's samples into LDS first (COPY variant,
+// chosen per call; copy_capable in fm_internal.h).
 template <int N1, int N2>
-constexpr bool kCopyCapable = (N1 <= 8) && (N2 >= 8);
+constexpr bool kCopyCapable = copy_capable(N1, N2);
 // The row layout is built up to N1 = 32: at N1 = 64 its 512 threads leave
 // each wave 256 registers, which the 64-point first pass overflows.
 template <int N1, int N2>

@@ -17,15 +17,6 @@ namespace {
 
 int power_mode(const Plan& p) { return p.power == 2.0 ? 0 : (p.power == 1.0 ? 1 : 2); }
 
-// Whole-tile sample copy (the COPY kernel variant) for this plan.  The
-// exchange buffer (G x (n_fft/2 + 4) complex) holds a tile's span ((G-1) hop
-// + n_fft samples + 32 bytes of alignment) whenever hop <= n_fft.  The copy
-// must land before any frame is computed, whereas the per-frame gather lets
-// early frames compute while later ones load; measured, the copy pays where
-// frames overlap at least 4 times (each sample gathered 4+ times): n_fft
-// 128/256 at hop n_fft/4 run 6-9% faster, n_fft 400 at hop 160 2% slower.
-bool use_tile_copy(const Plan& p) { return 4 * p.hop <= p.n_fft; }
-
 void* select_backward_kernel(const Plan& p) {
   const int pm = power_mode(p);
 #define FM_SELECT_SHAPE(A, B) \
@@ -51,9 +42,6 @@ void* select_large_kernel(const Plan& p, int in_dtype) {
   FM_FOR_EACH_LARGE_SHAPE(FM_SELECT_LARGE)
 #undef FM_SELECT_LARGE
   return nullptr;
-}
-void* select_rows_kernel(const Plan& p, int in_dtype) {
-  return select_kernel(p, in_dtype, use_tile_copy(p), true);
 }
 void* select_pair_kernel(const Plan& p, int in_dtype) {
   if (p.pair_r == 20) return pair_kernel_for<20>(in_dtype, power_mode(p));
@@ -141,12 +129,19 @@ int upload_plan(Plan& p) {
     p.has_device = true;
     return FM_OK;
   }
-  // Tiles above 64 KB of LDS need the per-kernel opt-in.
+  // Tiles above 64 KB of LDS need the per-kernel opt-in (every variant a
+  // call may choose: gather or tile copy, pair or row layout).
+  const bool rows_built = p.fwd_variant == kFwdRows || p.fwd_variant == kFwdAuto;
   for (int dt : {FM_F32, FM_I16}) {
-    void* k = select_kernel(p, dt, use_tile_copy(p), false);
-    if (!k) return set_error(FM_E_UNSUPPORTED, "no kernel for this n_fft");
-    e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, p.lds_bytes);
-    if (e != hipSuccess) return hip_fail(e, "hipFuncSetAttribute");
+    for (bool copy : {false, true}) {
+      for (bool rows : {false, true}) {
+        if (rows && !rows_built) continue;
+        void* k = select_kernel(p, dt, copy, rows);
+        if (!k) return set_error(FM_E_UNSUPPORTED, "no kernel for this n_fft");
+        e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, p.lds_bytes);
+        if (e != hipSuccess) return hip_fail(e, "hipFuncSetAttribute");
+      }
+    }
   }
   // The paired kernel: LDS opt-in and residency.
   if (p.fwd_variant == kFwdPaired) {
@@ -163,23 +158,17 @@ int upload_plan(Plan& p) {
   }
   // Resident workgroups per CU for each tile size (registers and LDS).
   p.wg_per_cu.assign(p.tile_max + 1, 1);
-  if (void* k = select_kernel(p, FM_F32, use_tile_copy(p), false)) {
+  if (void* k = select_kernel(p, FM_F32, false, false)) {
     for (int g = (p.tile_max + 1) / 2; g <= p.tile_max; ++g) {
       int n = 0;
       if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k, p.threads, tile_lds_bytes(p, g)) == hipSuccess)
         p.wg_per_cu[g] = std::max(1, n);
     }
   }
-  // The row kernel (same LDS layout): opt-in and residency.
-  if (p.fwd_variant == kFwdRows || p.fwd_variant == kFwdAuto) {
-    for (int dt : {FM_F32, FM_I16}) {
-      void* k = select_rows_kernel(p, dt);
-      if (!k) return set_error(FM_E_UNSUPPORTED, "no row-layout kernel for this n_fft");
-      e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, p.lds_bytes);
-      if (e != hipSuccess) return hip_fail(e, "hipFuncSetAttribute (rows)");
-    }
+  // The row layout (same LDS layout): residency.
+  if (rows_built) {
     p.rows_wg_per_cu.assign(p.tile_max + 1, 1);
-    void* k = select_rows_kernel(p, FM_F32);
+    void* k = select_kernel(p, FM_F32, false, true);
     for (int g = (p.tile_max + 1) / 2; g <= p.tile_max; ++g) {
       int n = 0;
       if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k, kRowsThreads, tile_lds_bytes(p, g)) == hipSuccess)
@@ -229,7 +218,7 @@ int launch_forward(const Plan& p, const void* in, int in_dtype, int64_t batch, i
   hipError_t e = hipGetDevice(&cur);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
   if (cur != p.device) return set_error(FM_E_INVAL, "plan belongs to another device than the current one");
-  const FwdChoice c = choose_forward(p, in_dtype, batch, T);
+  const FwdChoice c = choose_forward(p, batch, T);
   if (c.variant == kFwdPaired) {
     if (length > (1 << 29)) return set_error(FM_E_INVAL, "problem too large for one launch (length <= 2^29)");
     const int64_t total = batch * T;
@@ -338,7 +327,7 @@ int launch_forward(const Plan& p, const void* in, int in_dtype, int64_t batch, i
   a.tab_lds = tile_tables_offset(p, G);
   a.twn_lds = tile_twiddles_offset(p, G);
 
-  void* k = select_kernel(p, in_dtype, use_tile_copy(p), rows);
+  void* k = select_kernel(p, in_dtype, c.copy, rows);
   if (!k) return set_error(FM_E_UNSUPPORTED, "no kernel for this n_fft");
   void* args[] = {&a};
   e = hipLaunchKernel(k, dim3(static_cast<unsigned>(n_tiles)), dim3(rows ? kRowsThreads : p.threads),

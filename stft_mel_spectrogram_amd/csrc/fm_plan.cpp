@@ -545,25 +545,32 @@ int choose_tile(const Plan& p, int64_t batch, int64_t T, int threads, const std:
 // Kernel and tiling of one forward call.  FM_FWD_AUTO plans choose the
 // second pass's layout per call, from same-box A/B measurements of the two
 // (identical outputs):
-// - n_fft 2048 (32 x 32): rows always.  The pair layout leaves half of its
-//   512 threads idle in pass 2 at the 14-17-frame tiles that fit the LDS;
-//   rows measured 8-11% faster from 1 to 128 signals of 220500 samples
-//   (64 signals: 94.1 against 103.1 us).
-// - n_fft 400 (8 x 25): rows, except for float32 calls whose pair-layout
-//   tiles fill more than 7/8 of one round of resident workgroups.  There
-//   every CU runs two tiles whose phases proceed in lockstep, the second
-//   pass is bound by the SIMDs' issue rate rather than by one thread's chain
-//   of dependent operations, and the pair layout measured about 1% faster
-//   (8 x 480000: 16.78 against 16.98 us per launch); elsewhere rows measured
-//   1-17% faster (1 x 16000: 6.7 against 8.1 us; 32 x 480000: 60.5 against
-//   62.7 us), int16 input included at 8 x 480000 (17.10 against 17.42 us).
+// - n_fft 400 (8 x 25) and 2048 (32 x 32): rows always.  At n_fft 2048 the
+//   pair layout leaves half of its 512 threads idle in pass 2 at the
+//   14-17-frame tiles that fit the LDS (64 x 220500: 94.1 against 103.1
+//   us).  At n_fft 400 rows measured 1-17% faster at every call size tried
+//   with the tile copy below (8 x 480000: 16.76-16.87 against 17.24-17.31
+//   us; int16: 16.36 against 17.29; 16 x 480000: 30.3 against 32.5; 1 x
+//   16000: 6.6 against 8.1).
 // - the other shapes built with both layouts: rows when its workgroups fit
 //   one per compute unit (the latency-bound calls: n_fft 1024, 16 x 32768:
 //   13.7 against 14.5 us; n_fft 512, 1 x 480000: 9.1 against 9.7 us); the
 //   pair layout for larger calls, where its workgroups share the CUs with
 //   fewer barriers per frame (n_fft 1024, 32 x 32768: 17.3 against 24.1 us;
 //   n_fft 256, 4 x 480000: 13.3 against 13.7 us).
-FwdChoice choose_forward(const Plan& p, int in_dtype, int64_t batch, int64_t T) {
+// Whole-tile sample copy (COPY variant; shapes with copy_capable): the
+// exchange buffer (G x (n_fft/2 + 4) complex) holds a tile's span ((G-1)
+// hop + n_fft samples + 32 bytes of alignment) whenever hop <= n_fft.  The
+// copy must land before any frame is computed, whereas the per-frame gather
+// lets early frames compute while later ones load.  Both layouts copy where
+// frames overlap at least 4 times (n_fft 128/256 at hop n_fft/4: 6-9%
+// faster).  The row layout also copies tiles of 32 frames or more that
+// overlap at least 2.5 times: its four youngest waves, last in issue order,
+// otherwise issue their gathers late and end pass 1 about 1 us after the
+// others (per-wave stamps); a few wide copies avoid that (n_fft 400, 8 x
+// 480000: 16.8 against 17.2 us), while for the small tiles of latency-bound
+// calls it measured the same or slower (1 x 16000: 6.7 against 6.6 us).
+FwdChoice choose_forward(const Plan& p, int64_t batch, int64_t T) {
   FwdChoice c;
   const int64_t ncu = p.n_cu > 0 ? p.n_cu : 256;
   const int64_t nb = std::max<int64_t>(batch, 1);
@@ -585,28 +592,28 @@ FwdChoice choose_forward(const Plan& p, int in_dtype, int64_t batch, int64_t T) 
     c.workgroups = batch * ((T + g - 1) / g);
     return c;
   }
+  auto tile_copy = [&](bool rows, int g) {
+    if (!copy_capable(p.fft.n1, p.fft.n2)) return false;
+    if (4 * p.hop <= p.n_fft) return true;
+    return rows && 5 * p.hop <= 2 * p.n_fft && g >= 32;
+  };
   c.variant = kFwdSplit;
   c.tile = choose_tile(p, nb, T, p.threads, p.wg_per_cu);
   c.workgroups = batch * ((T + c.tile - 1) / c.tile);
+  c.copy = tile_copy(false, c.tile);
   if (p.fwd_variant != kFwdRows && p.fwd_variant != kFwdAuto) return c;
   const int rows_tile = choose_tile(p, nb, T, kRowsThreads, p.rows_wg_per_cu);
   const int64_t rows_tiles = nb * ((T + rows_tile - 1) / rows_tile);
   bool rows = p.fwd_variant == kFwdRows;
   if (p.fwd_variant == kFwdAuto) {
-    if (p.fft.n1 == 32 && p.fft.n2 == 32) {
-      rows = true;
-    } else if (p.fft.n1 == 8 && p.fft.n2 == 25) {
-      const int64_t tiles = nb * ((T + c.tile - 1) / c.tile);
-      const int64_t slots = ncu * occupancy(p.wg_per_cu, c.tile);
-      rows = in_dtype != FM_F32 || !(8 * tiles > 7 * slots && tiles <= slots);
-    } else {
-      rows = rows_tiles <= ncu;
-    }
+    const bool always = (p.fft.n1 == 32 && p.fft.n2 == 32) || (p.fft.n1 == 8 && p.fft.n2 == 25);
+    rows = always || rows_tiles <= ncu;
   }
   if (rows) {
     c.variant = kFwdRows;
     c.tile = rows_tile;
     c.workgroups = batch * ((T + rows_tile - 1) / rows_tile);
+    c.copy = tile_copy(true, rows_tile);
   }
   return c;
 }

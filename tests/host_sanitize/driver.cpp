@@ -41,7 +41,7 @@ static void inspect(fm_plan* h) {
     for (int64_t batch : {0LL, 1LL, 8LL, 64LL}) {
       int v = -1, tile = -1;
       int64_t wg = -1;
-      const int st = fm_forward_config(h, batch % 2 ? FM_I16 : FM_F32, batch, L, &v, &tile, &wg);
+      const int st = fm_forward_config(h, batch, L, &v, &tile, &wg);
       EXPECT((st == FM_OK) == (T > 0));
       if (st != FM_OK) continue;
       EXPECT(v == FM_FWD_SPLIT || v == FM_FWD_ROWS || v == FM_FWD_PAIRED || v == FM_FWD_LARGE);
@@ -51,8 +51,7 @@ static void inspect(fm_plan* h) {
       if (v != FM_FWD_PAIRED) EXPECT(wg == batch * ((T + tile - 1) / tile));
     }
   }
-  EXPECT(fm_forward_config(h, FM_F32, -1, 4000, nullptr, nullptr, nullptr) == FM_E_INVAL);
-  EXPECT(fm_forward_config(h, 7, 1, 4000, nullptr, nullptr, nullptr) == FM_E_INVAL);
+  EXPECT(fm_forward_config(h, -1, 4000, nullptr, nullptr, nullptr) == FM_E_INVAL);
   // a host plan has no device tables: both passes refuse before touching memory
   EXPECT(fm_forward(h, nullptr, FM_F32, 1, 4000, nullptr, nullptr) == FM_E_NODEVICE);
   EXPECT(fm_backward(h, nullptr, 1, 4000, nullptr, nullptr, nullptr) == FM_E_NODEVICE);
@@ -119,7 +118,7 @@ int main() {
   EXPECT(fm_args_default(nullptr) == FM_E_INVAL);
   EXPECT(fm_plan_info_get(nullptr, nullptr) < 0);
   EXPECT(fm_out_frames(nullptr, 100) == FM_E_INVAL);
-  EXPECT(fm_forward_config(nullptr, FM_F32, 1, 100, nullptr, nullptr, nullptr) == FM_E_INVAL);
+  EXPECT(fm_forward_config(nullptr, 1, 100, nullptr, nullptr, nullptr) == FM_E_INVAL);
   EXPECT(fm_plan_destroy(nullptr) == FM_OK);
   for (int s = -7; s <= 1; ++s) EXPECT(fm_strerror(s) != nullptr);
   std::printf("plans built %d, rejected %d, failures %d\n", made, rejected, failures);

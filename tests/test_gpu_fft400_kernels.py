@@ -134,13 +134,11 @@ def test_auto_choice_equals_both_kernels(batch, L, monkeypatch):
 
 
 def test_auto_choice_on_the_device():
-    """On the device (256 compute units, two resident tiles of 47 frames per
-    unit) the float32 8 x 480000 call fills one round and takes the split
-    kernel; its int16 form, one 16000-sample signal and 16 x 480000 take the
-    row kernel."""
+    """On the device (256 compute units) every n_fft-400 call takes the row
+    layout: 8 x 480000 in 47-frame tiles, two per compute unit."""
     import os
     from stft_mel_spectrogram_amd import MelSpectrogram
-    from stft_mel_spectrogram_amd._native import FM_FWD_ROWS, FM_FWD_SPLIT
+    from stft_mel_spectrogram_amd._native import FM_FWD_ROWS
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     if "FM_FORWARD" in os.environ or "FM_TILE_FRAMES" in os.environ:
@@ -149,7 +147,6 @@ def test_auto_choice_on_the_device():
     n_cu = torch.cuda.get_device_properties(0).multi_processor_count
     if n_cu != 256:
         pytest.skip(f"device with {n_cu} compute units")
-    assert mel.plan.forward_config(8, 480000) == (FM_FWD_SPLIT, 47, 512)
-    assert mel.plan.forward_config(8, 480000, 1)[0] == FM_FWD_ROWS   # int16 input
+    assert mel.plan.forward_config(8, 480000) == (FM_FWD_ROWS, 47, 512)
     assert mel.plan.forward_config(1, 16000)[0] == FM_FWD_ROWS
     assert mel.plan.forward_config(16, 480000)[0] == FM_FWD_ROWS

@@ -259,14 +259,18 @@ def test_f16_full_whisper_sampled_rows():
     assert_parity_f16(got[[0, 7]], oracle(x[[0, 7]], **targs), "f16 full whisper rows 0, 7")
 
 
-@pytest.mark.parametrize("n_fft", [128, 256, 400])
+@pytest.mark.parametrize("n_fft,hop,tile", [(128, 32, 0), (256, 64, 0), (400, 100, 0), (400, 160, 40)])
 @pytest.mark.parametrize("dtype", ["f32", "i16"])
-def test_tile_copy_path(n_fft, dtype):
-    """hop = n_fft/4: interior tiles copy their sample span into LDS (edge
-    tiles, and inputs not aligned for it, gather); also from an input that
-    starts 4 (f32) or 2 (int16) bytes into its allocation."""
+def test_tile_copy_path(n_fft, hop, tile, dtype, monkeypatch):
+    """Interior tiles copy their sample span into LDS (edge tiles, and inputs
+    not aligned for it, gather): at hop = n_fft/4 in both layouts of the
+    second pass, and at n_fft 400, hop 160 in the row layout's tiles of 32
+    frames or more (forced here to 40); also from an input that starts 4
+    (f32) or 2 (int16) bytes into its allocation."""
     from stft_mel_spectrogram_amd import MelSpectrogram
     _require_gpu()
+    if tile:
+        monkeypatch.setenv("FM_TILE_FRAMES", str(tile))
     rng = np.random.default_rng(n_fft)
     n = 20_011
     if dtype == "f32":
@@ -275,15 +279,15 @@ def test_tile_copy_path(n_fft, dtype):
     else:
         x = rng.integers(-32768, 32768, size=(3, n)).astype(np.int16)
         tdt = torch.int16
-    targs = dict(sample_rate=16000, n_fft=n_fft, hop_length=n_fft // 4, n_mels=64)
+    targs = dict(sample_rate=16000, n_fft=n_fft, hop_length=hop, n_mels=64)
     ref = oracle(x, **targs)
-    assert_parity(run_gpu(x, **targs), ref, f"copy {dtype} {n_fft}")
+    assert_parity(run_gpu(x, **targs), ref, f"copy {dtype} {n_fft} hop {hop}")
     base = torch.empty(3 * n + 1, dtype=tdt, device="cuda")
     base[1:] = torch.from_numpy(x.reshape(-1)).to("cuda")
     shifted = base[1:].view(3, n)
     y = MelSpectrogram(**targs)(shifted)
     torch.cuda.synchronize()
-    assert_parity(y.cpu().numpy(), ref, f"copy {dtype} {n_fft} misaligned")
+    assert_parity(y.cpu().numpy(), ref, f"copy {dtype} {n_fft} hop {hop} misaligned")
 
 
 @pytest.mark.parametrize("n_fft,tiles", [(400, [1, 7, 16, 17, 32, 33, 48, 49, 64]),

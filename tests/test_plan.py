@@ -416,38 +416,26 @@ def test_forward_variant_choice(monkeypatch):
 
 
 def test_forward_config(monkeypatch):
-    """The per-call choice of an n_fft-400 plan: the row kernel, except for
-    calls whose split tiles fill more than 7/8 of one round of resident
-    workgroups (a host-only plan assumes 256 compute units, one workgroup
-    each); the workgroup count is batch x tiles per signal."""
+    """The per-call choice: n_fft 400 and 2048 take the row layout for every
+    call; the other sizes take it while its workgroups fit one per compute
+    unit (a host-only plan assumes 256 compute units, one workgroup each);
+    the workgroup count is batch x tiles per signal."""
     monkeypatch.delenv("FM_FORWARD", raising=False)
     monkeypatch.delenv("FM_TILE_FRAMES", raising=False)
     p = N.Plan(device=False, sample_rate=16000, n_fft=400, hop_length=160, n_mels=128)
     assert p.info().forward_variant == N.FM_FWD_AUTO and p.info().threads == 256
     T = p.out_frames(480000)
     assert T == 3001
-    v, g, wg = p.forward_config(4, 480000)          # 4 x 64 tiles of 47 = one full round
-    assert (v, g, wg) == (N.FM_FWD_SPLIT, 47, 256)
-    assert p.forward_config(4, 480000, N.FM_I16)[0] == N.FM_FWD_ROWS   # int16: rows
-    v, g, wg = p.forward_config(8, 480000)          # two rounds
-    assert v == N.FM_FWD_ROWS and wg == 8 * -(-T // g)
     v, g, wg = p.forward_config(1, 16000)           # fewer tiles than compute units
     assert v == N.FM_FWD_ROWS and g == 1 and wg == 101
-    for batch in (1, 2, 3, 5, 8, 16, 64):
+    for batch in (1, 2, 3, 4, 5, 8, 16, 64):
         for L in (16000, 160000, 480000):
             v, g, wg = p.forward_config(batch, L)
             T = p.out_frames(L)
-            tiles = batch * -(-T // g)
-            assert wg == tiles and 1 <= g <= p.info().tile_frames
-            vs, gs, ws = N.Plan(device=False, sample_rate=16000, n_fft=400, hop_length=160,
-                                n_mels=128).forward_config(batch, L)
-            split_fill = ws / 256
-            assert (v == N.FM_FWD_SPLIT) == (7 / 8 < split_fill <= 1), (batch, L, v, split_fill)
+            assert v == N.FM_FWD_ROWS and wg == batch * -(-T // g) and 1 <= g <= p.info().tile_frames
     assert p.forward_config(0, 480000)[2] == 0
     with pytest.raises(N.FmError):
         p.forward_config(-1, 480000)
-    with pytest.raises(N.FmError):
-        p.forward_config(1, 480000, 7)
     monkeypatch.setenv("FM_FORWARD", "split")
     ps = N.Plan(device=False, sample_rate=16000, n_fft=400, hop_length=160, n_mels=128)
     monkeypatch.setenv("FM_FORWARD", "rows")
