@@ -125,10 +125,11 @@ constexpr int kFwdAuto = 4;  // ROWS or SPLIT, chosen per call (choose_forward)
 constexpr int kRowsThreads = 512;
 constexpr int kRowsMaxN1 = 32;  // built for n1 <= 32 (fm_kernel.h kRowsCapable)
 constexpr int rows_waves_per_simd(int n1, int n2) { return (n1 <= 16 && n2 <= 25) ? 4 : 2; }
-// Shapes whose pass-1 threads hold all their samples in registers (n1 <= 8)
-// and load two or more frames each can copy a tile's samples into LDS first
-// (fm_kernel.h's COPY variant, chosen per call); the others only gather.
-constexpr bool copy_capable(int n1, int n2) { return n1 <= 8 && n2 >= 8; }
+// Shapes with a whole-tile sample copy (fm_kernel.h's COPY variant, chosen
+// per call): those whose pass-1 threads hold all their samples in registers
+// (n1 <= 8) and load two or more frames each, and those with larger n1,
+// whose copy serves tiles of at most one frame per pass-1 thread.
+constexpr bool copy_capable(int n1, int n2) { return n1 > 8 || n2 >= 8; }
 // Paired kernel: R x R complex points per frame pair (n_fft = R*R); shapes
 // built into the library.
 constexpr int pair_radix_for(int n_fft) { return n_fft == 400 ? 20 : 0; }
@@ -178,6 +179,7 @@ struct Plan {
   FftShape fft{0, 0};
   int tile_max = 0;      // most frames a workgroup tile may hold
   int tile_override = 0; // FM_TILE_FRAMES, for sweeps (0: chosen per call)
+  int copy_override = -1; // FM_TILE_COPY=0|1, for A/B measurements (-1: chosen per call)
   int threads = 256;
   int lds_bytes = 0;     // dynamic LDS of a tile of tile_max frames
   // mel blocks in wave order: wave w takes blocks [wave_beg[w], wave_beg[w+1])

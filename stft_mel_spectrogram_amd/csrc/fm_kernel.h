@@ -404,38 +404,46 @@ __global__ __launch_bounds__((kThreads<N1, N2, ROWS>), (kMinWavesPerSimd<N1, N2,
           yrow[k1 * RS] = cmul(v[k1], kHoist ? twv[kHoist ? k1 : 0]
                                              : (kTabLds ? tab_tw[N2 * k1 + n2] : a.tw_m[N2 * k1 + n2]));
       };
-      if constexpr (kHoist) {
-        // Every frame of this thread is loaded before any is computed.  A
-        // tile whose samples lie inside the signal first copies its whole
-        // contiguous span into LDS with 16-byte direct loads (a few wide
-        // instructions per wave instead of one 8-byte gather per sample
-        // pair, and each sample read once instead of n_fft/hop times); the
-        // copy aliases the exchange buffer, so every thread takes its
-        // samples into registers before the first Y store.  Edge tiles
-        // gather through the padding index map.
-        constexpr int RMAX = (64 + SLOTS - 1) / SLOTS;
-        constexpr int ES = static_cast<int>(sizeof(InT));
-        float2 sb[RMAX][N1];
+      // Whole-tile sample copy (COPY variants): a tile whose samples lie
+      // inside the signal first copies its whole contiguous span into LDS
+      // with 16-byte direct loads (a few wide instructions per wave instead
+      // of one 8-byte gather per sample pair, and each sample read once
+      // instead of n_fft/hop times); the copy aliases the exchange buffer, so
+      // every thread takes its samples into registers before the first Y
+      // store.  Edge tiles gather through the padding index map.  Returns
+      // the LDS address of the tile's first sample once every copy (and any
+      // earlier direct load into LDS) has landed, or null where the tile
+      // gathers; the choice depends on the tile only (uniform across the
+      // workgroup, so are the barriers).
+      constexpr int ES = static_cast<int>(sizeof(InT));
+      auto span_copy = [&]() -> const unsigned char* {
         const int base0 = t0 * a.hop - a.pad;  // first sample of the tile
         const int span = (nvalid - 1) * a.hop + NF;
         const uintptr_t xa = reinterpret_cast<uintptr_t>(x);
         const uintptr_t b_lo = xa + static_cast<uintptr_t>(static_cast<long long>(base0) * ES);
         const uintptr_t g_lo = b_lo & ~static_cast<uintptr_t>(15);
         const uintptr_t g_hi = (b_lo + static_cast<uintptr_t>(span) * ES + 15) & ~static_cast<uintptr_t>(15);
-        const bool copy = COPY && base0 >= 0 && base0 + span <= L && g_lo >= xa &&
+        const bool copy = base0 >= 0 && base0 + span <= L && g_lo >= xa &&
                           g_hi <= xa + static_cast<uintptr_t>(L) * ES && (b_lo % (2 * ES)) == 0 &&
-                          (a.hop % 2) == 0;  // wave-uniform: depends on the tile only
-        if (copy) {
-          const int n16 = static_cast<int>((g_hi - g_lo) >> 4);
-          for (int c = wave; c * 64 < n16; c += NW) {
-            const int q = c * 64 + lane;
-            if (q < n16)
-              __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(g_lo + static_cast<uintptr_t>(q) * 16),
-                                               lds + c * 1024, 16, 0, 0);
-          }
-          __builtin_amdgcn_s_waitcnt(0);  // the copies have landed
-          __syncthreads();
-          const unsigned char* r0 = lds + (b_lo - g_lo);
+                          (a.hop % 2) == 0;
+        if (!copy) return nullptr;
+        const int n16 = static_cast<int>((g_hi - g_lo) >> 4);
+        for (int c = wave; c * 64 < n16; c += NW) {
+          const int q = c * 64 + lane;
+          if (q < n16)
+            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(g_lo + static_cast<uintptr_t>(q) * 16),
+                                             lds + c * 1024, 16, 0, 0);
+        }
+        __builtin_amdgcn_s_waitcnt(0);  // the copies have landed
+        __syncthreads();
+        return lds + (b_lo - g_lo);
+      };
+      if constexpr (kHoist) {
+        // Every frame of this thread is loaded before any is computed.
+        constexpr int RMAX = (64 + SLOTS - 1) / SLOTS;
+        float2 sb[RMAX][N1];
+        const unsigned char* r0 = COPY ? span_copy() : nullptr;
+        if (r0) {
           if (p1) {
 #pragma unroll
             for (int r = 0; r < RMAX; ++r) {
@@ -458,26 +466,40 @@ __global__ __launch_bounds__((kThreads<N1, N2, ROWS>), (kMinWavesPerSimd<N1, N2,
           for (int r = 0; r < RMAX; ++r)
             if (slot + SLOTS * r < nvalid) compute(slot + SLOTS * r, sb[r]);
         }
-      } else if constexpr (kTabLds) {
-        // the tables land in LDS while the first frame's samples load
-        for (int c = wave; c < M / 64; c += NW)
-          __builtin_amdgcn_global_load_lds(reinterpret_cast<const float*>(a.win2) + c * 256 + lane * 4,
-                                           lds + a.tab_lds + c * 1024, 16, 0, 0);
-        float2 s0[N1];
-        if (p1 && slot < nvalid) fetch(slot, s0);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (p1) {
+      } else {
+        // the tables land in LDS while the samples load
+        if constexpr (kTabLds) {
+          for (int c = wave; c < M / 64; c += NW)
+            __builtin_amdgcn_global_load_lds(reinterpret_cast<const float*>(a.win2) + c * 256 + lane * 4,
+                                             lds + a.tab_lds + c * 1024, 16, 0, 0);
+        }
+        // COPY: tiles of at most one frame per pass-1 thread copy their span
+        const unsigned char* r0 = (COPY && nvalid <= SLOTS) ? span_copy() : nullptr;
+        if (r0) {
+          float2 s0[N1];
+          if (p1 && slot < nvalid) {
+#pragma unroll
+            for (int n1 = 0; n1 < N1; ++n1) s0[n1] = lds_pair_raw<InT>(r0 + (slot * a.hop + 2 * (N2 * n1 + n2)) * ES);
+          }
+          __syncthreads();  // the copy is consumed: Y may overwrite it
+          if (p1 && slot < nvalid) compute(slot, s0);
+        } else if constexpr (kTabLds) {
+          float2 s0[N1];
+          if (p1 && slot < nvalid) fetch(slot, s0);
+          __builtin_amdgcn_s_waitcnt(0);
+          __syncthreads();
+          if (p1) {
+            for (int f = slot; f < nvalid; f += SLOTS) {
+              if (f != slot) fetch(f, s0);
+              compute(f, s0);
+            }
+          }
+        } else if (p1) {
           for (int f = slot; f < nvalid; f += SLOTS) {
-            if (f != slot) fetch(f, s0);
+            float2 s0[N1];
+            fetch(f, s0);
             compute(f, s0);
           }
-        }
-      } else if (p1) {
-        for (int f = slot; f < nvalid; f += SLOTS) {
-          float2 s0[N1];
-          fetch(f, s0);
-          compute(f, s0);
         }
       }
     }

@@ -494,6 +494,10 @@ int build_host_plan(Plan& p, const fm_args& a) {
     int v = std::atoi(e);
     if (v >= 1 && v <= tmax) p.tile_override = v;
   }
+  if (const char* e = std::getenv("FM_TILE_COPY")) {
+    if (std::string(e) == "0") p.copy_override = 0;
+    if (std::string(e) == "1") p.copy_override = 1;
+  }
   return FM_OK;
 }
 
@@ -570,6 +574,13 @@ int choose_tile(const Plan& p, int64_t batch, int64_t T, int threads, const std:
 // others (per-wave stamps); a few wide copies avoid that (n_fft 400, 8 x
 // 480000: 16.8 against 17.2 us), while for the small tiles of latency-bound
 // calls it measured the same or slower (1 x 16000: 6.7 against 6.6 us).
+// Shapes with n1 > 8 (one frame per pass-1 thread) copy where frames
+// overlap at least 2.5 times, in calls with more workgroups than compute
+// units (n_fft 4096, 4 x 1323000: 76.5 against 91.2 us; n_fft 2048, 64 x
+// 220500: 91.3 against 94.5 us; n_fft 1024, 64 x 32768: 28.9 against 29.8
+// us; n_fft 512 at hop 160, 32 x 480000: 57.4 against 59.1 us); in smaller
+// calls the copy's wait before any frame is computed costs more than it
+// saves (n_fft 2048, 8 x 220500: 18.3 against 17.7 us).
 FwdChoice choose_forward(const Plan& p, int64_t batch, int64_t T) {
   FwdChoice c;
   const int64_t ncu = p.n_cu > 0 ? p.n_cu : 256;
@@ -594,6 +605,8 @@ FwdChoice choose_forward(const Plan& p, int64_t batch, int64_t T) {
   }
   auto tile_copy = [&](bool rows, int g) {
     if (!copy_capable(p.fft.n1, p.fft.n2)) return false;
+    if (p.copy_override >= 0) return p.copy_override == 1;
+    if (p.fft.n1 > 8) return 5 * p.hop <= 2 * p.n_fft && nb * ((T + g - 1) / g) > ncu;
     if (4 * p.hop <= p.n_fft) return true;
     return rows && 5 * p.hop <= 2 * p.n_fft && g >= 32;
   };

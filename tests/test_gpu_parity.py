@@ -259,18 +259,23 @@ def test_f16_full_whisper_sampled_rows():
     assert_parity_f16(got[[0, 7]], oracle(x[[0, 7]], **targs), "f16 full whisper rows 0, 7")
 
 
-@pytest.mark.parametrize("n_fft,hop,tile", [(128, 32, 0), (256, 64, 0), (400, 100, 0), (400, 160, 40)])
+@pytest.mark.parametrize("n_fft,hop,tile", [(128, 32, 0), (256, 64, 0), (400, 100, 0), (400, 160, 40),
+                                            (512, 128, 0), (1024, 256, 0), (2048, 512, 0), (4096, 1024, 0)])
 @pytest.mark.parametrize("dtype", ["f32", "i16"])
 def test_tile_copy_path(n_fft, hop, tile, dtype, monkeypatch):
     """Interior tiles copy their sample span into LDS (edge tiles, and inputs
     not aligned for it, gather): at hop = n_fft/4 in both layouts of the
-    second pass, and at n_fft 400, hop 160 in the row layout's tiles of 32
-    frames or more (forced here to 40); also from an input that starts 4
-    (f32) or 2 (int16) bytes into its allocation."""
+    second pass, at n_fft 400, hop 160 in the row layout's tiles of 32
+    frames or more (forced here to 40), and for n_fft 512 ... 4096 (one frame
+    per pass-1 thread), whose calls copy only when they have more workgroups
+    than compute units (forced here with FM_TILE_COPY=1); also from an input
+    that starts 4 (f32) or 2 (int16) bytes into its allocation."""
     from stft_mel_spectrogram_amd import MelSpectrogram
     _require_gpu()
     if tile:
         monkeypatch.setenv("FM_TILE_FRAMES", str(tile))
+    if n_fft >= 512:
+        monkeypatch.setenv("FM_TILE_COPY", "1")
     rng = np.random.default_rng(n_fft)
     n = 20_011
     if dtype == "f32":
