@@ -12,11 +12,18 @@
 // LDS exchange between them:
 //   pass 1, one thread per (frame, n2):  N1-point DFT over n1 of
 //           z[N2*n1 + n2], times exp(-2*pi*i*n2*k1/M), stored Y[f][k1][n2];
-//   pass 2, one thread per (frame, pair of k1): N2-point DFTs of Y[f][k1][.]
-//           for k1 and N1-k1, giving Z[k1 + N1*k2] and the mirrored bins
-//           Z[M - k] in the same thread, so the split into the real spectrum
+//   pass 2, in one of two layouts (template flag ROWS, chosen per call):
+//           pair layout, one thread per (frame, pair of k1): N2-point DFTs
+//           of Y[f][k1][.] for k1 and N1-k1, giving Z[k1 + N1*k2] and the
+//           mirrored bins Z[M - k] in the same thread; row layout (512
+//           threads), one thread per (frame, k1): one N2-point DFT, the
+//           mirrored row's values fetched from the partner lane.  Either way
+//           the split into the real spectrum
 //              X[k] = (Z[k] + conj Z[M-k]) - i W_N^k (Z[k] - conj Z[M-k])
-//           (window pre-scaled by 1/2) and |X|^p need no further exchange.
+//           (window pre-scaled by 1/2) and |X|^p follow with the same
+//           operations in the same order.
+// A tile's samples are gathered per frame or, in the COPY variants, copied
+// into LDS as one contiguous span first (also chosen per call).
 // The power tile P[f][k] (odd frame stride n_fft/2+1) reuses the exchange
 // buffer (rows of N2 complex values, padded to N2 + 1 where N2 is even;
 // frames 4 complex values apart beyond their rows).  The mel projection is
