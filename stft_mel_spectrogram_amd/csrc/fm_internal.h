@@ -64,6 +64,15 @@ constexpr bool tables_in_lds(int n1, int m) {
 constexpr int kMelStageMinFrames = 33;
 // Staging floats per wave: 16 filters x (64 frames + 1 pad).
 constexpr int kMelStageFloats = 16 * 65;
+// Staging floats of a wide tile of `frames` frames, all waves: the pair
+// layout stages on its kMelWaves mel waves; the row layout spreads the mel
+// blocks over its 8 waves, each staging 16 filters x (16 nfb + 1) floats for
+// the tile's nfb 16-frame column groups.
+constexpr long mel_stage_floats(bool rows, int frames) {
+  return frames < kMelStageMinFrames ? 0
+         : rows ? 8L * 16 * (16 * ((frames + 15) / 16) + 1)
+                : static_cast<long>(kMelWaves) * kMelStageFloats;
+}
 
 // LDS strides of a tile, padded against bank conflicts.  The exchange
 // buffer Y holds a frame's n1 rows of n2 complex values (row k1 written by
@@ -245,18 +254,18 @@ void default_args(fm_args* a);
 // LDS layout of a tile of `frames` frames: the FFT exchange buffer (during
 // pass 1 followed by the pass-1 tables where tables_in_lds), which later
 // holds the power tile, its zeroed overrun floats, (from float
-// tile_weights_offset) the mel block weights and, for wide tiles, the 4
-// waves' output staging areas right after them; behind all of that (byte
-// tile_twiddles_offset), where twiddles_in_lds, the split twiddles W_N^k,
-// k < n_fft/2.
+// tile_weights_offset) the mel block weights and, for wide tiles, the mel
+// waves' output staging areas right after them (mel_stage_floats: `rows` is
+// the second pass's layout); behind all of that (byte tile_twiddles_offset),
+// where twiddles_in_lds, the split twiddles W_N^k, k < n_fft/2.
 int tile_exchange_bytes(const Plan& p, int frames);
 int tile_weights_offset(const Plan& p, int frames);
 int tile_tables_offset(const Plan& p, int frames);  // bytes; pass-1 tables in LDS
 // Split twiddles W_N^k copied into LDS (complex FFTs of 1024 points or more;
 // smaller ones hold them in registers or read them from L2).
 constexpr bool twiddles_in_lds(int m) { return m >= 1024; }
-int tile_twiddles_offset(const Plan& p, int frames);  // bytes; split twiddles in LDS
-int tile_lds_bytes(const Plan& p, int frames);
+int tile_twiddles_offset(const Plan& p, int frames, bool rows);  // bytes; split twiddles in LDS
+int tile_lds_bytes(const Plan& p, int frames, bool rows);
 
 // LDS layout of a backward pass of `chunk` frames (floats from the start):
 // the exchange buffer (frame stride n_fft/2 + 4 complex), which after the

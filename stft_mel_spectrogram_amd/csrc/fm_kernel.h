@@ -106,13 +106,13 @@ using f32x4 = float __attribute__((ext_vector_type(4)));
 template <int KS, int NFB, bool STAGE, bool GW, typename OT>
 __device__ __forceinline__ void mel_blocks(const float* P, const float* WL, float* stg, int G,
                                            int nvalid, int lane, OT* obase, int n_frames,
-                                           int n_mels, CInt* blk, int bb, int be) {
+                                           int n_mels, CInt* blk, int bb, int be, int bstep) {
   constexpr int U = kMelStepGroup;
   const int fr = lane & 15, kq = lane >> 4;
   int roff[NFB];
 #pragma unroll
   for (int f = 0; f < NFB; ++f) roff[f] = min(16 * f + fr, nvalid - 1) * KS + kq;
-  for (int bi = bb; bi < be; ++bi) {
+  for (int bi = bb; bi < be; bi += bstep) {
     const int kb = blk[4 * bi], ks = blk[4 * bi + 1], woff = blk[4 * bi + 2],
               mel0 = blk[4 * bi + 3];
     f32x4 acc[NFB];
@@ -661,25 +661,34 @@ __global__ __launch_bounds__((kThreads<N1, N2, ROWS>), (kMinWavesPerSimd<N1, N2,
     //      16-frame column groups across the tile ---------------------------
     {
       CInt* tbl = (CInt*)(a.mel_tbl);  // address-space cast: scalar loads
-      // (the blocks are shared out over the first kMelWaves waves)
-      const int bb = wave < kMelWaves ? tbl[wave] : 0, be = wave < kMelWaves ? tbl[wave + 1] : 0;
-      const long long obase = static_cast<long long>(b) * a.n_mels * a.n_frames + t0;  // element offset
+      // The plan shares the blocks out over kMelWaves waves.  The row layout
+      // spreads them over its 8 waves once the tile has two or more column
+      // groups: waves w and w + 4 take alternate blocks of wave w's share
+      // (8 x 480000 at n_fft 400: 16.2 against 16.7 us; 1-frame tiles stay
+      // on 4 waves).
       const int nfb = (G + 15) >> 4;
+      const bool mel8 = ROWS && nfb >= 2;
+      const int mw = mel8 ? (wave & 3) : wave;
+      const int bb = mw < kMelWaves ? tbl[mw] + (mel8 ? (wave >> 2) : 0) : 0;
+      const int be = mw < kMelWaves ? tbl[mw + 1] : 0;
+      const int bstep = mel8 ? 2 : 1;
+      const long long obase = static_cast<long long>(b) * a.n_mels * a.n_frames + t0;  // element offset
       CInt* blk = tbl + 8;
       constexpr bool GW = M >= kMelGlobalWeightsFrom;
       const float* WL = GW ? a.blk_w : P + a.w_lds;
-      float* stg = P + a.w_lds + a.w_chunks * 256 + wave * kMelStageFloats;
+      // this wave's staging area (mel_stage_floats)
+      float* stg = P + a.w_lds + a.w_chunks * 256 + wave * (ROWS ? 16 * (16 * nfb + 1) : kMelStageFloats);
       static_assert(kMelStageMinFrames == 33, "staging is chosen for 3 and 4 column groups");
       switch (nfb) {
 #define FM_MEL_CALL(NFB, STAGE)                                                                \
   if (a.out_f16)                                                                              \
     mel_blocks<SP, NFB, STAGE, GW, _Float16>(P, WL, stg, G, nvalid, lane,                      \
                                          static_cast<_Float16*>(a.out) + obase, a.n_frames,   \
-                                         a.n_mels, blk, bb, be);                              \
+                                         a.n_mels, blk, bb, be, bstep);                       \
   else                                                                                        \
     mel_blocks<SP, NFB, STAGE, GW, float>(P, WL, stg, G, nvalid, lane,                        \
                                       static_cast<float*>(a.out) + obase, a.n_frames, a.n_mels, \
-                                      blk, bb, be)
+                                      blk, bb, be, bstep)
         case 1: FM_MEL_CALL(1, false); break;
         case 2: FM_MEL_CALL(2, false); break;
         case 3: FM_MEL_CALL(3, true); break;

@@ -161,7 +161,7 @@ int upload_plan(Plan& p) {
   if (void* k = select_kernel(p, FM_F32, false, false)) {
     for (int g = (p.tile_max + 1) / 2; g <= p.tile_max; ++g) {
       int n = 0;
-      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k, p.threads, tile_lds_bytes(p, g)) == hipSuccess)
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k, p.threads, tile_lds_bytes(p, g, false)) == hipSuccess)
         p.wg_per_cu[g] = std::max(1, n);
     }
   }
@@ -171,7 +171,7 @@ int upload_plan(Plan& p) {
     void* k = select_kernel(p, FM_F32, false, true);
     for (int g = (p.tile_max + 1) / 2; g <= p.tile_max; ++g) {
       int n = 0;
-      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k, kRowsThreads, tile_lds_bytes(p, g)) == hipSuccess)
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k, kRowsThreads, tile_lds_bytes(p, g, true)) == hipSuccess)
         p.rows_wg_per_cu[g] = std::max(1, n);
     }
   }
@@ -296,7 +296,7 @@ int launch_forward(const Plan& p, const void* in, int in_dtype, int64_t batch, i
   const int64_t tiles = (T + G - 1) / G;
   if (length > (1 << 29) || tiles * batch > INT32_MAX)
     return set_error(FM_E_INVAL, "problem too large for one launch (length <= 2^29, tiles < 2^31)");
-  const int lds = tile_lds_bytes(p, G);
+  const int lds = tile_lds_bytes(p, G, rows);
   const int64_t n_tiles = tiles * batch;
 
   KArgs a;
@@ -325,7 +325,7 @@ int launch_forward(const Plan& p, const void* in, int in_dtype, int64_t batch, i
   a.w_lds = tile_weights_offset(p, G);
   a.out_f16 = p.out_dtype == FM_F16 ? 1 : 0;
   a.tab_lds = tile_tables_offset(p, G);
-  a.twn_lds = tile_twiddles_offset(p, G);
+  a.twn_lds = tile_twiddles_offset(p, G, rows);
 
   void* k = select_kernel(p, in_dtype, c.copy, rows);
   if (!k) return set_error(FM_E_UNSUPPORTED, "no kernel for this n_fft");

@@ -108,18 +108,18 @@ int tile_weights_offset(const Plan& p, int frames) {
 
 int tile_tables_offset(const Plan& p, int frames) { return tile_exchange_bytes(p, frames); }
 
-int tile_twiddles_offset(const Plan& p, int frames) {
+int tile_twiddles_offset(const Plan& p, int frames, bool rows) {
   const long tables = tables_in_lds(p.fft.n1, p.n_fft / 2) ? 16L * (p.n_fft / 2) : 0;
   const long pass1 = tile_tables_offset(p, frames) + tables;
-  const long stage = frames >= kMelStageMinFrames ? kMelWaves * kMelStageFloats : 0;
+  const long stage = mel_stage_floats(rows, frames);
   const long weights = p.w_in_lds ? static_cast<long>(p.blk_w.size()) : 0;
   const long after_fft = (static_cast<long>(tile_weights_offset(p, frames)) + weights + stage) * 4;
   return static_cast<int>((std::max<long>(pass1, after_fft) + 15) / 16 * 16);
 }
 
-int tile_lds_bytes(const Plan& p, int frames) {
+int tile_lds_bytes(const Plan& p, int frames, bool rows) {
   const long twiddles = twiddles_in_lds(p.n_fft / 2) ? 8L * (p.n_fft / 2) : 0;
-  return static_cast<int>(tile_twiddles_offset(p, frames) + twiddles);
+  return static_cast<int>(tile_twiddles_offset(p, frames, rows) + twiddles);
 }
 
 int pair_lds_layout(int r, int chunk, int n_mels, long w_floats, int* span_b, int* w_f) {
@@ -441,11 +441,13 @@ int build_host_plan(Plan& p, const fm_args& a) {
   // the power tile plus the mel weights) must fit the 160 KB of a CU.
   int tmax = 64;
   while (tmax > 1 && tmax * (fs.n1 / 2) > p.threads) --tmax;
-  while (tmax > 1 && tile_lds_bytes(p, tmax) > 160 * 1024) --tmax;
-  if (tile_lds_bytes(p, tmax) > 160 * 1024)
+  // (either layout of the second pass)
+  auto lds_of = [&](int g) { return std::max(tile_lds_bytes(p, g, false), tile_lds_bytes(p, g, true)); };
+  while (tmax > 1 && lds_of(tmax) > 160 * 1024) --tmax;
+  if (lds_of(tmax) > 160 * 1024)
     return set_error(FM_E_UNSUPPORTED, "mel filterbank too large for the LDS of one tile");
   p.tile_max = tmax;
-  p.lds_bytes = tile_lds_bytes(p, tmax);
+  p.lds_bytes = lds_of(tmax);
   // backward passes: as many frames as the kernel's registers and the LDS
   // allow
   int cmax = bwd_chunk_cap(fs.n1, fs.n2, kBwdThreads);
