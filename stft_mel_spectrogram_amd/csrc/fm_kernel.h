@@ -662,12 +662,14 @@ __global__ __launch_bounds__((kThreads<N1, N2, ROWS>), (kMinWavesPerSimd<N1, N2,
     {
       CInt* tbl = (CInt*)(a.mel_tbl);  // address-space cast: scalar loads
       // The plan shares the blocks out over kMelWaves waves.  The row layout
-      // spreads them over its 8 waves once the tile has two or more column
-      // groups: waves w and w + 4 take alternate blocks of wave w's share
-      // (8 x 480000 at n_fft 400: 16.2 against 16.7 us; 1-frame tiles stay
-      // on 4 waves).
+      // spreads them over its 8 waves (waves w and w + 4 take alternate
+      // blocks of wave w's share) once the tile has two or more column
+      // groups, or there are blocks for every wave (8 x 480000 at n_fft 400:
+      // 16.2 against 16.7 us; 1 x 480000: 7.9 against 8.2 us; n_fft 2048,
+      // 64 x 220500: 89.9 against 90.8 us; with 5 blocks and 1-column tiles
+      // the same or slower).
       const int nfb = (G + 15) >> 4;
-      const bool mel8 = ROWS && nfb >= 2;
+      const bool mel8 = ROWS && (nfb >= 2 || tbl[kMelWaves] >= 2 * kMelWaves);
       const int mw = mel8 ? (wave & 3) : wave;
       const int bb = mw < kMelWaves ? tbl[mw] + (mel8 ? (wave >> 2) : 0) : 0;
       const int be = mw < kMelWaves ? tbl[mw + 1] : 0;
