@@ -28,7 +28,12 @@ struct MelBlock {
                    // filter of the block is empty)
   int32_t w_off;   // offset of the block's weights (floats)
   int32_t mel0;    // first filter of the block
+  int32_t s_hi = 0; // steps from s_hi on hold only zero weights
 };
+// A block's step word in the device table: ksteps, and s_hi in bits 20 and
+// up (the kernel may skip the products of the steps from s_hi on).  ksteps
+// <= (n_fft/2 + 1 + 3)/4 + 3 <= 516 for n_fft <= 4096: ten bits.
+constexpr int32_t mel_step_word(int ksteps, int s_hi) { return ksteps | (s_hi << 20); }
 constexpr int kMelBlock = 16;
 constexpr int kMaxMelBlocks = 16;  // n_mels <= 256
 constexpr int kMelWaves = 4;       // waves of a workgroup

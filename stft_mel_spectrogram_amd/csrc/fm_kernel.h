@@ -62,7 +62,7 @@ struct KArgs {
   int pad_mode;
   float half_power;     // power / 2
   int vec_ok;           // interior tiles may use paired (2-sample) loads
-  const int* mel_tbl;   // wave_beg[5], 3 pad, then {kb, ksteps, w_off, mel0} per block
+  const int* mel_tbl;   // wave_beg[5], 3 pad, then {kb, step word (mel_step_word), w_off, mel0} per block
   const float* blk_w;   // block weights, 64 per 4-bin step (MFMA A-operand order)
   int w_chunks;         // block weights / 256 (copied to LDS in 1 KB chunks;
                         // 0 when the shape reads them from global memory)
@@ -113,41 +113,61 @@ __device__ __forceinline__ void mel_blocks(const float* P, const float* WL, floa
 #pragma unroll
   for (int f = 0; f < NFB; ++f) roff[f] = min(16 * f + fr, nvalid - 1) * KS + kq;
   for (int bi = bb; bi < be; bi += bstep) {
-    const int kb = blk[4 * bi], ks = blk[4 * bi + 1], woff = blk[4 * bi + 2],
+    // Step word (mel_step_word): ksteps, and s_hi, from which on every step
+    // holds only zero weights.  The wide-tile (STAGE) and global-weight (GW)
+    // instantiations stop at s_hi: they skip the groups past it and, in the
+    // group holding it, the products of the zero steps (8 x 480000 at n_fft
+    // 400: 16.3 against 16.6 us; n_fft 4096, 4 x 1323000: 74.6 against 76.5
+    // us).  The others run every padded step: with the branches the
+    // narrow-tile loop measured 3-7% slower (n_fft 2048: 97.2 against 91.1).
+    constexpr bool kSkip = STAGE || GW;
+    const int kb = blk[4 * bi], sw = blk[4 * bi + 1], woff = blk[4 * bi + 2],
               mel0 = blk[4 * bi + 3];
+    const int s_end = kSkip ? sw >> 20 : (sw & 1023);
     f32x4 acc[NFB];
 #pragma unroll
     for (int f = 0; f < NFB; ++f) acc[f] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     const float* pb = P + kb;
     const float* wl = WL + woff + lane;
-    auto group = [&](const float* av, const float* pg) {
+    auto group = [&](const float* av, const float* pg, int nu) {
       float bv[U][NFB];
 #pragma unroll
       for (int u = 0; u < U; ++u)
 #pragma unroll
         for (int f = 0; f < NFB; ++f) bv[u][f] = pg[roff[f] + 4 * u];
+      if (!kSkip || nu >= U) {
 #pragma unroll
-      for (int u = 0; u < U; ++u)
+        for (int u = 0; u < U; ++u)
 #pragma unroll
-        for (int f = 0; f < NFB; ++f)
-          acc[f] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[u], bv[u][f], acc[f], 0, 0, 0);
+          for (int f = 0; f < NFB; ++f)
+            acc[f] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[u], bv[u][f], acc[f], 0, 0, 0);
+      } else {
+#pragma unroll
+        for (int u = 0; u < U - 1; ++u) {
+          if (u < nu) {  // wave-uniform
+#pragma unroll
+            for (int f = 0; f < NFB; ++f)
+              acc[f] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[u], bv[u][f], acc[f], 0, 0, 0);
+          }
+        }
+      }
     };
     if constexpr (GW) {
       constexpr int CH = kMelGlobalChunk;
-      for (int s0 = 0; s0 < ks; s0 += CH, pb += 4 * CH, wl += 64 * CH) {
+      for (int s0 = 0; s0 < s_end; s0 += CH, pb += 4 * CH, wl += 64 * CH) {
         float av[CH];  // one chunk of weights in flight at once (slack covers the tail)
 #pragma unroll
         for (int j = 0; j < CH; ++j) av[j] = wl[64 * j];
 #pragma unroll
         for (int g = 0; g < CH / U; ++g)
-          if (s0 + U * g < ks) group(av + U * g, pb + 4 * U * g);
+          if (s0 + U * g < s_end) group(av + U * g, pb + 4 * U * g, s_end - s0 - U * g);
       }
     } else {
-      for (int s0 = 0; s0 < ks; s0 += U, pb += 4 * U, wl += 64 * U) {
+      for (int s0 = 0; s0 < s_end; s0 += U, pb += 4 * U, wl += 64 * U) {
         float av[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) av[u] = wl[64 * u];
-        group(av, pb);
+        group(av, pb, s_end - s0);
       }
     }
     if constexpr (STAGE) {

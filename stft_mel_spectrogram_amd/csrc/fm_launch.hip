@@ -89,7 +89,7 @@ int upload_plan(Plan& p) {
   for (int w = 0; w <= kMelWaves; ++w) tbl[w] = p.wave_beg[w];
   for (size_t j = 0; j < p.blocks.size(); ++j) {
     tbl[8 + 4 * j + 0] = p.blocks[j].kb;
-    tbl[8 + 4 * j + 1] = p.blocks[j].ksteps;
+    tbl[8 + 4 * j + 1] = mel_step_word(p.blocks[j].ksteps, p.blocks[j].s_hi);
     tbl[8 + 4 * j + 2] = p.blocks[j].w_off;
     tbl[8 + 4 * j + 3] = p.blocks[j].mel0;
   }

@@ -377,8 +377,10 @@ int build_host_plan(Plan& p, const fm_args& a) {
             const int m = m0 + l % kMelBlock, k = b.kb + 4 * s + l / kMelBlock;
             if (m >= n_mels) continue;
             const MelRow& r = p.rows[m];
-            if (r.len > 0 && k >= r.first && k < r.first + r.len)
+            if (r.len > 0 && k >= r.first && k < r.first + r.len) {
               bw[j][static_cast<size_t>(s) * 64 + l] = p.mel_w[r.off + k - r.first];
+              b.s_hi = std::max(b.s_hi, s + 1);
+            }
           }
       }
       blk[j] = b;
