@@ -240,6 +240,15 @@ __device__ __forceinline__ float padded_sample_raw(const T* x, int i, int L, int
   if constexpr (std::is_same<T, int16_t>::value) return static_cast<float>(x[j]);
   else return x[j];
 }
+// The same sample in the input's own type (int16 unscaled), 0 at a
+// constant-zero position.
+template <typename T>
+__device__ __forceinline__ T padded_value(const T* x, int i, int L, int zpad, int mode) {
+  const int e = padded_index(i + zpad, L + 2 * zpad, mode);
+  const int j = e - zpad;
+  if (e < 0 || static_cast<unsigned>(j) >= static_cast<unsigned>(L)) return T(0);
+  return x[j];
+}
 // Two consecutive samples from the LDS copy of a tile (int16 unscaled).
 template <typename T>
 __device__ __forceinline__ float2 lds_pair_raw(const unsigned char* p);
@@ -431,39 +440,68 @@ __global__ __launch_bounds__((kThreads<N1, N2, ROWS>), (kMinWavesPerSimd<N1, N2,
           yrow[k1 * RS] = cmul(v[k1], kHoist ? twv[kHoist ? k1 : 0]
                                              : (kTabLds ? tab_tw[N2 * k1 + n2] : a.tw_m[N2 * k1 + n2]));
       };
-      // Whole-tile sample copy (COPY variants): a tile whose samples lie
-      // inside the signal first copies its whole contiguous span into LDS
-      // with 16-byte direct loads (a few wide instructions per wave instead
-      // of one 8-byte gather per sample pair, and each sample read once
-      // instead of n_fft/hop times); the copy aliases the exchange buffer, so
-      // every thread takes its samples into registers before the first Y
-      // store.  Edge tiles gather through the padding index map.  Returns
-      // the LDS address of the tile's first sample once every copy (and any
-      // earlier direct load into LDS) has landed, or null where the tile
-      // gathers; the choice depends on the tile only (uniform across the
-      // workgroup, so are the barriers).
+      // Whole-tile sample copy (COPY variants): the tile's contiguous span
+      // of samples is copied into LDS first, with 16-byte direct loads (a
+      // few wide instructions per wave instead of one 8-byte gather per
+      // sample pair, and each sample read once instead of n_fft/hop times).
+      // The loads take the 16-byte chunks that lie inside the signal; the
+      // span's other positions (the padding at a signal's ends, and the
+      // partial chunks next to them) are filled one sample each through the
+      // padding index map, so edge tiles copy too.  The copy aliases the
+      // exchange buffer, so every thread takes its samples into registers
+      // before the first Y store.  Returns the LDS address of the tile's
+      // first (padded) sample once the copy is complete, or null where the
+      // input is not aligned for paired reads (then the tile gathers); the
+      // choice depends on the tile only (uniform across the workgroup, so are
+      // the barriers).
       constexpr int ES = static_cast<int>(sizeof(InT));
       auto span_copy = [&]() -> const unsigned char* {
         const int base0 = t0 * a.hop - a.pad;  // first sample of the tile
         const int span = (nvalid - 1) * a.hop + NF;
-        const uintptr_t xa = reinterpret_cast<uintptr_t>(x);
-        const uintptr_t b_lo = xa + static_cast<uintptr_t>(static_cast<long long>(base0) * ES);
-        const uintptr_t g_lo = b_lo & ~static_cast<uintptr_t>(15);
-        const uintptr_t g_hi = (b_lo + static_cast<uintptr_t>(span) * ES + 15) & ~static_cast<uintptr_t>(15);
-        const bool copy = base0 >= 0 && base0 + span <= L && g_lo >= xa &&
-                          g_hi <= xa + static_cast<uintptr_t>(L) * ES && (b_lo % (2 * ES)) == 0 &&
-                          (a.hop % 2) == 0;
-        if (!copy) return nullptr;
-        const int n16 = static_cast<int>((g_hi - g_lo) >> 4);
+        const long long xa = static_cast<long long>(reinterpret_cast<uintptr_t>(x));
+        const long long lo = xa + static_cast<long long>(base0) * ES;  // may lie before x[0]
+        const long long hi = lo + static_cast<long long>(span) * ES;
+        const long long sig_hi = xa + static_cast<long long>(L) * ES;
+        if (lo % (2 * ES) != 0 || (a.hop % 2) != 0) return nullptr;
+        // whole 16-byte chunks inside the signal: rounded outwards where that
+        // stays inside it, else inwards
+        long long g_lo = (lo > xa ? lo : xa) & ~15LL;
+        if (g_lo < xa) g_lo += 16;
+        long long g_hi = ((hi < sig_hi ? hi : sig_hi) + 15) & ~15LL;
+        if (g_hi > sig_hi) g_hi -= 16;
+        const long long v0 = lo & ~15LL;  // the global address LDS byte 0 stands for
+        const int n16 = g_hi > g_lo ? static_cast<int>((g_hi - g_lo) >> 4) : 0;
+        unsigned char* dst = lds + (g_lo - v0);
         for (int c = wave; c * 64 < n16; c += NW) {
           const int q = c * 64 + lane;
           if (q < n16)
-            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(g_lo + static_cast<uintptr_t>(q) * 16),
-                                             lds + c * 1024, 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(g_lo + static_cast<long long>(q) * 16),
+                                             dst + c * 1024, 16, 0, 0);
         }
-        __builtin_amdgcn_s_waitcnt(0);  // the copies have landed
+        // positions [0, qa) and [qb, span) of the span are filled per sample
+        const int qa = n16 ? (g_lo > lo ? static_cast<int>((g_lo - lo) / ES) : 0) : span;
+        const int qb = n16 ? (g_hi < hi ? static_cast<int>((g_hi - lo) / ES) : span) : span;
+        const int nfill = qa + (span - qb);
+        unsigned char* r0 = lds + (lo - v0);
+        constexpr int KF = 4;
+        for (int q0 = 0; q0 < nfill; q0 += KF * NT) {
+          InT fv[KF];
+#pragma unroll
+          for (int k = 0; k < KF; ++k) {
+            const int idx = q0 + k * NT + tid;
+            const int q = idx < qa ? idx : qb + (idx - qa);
+            fv[k] = idx < nfill ? padded_value(x, base0 + q, L, a.zpad, a.pad_mode) : InT(0);
+          }
+#pragma unroll
+          for (int k = 0; k < KF; ++k) {
+            const int idx = q0 + k * NT + tid;
+            const int q = idx < qa ? idx : qb + (idx - qa);
+            if (idx < nfill) *reinterpret_cast<InT*>(r0 + q * ES) = fv[k];
+          }
+        }
+        __builtin_amdgcn_s_waitcnt(0);  // the copies and fills have landed
         __syncthreads();
-        return lds + (b_lo - g_lo);
+        return r0;
       };
       if constexpr (kHoist) {
         // Every frame of this thread is loaded before any is computed.

@@ -609,6 +609,9 @@ FwdChoice choose_forward(const Plan& p, int64_t batch, int64_t T) {
   }
   auto tile_copy = [&](bool rows, int g) {
     if (!copy_capable(p.fft.n1, p.fft.n2)) return false;
+    // the exchange buffer must hold the span ((g - 1) hop + n_fft samples of
+    // up to 4 bytes, and up to 30 bytes of 16-byte rounding), also when forced
+    if ((static_cast<long>(g - 1) * p.hop + p.n_fft) * 4 + 32 > tile_exchange_bytes(p, g)) return false;
     if (p.copy_override >= 0) return p.copy_override == 1;
     if (p.fft.n1 > 8) return 5 * p.hop <= 2 * p.n_fft && nb * ((T + g - 1) / g) > ncu;
     if (4 * p.hop <= p.n_fft) return true;
