@@ -182,8 +182,9 @@ __device__ __forceinline__ void mel_blocks(const float* P, const float* WL, floa
       __builtin_amdgcn_wave_barrier();
       const int nrow = min(16, n_mels - mel0);
       const bool st = lane < nvalid && lane < 16 * NFB;
+      const int col = lane < 16 * NFB ? lane : 0;  // lanes past the tile's columns stay in the stage
       for (int m = 0; m < nrow; ++m) {
-        const float v = stg[m * PITCH + lane];
+        const float v = stg[m * PITCH + col];
         // output is written once and never re-read here: streaming stores
         if (st) __builtin_nontemporal_store(static_cast<OT>(v), obase + static_cast<long long>(mel0 + m) * n_frames + lane);
       }

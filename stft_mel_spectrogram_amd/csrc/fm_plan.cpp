@@ -568,23 +568,17 @@ int choose_tile(const Plan& p, int64_t batch, int64_t T, int threads, const std:
 //   n_fft 256, 4 x 480000: 13.3 against 13.7 us).
 // Whole-tile sample copy (COPY variant; shapes with copy_capable): the
 // exchange buffer (G x (n_fft/2 + 4) complex) holds a tile's span ((G-1)
-// hop + n_fft samples + 32 bytes of alignment) whenever hop <= n_fft.  The
-// copy must land before any frame is computed, whereas the per-frame gather
-// lets early frames compute while later ones load.  Both layouts copy where
-// frames overlap at least 4 times (n_fft 128/256 at hop n_fft/4: 6-9%
-// faster).  The row layout also copies tiles of 32 frames or more that
-// overlap at least 2.5 times: its four youngest waves, last in issue order,
-// otherwise issue their gathers late and end pass 1 about 1 us after the
-// others (per-wave stamps); a few wide copies avoid that (n_fft 400, 8 x
-// 480000: 16.8 against 17.2 us), while for the small tiles of latency-bound
-// calls it measured the same or slower (1 x 16000: 6.7 against 6.6 us).
-// Shapes with n1 > 8 (one frame per pass-1 thread) copy where frames
-// overlap at least 2.5 times, in calls with more workgroups than compute
-// units (n_fft 4096, 4 x 1323000: 76.5 against 91.2 us; n_fft 2048, 64 x
-// 220500: 91.3 against 94.5 us; n_fft 1024, 64 x 32768: 28.9 against 29.8
-// us; n_fft 512 at hop 160, 32 x 480000: 57.4 against 59.1 us); in smaller
-// calls the copy's wait before any frame is computed costs more than it
-// saves (n_fft 2048, 8 x 220500: 18.3 against 17.7 us).
+// hop + n_fft samples + 32 bytes of alignment) whenever hop <= n_fft.  Every
+// tile copies, the first and last of a signal too (their padding filled per
+// sample), wherever frames overlap or touch (hop <= n_fft; with gaps between
+// frames the span would carry samples no frame reads).  Against the
+// per-frame gather (same box, us per launch): n_fft 400, 8 x 480000: 15.9
+// against 16.6; int16: 14.7 against 16.5; 1 x 16000: 6.5 against 6.8; 1 x
+// 480000: 7.5 against 7.9; n_fft 1024, 8 x 32768: 8.2 against 12.7; n_fft
+// 2048, 8 x 220500: 13.9 against 17.5; 64 x 220500: 83.4 against 93.7;
+// n_fft 512, 1 x 480000: 6.9 against 9.0; n_fft 4096, 1 x 1323000: 20.6
+// against 34.7.  (While edge tiles gathered, the copy lost in calls of few
+// workgroups: there the gathering edge tiles set the launch's length.)
 FwdChoice choose_forward(const Plan& p, int64_t batch, int64_t T) {
   FwdChoice c;
   const int64_t ncu = p.n_cu > 0 ? p.n_cu : 256;
@@ -607,20 +601,18 @@ FwdChoice choose_forward(const Plan& p, int64_t batch, int64_t T) {
     c.workgroups = batch * ((T + g - 1) / g);
     return c;
   }
-  auto tile_copy = [&](bool rows, int g) {
+  auto tile_copy = [&](int g) {
     if (!copy_capable(p.fft.n1, p.fft.n2)) return false;
     // the exchange buffer must hold the span ((g - 1) hop + n_fft samples of
     // up to 4 bytes, and up to 30 bytes of 16-byte rounding), also when forced
     if ((static_cast<long>(g - 1) * p.hop + p.n_fft) * 4 + 32 > tile_exchange_bytes(p, g)) return false;
     if (p.copy_override >= 0) return p.copy_override == 1;
-    if (p.fft.n1 > 8) return 5 * p.hop <= 2 * p.n_fft && nb * ((T + g - 1) / g) > ncu;
-    if (4 * p.hop <= p.n_fft) return true;
-    return rows && 5 * p.hop <= 2 * p.n_fft && g >= 32;
+    return p.hop <= p.n_fft;
   };
   c.variant = kFwdSplit;
   c.tile = choose_tile(p, nb, T, p.threads, p.wg_per_cu);
   c.workgroups = batch * ((T + c.tile - 1) / c.tile);
-  c.copy = tile_copy(false, c.tile);
+  c.copy = tile_copy(c.tile);
   if (p.fwd_variant != kFwdRows && p.fwd_variant != kFwdAuto) return c;
   const int rows_tile = choose_tile(p, nb, T, kRowsThreads, p.rows_wg_per_cu);
   const int64_t rows_tiles = nb * ((T + rows_tile - 1) / rows_tile);
@@ -633,7 +625,7 @@ FwdChoice choose_forward(const Plan& p, int64_t batch, int64_t T) {
     c.variant = kFwdRows;
     c.tile = rows_tile;
     c.workgroups = batch * ((T + rows_tile - 1) / rows_tile);
-    c.copy = tile_copy(true, rows_tile);
+    c.copy = tile_copy(rows_tile);
   }
   return c;
 }
