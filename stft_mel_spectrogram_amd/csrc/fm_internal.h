@@ -67,6 +67,21 @@ constexpr bool tables_in_lds(int n1, int m) {
 // per-wave LDS staging area (one contiguous store per row, rows long enough
 // to cover whole cache lines); narrower tiles store the MFMA results directly.
 constexpr int kMelStageMinFrames = 33;
+// Tiles of at least this many frames project on the vector units instead
+// (mel_valu in fm_kernel.h; Plan::mel_valu): one frame per lane, the filters
+// in quads of 4 consecutive filters, each quad's runs padded to its longest
+// run, weights read as scalars.  Quads are cut into kMelShares contiguous
+// shares of about equal cost; a workgroup of w waves gives each wave 8/w
+// shares.  The threshold is measured (same box, us per launch, against the
+// matrix-core blocks): n_fft 400, 8 x 480000 (47-frame tiles): 14.5 against
+// 15.9; 4 x 480000 (24 frames): 12.1 against 13.4; n_fft 256, 8 x 480000:
+// 21.0 against 22.1; 1 x 16000 (26 frames): 6.5 against 6.7; below 17
+// frames half a wave's lanes or more idle and the wider filters of the
+// larger FFTs lose (n_fft 2048, 16-frame tiles: 97.6 against 83.7; n_fft
+// 400, 1 x 480000, 12 frames: 8.4 against 7.6).
+constexpr int kMelValuMinFrames = 17;
+constexpr int kMelShares = 8;
+constexpr int kQuadHdr = 8;  // int32 per quad: 4 start bins, run length, weight offset (float4s), 2 pad
 // Staging floats per wave: 16 filters x (64 frames + 1 pad).
 constexpr int kMelStageFloats = 16 * 65;
 // Staging floats of a wide tile of `frames` frames, all waves: the pair
@@ -201,6 +216,14 @@ struct Plan {
   int wave_beg[kMelWaves + 1] = {};
   std::vector<float> blk_w;            // block weights (see MelBlock)
   bool w_in_lds = true;                // weights staged in LDS (else read from L2)
+  // vector-unit projection of wide tiles (kMelValuMinFrames): quads of 4
+  // filters; quad q's header at quad_hdr[kQuadHdr*q], its weights at
+  // quad_w[4 * (header offset) ...], 4 per step
+  std::vector<int32_t> quad_hdr;
+  std::vector<float> quad_w;
+  int quad_beg[kMelShares + 1] = {};  // share s: quads [quad_beg[s], quad_beg[s+1])
+  int mel_valu = 1;                   // 0 (FM_MEL=mfma): every tile projects on the matrix cores
+  int mel_valu_from = kMelValuMinFrames;  // tiles of at least this many frames use the vector units
   int nnz = 0, w_max = 0;
   // host tables (float32 after one rounding from float64)
   std::vector<float> window;  // [n_fft], unscaled
@@ -225,6 +248,8 @@ struct Plan {
   const void* d_mel_w = nullptr;  // float[nnz]
   const void* d_mel_tbl = nullptr;    // int32[8 + 4*n_blocks]: wave_beg, pad, blocks
   const void* d_blk_w = nullptr;      // float[blk_w.size()]
+  const void* d_quad = nullptr;       // int32[16 + kQuadHdr*quads]: quad_beg, pad, headers
+  const void* d_quad_w = nullptr;     // float[quad_w.size()]
   // forward kernel variant: FM_FWD_SPLIT (fm_kernel.h: complex FFT of n_fft/2
   // points and the real split, one tile per workgroup), FM_FWD_ROWS
   // (fm_kernel.h with one second-pass thread per row), FM_FWD_AUTO

@@ -70,6 +70,9 @@ struct KArgs {
   int out_f16;          // 1: the output is float16
   int tab_lds;          // LDS byte offset of the pass-1 tables (tables_in_lds)
   int twn_lds;          // LDS byte offset of the split twiddles (n_fft/2 > 256)
+  int mel_valu;         // 1: this call's tiles project on the vector units (mel_valu)
+  const int* quad_tbl;  // quad_beg[kMelShares + 1], pad to 16, then kQuadHdr int32 per quad
+  const float* quad_w;  // quad weights, 4 per step
 };
 
 namespace {
@@ -201,6 +204,49 @@ __device__ __forceinline__ void mel_blocks(const float* P, const float* WL, floa
             if (mrow + r < n_mels) obase[static_cast<long long>(mrow + r) * n_frames + frame] = static_cast<OT>(acc[f][r]);
         }
       }
+    }
+  }
+}
+
+// Mel projection of a wide tile on the vector units.  Lane l computes frame
+// l's outputs (lanes past the last valid frame read that frame's row and
+// store nothing).  Each wave walks its quads of 4 consecutive filters: per
+// step of a quad the four weights are one scalar load and each filter's
+// power value one LDS read, so the quad's four multiply-add chains run side
+// by side; a filter's run is padded with zero weights to the quad's length
+// and starts early enough to end inside the frame's bins.  Each filter's
+// row of the tile then leaves with one streaming store (the tile's frames
+// are contiguous in the output).  Against the matrix-core blocks this does
+// the filterbank's nonzero products only (n_fft 400, 128 filters: 395 per
+// frame, where the 16-filter blocks spend 4096).
+template <int KS, typename OT>
+__device__ __forceinline__ void mel_valu(const float* P, CInt* qt, CFloat* qw, int nvalid, int lane,
+                                         OT* obase, int n_frames, int n_mels, int qb, int qe) {
+  const float* prow = P + min(lane, nvalid - 1) * KS;
+  const bool st = lane < nvalid;
+  for (int q = qb; q < qe; ++q) {
+    CInt* h = qt + 16 + kQuadHdr * q;
+    const int L = h[4];
+    CFloat* w = qw + 4 * h[5];
+    const float* p0 = prow + h[0];
+    const float* p1 = prow + h[1];
+    const float* p2 = prow + h[2];
+    const float* p3 = prow + h[3];
+    float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
+#pragma unroll 4
+    for (int i = 0; i < L; ++i) {
+      a0 = fmaf(w[4 * i + 0], p0[i], a0);
+      a1 = fmaf(w[4 * i + 1], p1[i], a1);
+      a2 = fmaf(w[4 * i + 2], p2[i], a2);
+      a3 = fmaf(w[4 * i + 3], p3[i], a3);
+    }
+    if (st) {
+      const int m = 4 * q;  // < n_mels
+      OT* o = obase + static_cast<long long>(m) * n_frames + lane;
+      __builtin_nontemporal_store(static_cast<OT>(a0), o);
+      if (m + 1 < n_mels) __builtin_nontemporal_store(static_cast<OT>(a1), o + n_frames);
+      if (m + 2 < n_mels) __builtin_nontemporal_store(static_cast<OT>(a2), o + 2 * n_frames);
+      if (m + 3 < n_mels) __builtin_nontemporal_store(static_cast<OT>(a3), o + 3 * n_frames);
     }
   }
 }
@@ -728,12 +774,27 @@ __global__ __launch_bounds__((kThreads<N1, N2, ROWS>), (kMinWavesPerSimd<N1, N2,
       // 64 x 220500: 89.9 against 90.8 us; with 5 blocks and 1-column tiles
       // the same or slower).
       const int nfb = (G + 15) >> 4;
+      const long long obase = static_cast<long long>(b) * a.n_mels * a.n_frames + t0;  // element offset
+      if (a.mel_valu) {
+        // the vector units, wave w taking its 8/NW shares of the filter
+        // quads (a tile's frames, at most 64, fit one wave's lanes)
+        static_assert(kMelShares % NW == 0, "whole shares per wave");
+        CInt* qt = (CInt*)(a.quad_tbl);
+        CFloat* qw = (CFloat*)(a.quad_w);
+        const int qb = qt[wave * (kMelShares / NW)], qe = qt[(wave + 1) * (kMelShares / NW)];
+        if (a.out_f16)
+          mel_valu<SP, _Float16>(P, qt, qw, nvalid, lane, static_cast<_Float16*>(a.out) + obase, a.n_frames,
+                                 a.n_mels, qb, qe);
+        else
+          mel_valu<SP, float>(P, qt, qw, nvalid, lane, static_cast<float*>(a.out) + obase, a.n_frames,
+                              a.n_mels, qb, qe);
+        return;
+      }
       const bool mel8 = ROWS && (nfb >= 2 || tbl[kMelWaves] >= 2 * kMelWaves);
       const int mw = mel8 ? (wave & 3) : wave;
       const int bb = mw < kMelWaves ? tbl[mw] + (mel8 ? (wave >> 2) : 0) : 0;
       const int be = mw < kMelWaves ? tbl[mw + 1] : 0;
       const int bstep = mel8 ? 2 : 1;
-      const long long obase = static_cast<long long>(b) * a.n_mels * a.n_frames + t0;  // element offset
       CInt* blk = tbl + 8;
       constexpr bool GW = M >= kMelGlobalWeightsFrom;
       const float* WL = GW ? a.blk_w : P + a.w_lds;

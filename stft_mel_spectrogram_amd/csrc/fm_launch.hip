@@ -73,7 +73,9 @@ int upload_plan(Plan& p) {
   const size_t o_tbl = o_w + al(static_cast<size_t>(p.nnz > 0 ? p.nnz : 1) * sizeof(float));
   const size_t o_bw = o_tbl + al((8 + 4 * p.blocks.size()) * sizeof(int32_t));
   const size_t o_taps = o_bw + al(std::max<size_t>(p.blk_w.size(), 1) * sizeof(float));
-  const size_t total = o_taps + al(p.taps.size() * sizeof(BinTap));
+  const size_t o_quad = o_taps + al(p.taps.size() * sizeof(BinTap));
+  const size_t o_qw = o_quad + al((16 + p.quad_hdr.size()) * sizeof(int32_t));
+  const size_t total = o_qw + al(std::max<size_t>(p.quad_w.size(), 1) * sizeof(float));
   // the kernels copy win2 and tw_p as one block of 16*M bytes
   if (o_twp != o_win + static_cast<size_t>(M) * sizeof(float2) && tables_in_lds(p.fft.n1, M))
     return set_error(FM_E_HIP, "internal: pass-1 tables are not contiguous");
@@ -95,6 +97,10 @@ int upload_plan(Plan& p) {
   }
   std::copy(p.blk_w.begin(), p.blk_w.end(), reinterpret_cast<float*>(host.data() + o_bw));
   std::copy(p.taps.begin(), p.taps.end(), reinterpret_cast<BinTap*>(host.data() + o_taps));
+  int32_t* qt = reinterpret_cast<int32_t*>(host.data() + o_quad);
+  for (int sh = 0; sh <= kMelShares; ++sh) qt[sh] = p.quad_beg[sh];
+  std::copy(p.quad_hdr.begin(), p.quad_hdr.end(), qt + 16);
+  std::copy(p.quad_w.begin(), p.quad_w.end(), reinterpret_cast<float*>(host.data() + o_qw));
   void* d = nullptr;
   e = hipMalloc(&d, total);
   if (e != hipSuccess) return set_error(FM_E_NOMEM, std::string("hipMalloc: ") + hipGetErrorString(e));
@@ -114,6 +120,8 @@ int upload_plan(Plan& p) {
   p.d_mel_tbl = base + o_tbl;
   p.d_blk_w = base + o_bw;
   p.d_taps = base + o_taps;
+  p.d_quad = base + o_quad;
+  p.d_quad_w = base + o_qw;
   // The large-FFT kernel: LDS opt-in and residency (no other kernel).
   if (p.fwd_variant == kFwdLarge) {
     for (int dt : {FM_F32, FM_I16}) {
@@ -321,8 +329,12 @@ int launch_forward(const Plan& p, const void* in, int in_dtype, int64_t batch, i
              ((p.pad_left + p.zpad) % 2 == 0);
   a.mel_tbl = static_cast<const int*>(p.d_mel_tbl);
   a.blk_w = static_cast<const float*>(p.d_blk_w);
-  a.w_chunks = p.w_in_lds ? static_cast<int>(p.blk_w.size() / 256) : 0;
+  // wide tiles project on the vector units (no block weights to copy)
+  a.mel_valu = (p.mel_valu && G >= p.mel_valu_from) ? 1 : 0;
+  a.w_chunks = (p.w_in_lds && !a.mel_valu) ? static_cast<int>(p.blk_w.size() / 256) : 0;
   a.w_lds = tile_weights_offset(p, G);
+  a.quad_tbl = static_cast<const int*>(p.d_quad);
+  a.quad_w = static_cast<const float*>(p.d_quad_w);
   a.out_f16 = p.out_dtype == FM_F16 ? 1 : 0;
   a.tab_lds = tile_tables_offset(p, G);
   a.twn_lds = tile_twiddles_offset(p, G, rows);

@@ -419,6 +419,52 @@ int build_host_plan(Plan& p, const fm_args& a) {
     static_assert(kMelTileOverrun >= 4 * kMelStepGroup - 1, "zeroed tail too short");
     static_assert(kMelStepGroup * 64 % 256 == 0, "blocks must fill whole copy chunks");
   }
+  // ---- filter quads (vector-unit projection of wide tiles) -----------------
+  // Quad q holds filters 4q .. 4q+3, each over a run of L bins, L its
+  // longest filter's run; a shorter run is padded with zero weights, and
+  // starts early enough that the padded run ends inside the frame's bins.
+  // Weights in step order, 4 per step (one per filter), so a step's four
+  // weights are one 16-byte scalar load.
+  {
+    const int K = p.n_freqs;
+    const int nq = (n_mels + 3) / 4;
+    p.quad_hdr.assign(static_cast<size_t>(nq) * kQuadHdr, 0);
+    p.quad_w.clear();
+    std::vector<long> cost(nq);
+    for (int q = 0; q < nq; ++q) {
+      int L = 0;
+      for (int a = 0; a < 4 && 4 * q + a < n_mels; ++a) L = std::max(L, static_cast<int>(p.rows[4 * q + a].len));
+      int32_t* h = &p.quad_hdr[static_cast<size_t>(q) * kQuadHdr];
+      h[4] = L;
+      h[5] = static_cast<int32_t>(p.quad_w.size() / 4);
+      p.quad_w.resize(p.quad_w.size() + 4 * static_cast<size_t>(L), 0.0f);
+      float* w = p.quad_w.data() + 4 * static_cast<size_t>(h[5]);
+      for (int a = 0; a < 4; ++a) {
+        const int m = 4 * q + a;
+        if (m >= n_mels || p.rows[m].len == 0) continue;  // start 0, zero weights
+        const MelRow& r = p.rows[m];
+        const int st = std::max(0, std::min(static_cast<int>(r.first), K - L));
+        h[a] = st;
+        for (int i = 0; i < L; ++i) {
+          const int k = st + i;
+          if (k >= r.first && k < r.first + r.len) w[4 * i + a] = p.mel_w[r.off + k - r.first];
+        }
+      }
+      cost[q] = L + 3;  // the steps, plus the header loads and 4 row stores
+    }
+    // contiguous shares of about equal cost
+    long total = 0;
+    for (long c : cost) total += c;
+    int q = 0;
+    long acc = 0;
+    p.quad_beg[0] = 0;
+    for (int sh = 1; sh < kMelShares; ++sh) {
+      const long target = (total * sh + kMelShares / 2) / kMelShares;
+      while (q < nq && acc + cost[q] / 2 < target) acc += cost[q++];
+      p.quad_beg[sh] = q;
+    }
+    p.quad_beg[kMelShares] = nq;
+  }
   // ---- tile geometry -------------------------------------------------------
   if (fs.n3) {
     // The large-FFT kernel holds one frame's exchange buffer and walks its
@@ -501,6 +547,14 @@ int build_host_plan(Plan& p, const fm_args& a) {
   if (const char* e = std::getenv("FM_TILE_COPY")) {
     if (std::string(e) == "0") p.copy_override = 0;
     if (std::string(e) == "1") p.copy_override = 1;
+  }
+  if (const char* e = std::getenv("FM_MEL")) {
+    if (std::string(e) == "mfma") p.mel_valu = 0;
+    if (std::string(e) == "valu") p.mel_valu = 1;
+  }
+  if (const char* e = std::getenv("FM_MEL_FROM")) {  // A/B of the threshold
+    const int v = std::atoi(e);
+    if (v >= 1 && v <= 64) p.mel_valu_from = v;
   }
   return FM_OK;
 }

@@ -150,3 +150,38 @@ def test_auto_choice_on_the_device():
     assert mel.plan.forward_config(8, 480000) == (FM_FWD_ROWS, 47, 512)
     assert mel.plan.forward_config(1, 16000)[0] == FM_FWD_ROWS
     assert mel.plan.forward_config(16, 480000)[0] == FM_FWD_ROWS
+
+
+@pytest.mark.parametrize("n_fft,tiles", [(400, [17, 24, 32, 33, 47, 48, 49, 64]), (128, [17, 40, 64]),
+                                         (256, [20, 64])])
+@pytest.mark.parametrize("dtype", ["f32", "i16"])
+def test_vector_mel_equals_matrix_mel(n_fft, tiles, dtype, monkeypatch):
+    """Tiles of 17 frames or more project on the vector units (quads of 4
+    filters, one frame per lane); FM_MEL=mfma forces the matrix-core blocks.
+    Both add each filter's nonzero products in increasing bin order with one
+    rounding per multiply-add (the padding adds exact zeros), so the outputs
+    are equal bit for bit, in both second-pass layouts; 80 filters, and 81
+    (a last quad of one filter)."""
+    from stft_mel_spectrogram_amd import MelSpectrogram
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    rng = np.random.default_rng(n_fft + len(tiles))
+    L = 70 * (n_fft // 4) + 77
+    if dtype == "f32":
+        x = torch.from_numpy(rng.standard_normal((2, L)).astype(np.float32)).to("cuda")
+    else:
+        x = torch.from_numpy(rng.integers(-32768, 32768, size=(2, L)).astype(np.int16)).to("cuda")
+    for n_mels in (80, 81):
+        for layout in ("rows", "split"):
+            for g in tiles:
+                outs = {}
+                for mel in ("valu", "mfma"):
+                    monkeypatch.setenv("FM_FORWARD", layout)
+                    monkeypatch.setenv("FM_TILE_FRAMES", str(g))
+                    monkeypatch.setenv("FM_MEL", mel)
+                    m = MelSpectrogram(sample_rate=16000, n_fft=n_fft, hop_length=n_fft // 4,
+                                       n_mels=n_mels)
+                    outs[mel] = m(x)
+                torch.cuda.synchronize()
+                print(f"[case] n_fft={n_fft} {dtype} mels={n_mels} {layout} tile={g}", flush=True)
+                assert torch.equal(outs["valu"], outs["mfma"]), (n_fft, dtype, n_mels, layout, g)
