@@ -300,12 +300,15 @@ int fm_plan_tables(const fm_plan* plan, float* window, int32_t* mel_first,
 
 /*
  * fm_plan_mel_blocks -- the mel stage's layout on the matrix cores (host
- * copy, for tests).  The filterbank is cut into blocks of 16 filters; block
- * j covers bins kb .. kb + 4*ksteps - 1 and its weights are stored dense, 64
- * floats per 4-bin step, float s*64 + l holding filter mel0 + l%16 at bin
- * kb + 4*s + l/16 (0 outside the filter, or past n_mels).
- *   blocks[4*n_blocks]  int32 {kb, ksteps, w_off, mel0} per block, grouped by
- *                       the workgroup wave that computes them;
+ * copy, for tests).  The filterbank is cut into blocks of up to 16
+ * consecutive filters (16, and the longest blocks split into halves of
+ * filters); block j covers bins kb .. kb + 4*ksteps - 1 and its weights are
+ * stored dense, 64 floats per 4-bin step, float s*64 + l holding filter
+ * mel0 + l%16 at bin kb + 4*s + l/16 (0 outside the filter, and for l%16 >=
+ * nrow, the block's filter count).
+ *   blocks[4*n_blocks]  int32 {kb, ksteps, w_off, mel0 + 65536*nrow} per
+ *                       block, grouped by the workgroup wave that computes
+ *                       them;
  *   wave_beg[5]         wave w computes blocks wave_beg[w] .. wave_beg[w+1]-1;
  *   weights[n_weights]  every block's weights (w_off indexes them), plus
  *                       zero slack at the end.

@@ -183,8 +183,8 @@ class Plan:
                     tw_m=twm[0::2] + 1j * twm[1::2], tw_n=twn[0::2] + 1j * twn[1::2])
 
     def mel_blocks(self):
-        """The mel stage's block layout: (blocks[n,4] = kb, ksteps, w_off, mel0;
-        wave_beg[5]; weights)."""
+        """The mel stage's block layout: (blocks[n,4] = kb, ksteps, w_off,
+        mel0 + 65536 * filters; wave_beg[5]; weights)."""
         import numpy as np
         nb = ctypes.c_int32()
         nw = ctypes.c_int64()

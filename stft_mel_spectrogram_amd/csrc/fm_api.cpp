@@ -197,7 +197,7 @@ int fm_plan_mel_blocks(const fm_plan* plan, int32_t* blocks, int32_t* wave_beg, 
       blocks[4 * j + 0] = p.blocks[j].kb;
       blocks[4 * j + 1] = p.blocks[j].ksteps;
       blocks[4 * j + 2] = p.blocks[j].w_off;
-      blocks[4 * j + 3] = p.blocks[j].mel0;
+      blocks[4 * j + 3] = fm::mel_filter_word(p.blocks[j].mel0, p.blocks[j].nrow);
     }
   if (wave_beg)
     for (int w = 0; w <= fm::kMelWaves; ++w) wave_beg[w] = p.wave_beg[w];

@@ -29,7 +29,11 @@ struct MelBlock {
   int32_t w_off;   // offset of the block's weights (floats)
   int32_t mel0;    // first filter of the block
   int32_t s_hi = 0; // steps from s_hi on hold only zero weights
+  int32_t nrow = 16; // filters mel0 .. mel0 + nrow - 1 (<= 16; lanes past them hold zero weights)
 };
+// A block's filter word in the device table: mel0, and its filter count in
+// bits 16 and up (mel0 < 256).
+constexpr int32_t mel_filter_word(int mel0, int nrow) { return mel0 | (nrow << 16); }
 // A block's step word in the device table: ksteps, and s_hi in bits 20 and
 // up (the kernel may skip the products of the steps from s_hi on).  ksteps
 // <= (n_fft/2 + 1 + 3)/4 + 3 <= 516 for n_fft <= 4096: ten bits.
@@ -295,6 +299,9 @@ int tile_tables_offset(const Plan& p, int frames);  // bytes; pass-1 tables in L
 // smaller ones hold them in registers or read them from L2).
 constexpr bool twiddles_in_lds(int m) { return m >= 1024; }
 int tile_twiddles_offset(const Plan& p, int frames, bool rows);  // bytes; split twiddles in LDS
+// Tiles of this many frames project on the vector units (no block weights
+// or staging in their LDS).
+bool tile_mel_valu(const Plan& p, int frames);
 int tile_lds_bytes(const Plan& p, int frames, bool rows);
 
 // LDS layout of a backward pass of `chunk` frames (floats from the start):

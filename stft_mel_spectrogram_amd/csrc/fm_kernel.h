@@ -62,7 +62,7 @@ struct KArgs {
   int pad_mode;
   float half_power;     // power / 2
   int vec_ok;           // interior tiles may use paired (2-sample) loads
-  const int* mel_tbl;   // wave_beg[5], 3 pad, then {kb, step word (mel_step_word), w_off, mel0} per block
+  const int* mel_tbl;   // wave_beg[5], 3 pad, then {kb, step word (mel_step_word), w_off, filter word (mel_filter_word)} per block
   const float* blk_w;   // block weights, 64 per 4-bin step (MFMA A-operand order)
   int w_chunks;         // block weights / 256 (copied to LDS in 1 KB chunks;
                         // 0 when the shape reads them from global memory)
@@ -125,7 +125,8 @@ __device__ __forceinline__ void mel_blocks(const float* P, const float* WL, floa
     // narrow-tile loop measured 3-7% slower (n_fft 2048: 97.2 against 91.1).
     constexpr bool kSkip = STAGE || GW;
     const int kb = blk[4 * bi], sw = blk[4 * bi + 1], woff = blk[4 * bi + 2],
-              mel0 = blk[4 * bi + 3];
+              fw = blk[4 * bi + 3];
+    const int mel0 = fw & 0xffff, nrow = fw >> 16;  // filters mel0 .. mel0 + nrow - 1 (mel_filter_word)
     const int s_end = kSkip ? sw >> 20 : (sw & 1023);
     f32x4 acc[NFB];
 #pragma unroll
@@ -183,7 +184,6 @@ __device__ __forceinline__ void mel_blocks(const float* P, const float* WL, floa
       // of one wave complete in order, so waiting for the writes suffices
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
       __builtin_amdgcn_wave_barrier();
-      const int nrow = min(16, n_mels - mel0);
       const bool st = lane < nvalid && lane < 16 * NFB;
       const int col = lane < 16 * NFB ? lane : 0;  // lanes past the tile's columns stay in the stage
       for (int m = 0; m < nrow; ++m) {
@@ -201,7 +201,7 @@ __device__ __forceinline__ void mel_blocks(const float* P, const float* WL, floa
         if (frame < nvalid) {
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            if (mrow + r < n_mels) obase[static_cast<long long>(mrow + r) * n_frames + frame] = static_cast<OT>(acc[f][r]);
+            if (4 * kq + r < nrow) obase[static_cast<long long>(mrow + r) * n_frames + frame] = static_cast<OT>(acc[f][r]);
         }
       }
     }

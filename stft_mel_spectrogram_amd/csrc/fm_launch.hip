@@ -93,7 +93,7 @@ int upload_plan(Plan& p) {
     tbl[8 + 4 * j + 0] = p.blocks[j].kb;
     tbl[8 + 4 * j + 1] = mel_step_word(p.blocks[j].ksteps, p.blocks[j].s_hi);
     tbl[8 + 4 * j + 2] = p.blocks[j].w_off;
-    tbl[8 + 4 * j + 3] = p.blocks[j].mel0;
+    tbl[8 + 4 * j + 3] = mel_filter_word(p.blocks[j].mel0, p.blocks[j].nrow);
   }
   std::copy(p.blk_w.begin(), p.blk_w.end(), reinterpret_cast<float*>(host.data() + o_bw));
   std::copy(p.taps.begin(), p.taps.end(), reinterpret_cast<BinTap*>(host.data() + o_taps));
@@ -330,7 +330,7 @@ int launch_forward(const Plan& p, const void* in, int in_dtype, int64_t batch, i
   a.mel_tbl = static_cast<const int*>(p.d_mel_tbl);
   a.blk_w = static_cast<const float*>(p.d_blk_w);
   // wide tiles project on the vector units (no block weights to copy)
-  a.mel_valu = (p.mel_valu && G >= p.mel_valu_from) ? 1 : 0;
+  a.mel_valu = tile_mel_valu(p, G) ? 1 : 0;
   a.w_chunks = (p.w_in_lds && !a.mel_valu) ? static_cast<int>(p.blk_w.size() / 256) : 0;
   a.w_lds = tile_weights_offset(p, G);
   a.quad_tbl = static_cast<const int*>(p.d_quad);

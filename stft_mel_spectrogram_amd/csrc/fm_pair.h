@@ -88,7 +88,8 @@ __device__ __forceinline__ void pair_mel(const float* P, const float* WL, float*
 #pragma unroll
   for (int f = 0; f < NFB; ++f) roff[f] = min(16 * f + fr, nv - 1) * KS + kq;
   for (int bi = bb; bi < be; ++bi) {
-    const int kb = blk[4 * bi], ks = blk[4 * bi + 1] & 1023, woff = blk[4 * bi + 2], mel0 = blk[4 * bi + 3];
+    const int kb = blk[4 * bi], ks = blk[4 * bi + 1] & 1023, woff = blk[4 * bi + 2];
+    const int mel0 = blk[4 * bi + 3] & 0xffff, nrow = blk[4 * bi + 3] >> 16;  // mel_filter_word
     f32x4 acc[NFB];
 #pragma unroll
     for (int f = 0; f < NFB; ++f) acc[f] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -114,7 +115,8 @@ __device__ __forceinline__ void pair_mel(const float* P, const float* WL, float*
 #pragma unroll
     for (int f = 0; f < NFB; ++f)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) orow[r * kPairOutPitch + 16 * f] = acc[f][r];
+      for (int r = 0; r < 4; ++r)
+        if (4 * kq + r < nrow) orow[r * kPairOutPitch + 16 * f] = acc[f][r];  // (the block's own filters only)
   }
 }
 

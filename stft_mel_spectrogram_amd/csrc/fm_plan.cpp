@@ -108,11 +108,15 @@ int tile_weights_offset(const Plan& p, int frames) {
 
 int tile_tables_offset(const Plan& p, int frames) { return tile_exchange_bytes(p, frames); }
 
+bool tile_mel_valu(const Plan& p, int frames) { return p.mel_valu && frames >= p.mel_valu_from; }
+
 int tile_twiddles_offset(const Plan& p, int frames, bool rows) {
   const long tables = tables_in_lds(p.fft.n1, p.n_fft / 2) ? 16L * (p.n_fft / 2) : 0;
   const long pass1 = tile_tables_offset(p, frames) + tables;
-  const long stage = mel_stage_floats(rows, frames);
-  const long weights = p.w_in_lds ? static_cast<long>(p.blk_w.size()) : 0;
+  // the matrix-core mel stage's weights and staging (none on the vector units)
+  const bool valu = tile_mel_valu(p, frames);
+  const long stage = valu ? 0 : mel_stage_floats(rows, frames);
+  const long weights = (p.w_in_lds && !valu) ? static_cast<long>(p.blk_w.size()) : 0;
   const long after_fft = (static_cast<long>(tile_weights_offset(p, frames)) + weights + stage) * 4;
   return static_cast<int>((std::max<long>(pass1, after_fft) + 15) / 16 * 16);
 }
@@ -348,7 +352,7 @@ int build_host_plan(Plan& p, const fm_args& a) {
   }
 
   // ---- mel blocks ----------------------------------------------------------
-  // Blocks of 16 filters; each covers the union of its filters' bin runs,
+  // Blocks of up to 16 filters; each covers the union of its filters' bin runs,
   // rounded up to whole groups of 4-bin steps and shifted left if it would
   // run past the last bin.  When 4*steps exceeds n_freqs it starts at bin 0
   // and reads at most 15 floats past a frame's row, all with zero weights:
@@ -356,11 +360,7 @@ int build_host_plan(Plan& p, const fm_args& a) {
   // (full or ragged), floats the kernel zeroes before the mel stage.
   {
     const int K = p.n_freqs;
-    const int nb = (n_mels + kMelBlock - 1) / kMelBlock;
-    std::vector<MelBlock> blk(nb);
-    std::vector<std::vector<float>> bw(nb);
-    for (int j = 0; j < nb; ++j) {
-      const int m0 = j * kMelBlock, m1 = std::min(n_mels, m0 + kMelBlock);
+    auto make_block = [&](int m0, int m1, std::vector<float>& w) {
       int lo = K, hi = 0;
       for (int m = m0; m < m1; ++m)
         if (p.rows[m].len > 0) {
@@ -368,23 +368,64 @@ int build_host_plan(Plan& p, const fm_args& a) {
           hi = std::max(hi, static_cast<int>(p.rows[m].first + p.rows[m].len));
         }
       MelBlock b{0, 0, 0, m0};
+      b.nrow = m1 - m0;
+      w.clear();
       if (hi > lo) {
         b.ksteps = ((hi - lo + 3) / 4 + kMelStepGroup - 1) / kMelStepGroup * kMelStepGroup;
         b.kb = std::max(0, std::min(lo, K - 4 * b.ksteps));
-        bw[j].assign(static_cast<size_t>(b.ksteps) * 64, 0.0f);
+        w.assign(static_cast<size_t>(b.ksteps) * 64, 0.0f);
         for (int s = 0; s < b.ksteps; ++s)
           for (int l = 0; l < 64; ++l) {
             const int m = m0 + l % kMelBlock, k = b.kb + 4 * s + l / kMelBlock;
-            if (m >= n_mels) continue;
+            if (m >= m1) continue;
             const MelRow& r = p.rows[m];
             if (r.len > 0 && k >= r.first && k < r.first + r.len) {
-              bw[j][static_cast<size_t>(s) * 64 + l] = p.mel_w[r.off + k - r.first];
+              w[static_cast<size_t>(s) * 64 + l] = p.mel_w[r.off + k - r.first];
               b.s_hi = std::max(b.s_hi, s + 1);
             }
           }
       }
-      blk[j] = b;
+      return b;
+    };
+    // 16 consecutive filters per block; then, while the longest block runs
+    // more than 32 steps and more than twice an eighth of all steps (the mel
+    // stage spreads over up to 8 waves, and each block is one wave's serial
+    // chain of steps), it is split into its two halves of filters, each over
+    // its own (shorter) bin run.  A filter's sum is the same either way: its
+    // bins all lie in its block's run, and the steps go in bin order.
+    // Measured (same box, us per launch, narrow tiles on the matrix cores):
+    // n_fft 1024, 8 x 32768 (longest block 60 -> 36 steps): 8.31 -> 8.00;
+    // n_fft 2048, 64 x 220500 (88 -> 60): 83.3 -> 81.5; n_fft 4096, 4 x
+    // 1323000: 60.5 -> 58.1.  Splitting shorter blocks, or down to 5/4 of an
+    // eighth, adds more steps than it saves (n_fft 400, 1 x 16000: 6.52 ->
+    // 6.67; n_fft 512, 32 x 480000: 56.0 -> 58.0).
+    std::vector<std::pair<int, int>> ranges;
+    for (int m0 = 0; m0 < n_mels; m0 += kMelBlock) ranges.push_back({m0, std::min(n_mels, m0 + kMelBlock)});
+    std::vector<float> tmp, tmp2;
+    for (int it = 0; it < 16; ++it) {
+      long total = 0;
+      int longest = -1, lsteps = 0;
+      for (size_t r = 0; r < ranges.size(); ++r) {
+        const int st = make_block(ranges[r].first, ranges[r].second, tmp).ksteps;
+        total += st;
+        if (st > lsteps) {
+          lsteps = st;
+          longest = static_cast<int>(r);
+        }
+      }
+      if (longest < 0 || lsteps <= 32 || 4L * lsteps <= total) break;
+      const int m0 = ranges[longest].first, m1 = ranges[longest].second;
+      if (m1 - m0 < 2) break;
+      const int mid = m0 + (m1 - m0) / 2;
+      const int sa = make_block(m0, mid, tmp).ksteps, sb = make_block(mid, m1, tmp2).ksteps;
+      if (std::max(sa, sb) >= lsteps) break;  // no shorter chain
+      ranges[longest] = {m0, mid};
+      ranges.insert(ranges.begin() + longest + 1, {mid, m1});
     }
+    const int nb = static_cast<int>(ranges.size());
+    std::vector<MelBlock> blk(nb);
+    std::vector<std::vector<float>> bw(nb);
+    for (int j = 0; j < nb; ++j) blk[j] = make_block(ranges[j].first, ranges[j].second, bw[j]);
     // Longest first onto the least loaded wave; a block costs its steps plus
     // 2 for the address set-up and the stores.
     std::vector<int> order(nb);
@@ -400,11 +441,13 @@ int build_host_plan(Plan& p, const fm_args& a) {
       owner[j] = w;
       load[w] += blk[j].ksteps + 2;
     }
+    // Within a share, longest first: where the row layout spreads a share over
+    // two waves (alternate blocks), that balances them too.
     p.blocks.clear();
     p.blk_w.clear();
     for (int w = 0; w < kMelWaves; ++w) {
       p.wave_beg[w] = static_cast<int>(p.blocks.size());
-      for (int j = 0; j < nb; ++j)
+      for (int j : order)
         if (owner[j] == w) {
           MelBlock b = blk[j];
           b.w_off = static_cast<int32_t>(p.blk_w.size());
@@ -465,6 +508,16 @@ int build_host_plan(Plan& p, const fm_args& a) {
     }
     p.quad_beg[kMelShares] = nq;
   }
+  // the mel stage's implementation per tile width (tile_mel_valu), before the
+  // tile geometry: it decides which tiles hold the block weights in LDS
+  if (const char* e = std::getenv("FM_MEL")) {
+    if (std::string(e) == "mfma") p.mel_valu = 0;
+    if (std::string(e) == "valu") p.mel_valu = 1;
+  }
+  if (const char* e = std::getenv("FM_MEL_FROM")) {  // A/B of the threshold
+    const int v = std::atoi(e);
+    if (v >= 1 && v <= 64) p.mel_valu_from = v;
+  }
   // ---- tile geometry -------------------------------------------------------
   if (fs.n3) {
     // The large-FFT kernel holds one frame's exchange buffer and walks its
@@ -490,12 +543,20 @@ int build_host_plan(Plan& p, const fm_args& a) {
   int tmax = 64;
   while (tmax > 1 && tmax * (fs.n1 / 2) > p.threads) --tmax;
   // (either layout of the second pass)
+  // (either layout of the second pass; every width up to the maximum must fit:
+  // tiles that project on the vector units hold no block weights, so a
+  // narrower tile may need more LDS than a wider one)
   auto lds_of = [&](int g) { return std::max(tile_lds_bytes(p, g, false), tile_lds_bytes(p, g, true)); };
-  while (tmax > 1 && lds_of(tmax) > 160 * 1024) --tmax;
-  if (lds_of(tmax) > 160 * 1024)
+  auto lds_upto = [&](int g) {
+    int m = 0;
+    for (int h = 1; h <= g; ++h) m = std::max(m, lds_of(h));
+    return m;
+  };
+  while (tmax > 1 && lds_upto(tmax) > 160 * 1024) --tmax;
+  if (lds_upto(tmax) > 160 * 1024)
     return set_error(FM_E_UNSUPPORTED, "mel filterbank too large for the LDS of one tile");
   p.tile_max = tmax;
-  p.lds_bytes = lds_of(tmax);
+  p.lds_bytes = lds_upto(tmax);
   // backward passes: as many frames as the kernel's registers and the LDS
   // allow
   int cmax = bwd_chunk_cap(fs.n1, fs.n2, kBwdThreads);
@@ -547,14 +608,6 @@ int build_host_plan(Plan& p, const fm_args& a) {
   if (const char* e = std::getenv("FM_TILE_COPY")) {
     if (std::string(e) == "0") p.copy_override = 0;
     if (std::string(e) == "1") p.copy_override = 1;
-  }
-  if (const char* e = std::getenv("FM_MEL")) {
-    if (std::string(e) == "mfma") p.mel_valu = 0;
-    if (std::string(e) == "valu") p.mel_valu = 1;
-  }
-  if (const char* e = std::getenv("FM_MEL_FROM")) {  // A/B of the threshold
-    const int v = std::atoi(e);
-    if (v >= 1 && v <= 64) p.mel_valu_from = v;
   }
   return FM_OK;
 }

@@ -153,9 +153,10 @@ def test_csr_statistics_of_the_workloads():
                                        ("whisper", dict(n_mels=37)),
                                        ("whisper", dict(mel_scale="slaney", norm="slaney"))])
 def test_mel_blocks_equal_the_csr_filterbank(name, over):
-    """The kernel's mel layout (16-filter blocks, dense 4-bin steps in the
-    matrix-core lane order, split over 4 waves) holds exactly the CSR
-    weights, stays inside the bins, and covers every filter once."""
+    """The kernel's mel layout (blocks of up to 16 consecutive filters, dense
+    4-bin steps in the matrix-core lane order, split over 4 waves) holds
+    exactly the CSR weights, stays inside the bins, and covers every filter
+    once: the blocks' filter ranges tile 0 .. n_mels - 1."""
     cfg = dict(W.WORKLOADS[name])
     cfg.update(over)
     p = host_plan(cfg)
@@ -163,19 +164,24 @@ def test_mel_blocks_equal_the_csr_filterbank(name, over):
     blocks, wave_beg, wts = p.mel_blocks()
     K = cfg["n_fft"] // 2 + 1
     M = cfg["n_mels"]
-    nb = (M + 15) // 16
-    assert len(blocks) == nb and wave_beg[0] == 0 and wave_beg[4] == nb
+    nb = len(blocks)
+    assert nb >= (M + 15) // 16 and wave_beg[0] == 0 and wave_beg[4] == nb
     assert all(wave_beg[w] <= wave_beg[w + 1] for w in range(4))
-    assert sorted(blocks[:, 3]) == list(range(0, 16 * nb, 16))
+    mel0s, nrows = blocks[:, 3] & 0xFFFF, blocks[:, 3] >> 16
+    assert np.all((nrows >= 1) & (nrows <= 16))
+    order = np.argsort(mel0s)
+    assert mel0s[order][0] == 0 and np.array_equal(mel0s[order][1:], (mel0s + nrows)[order][:-1])
+    assert (mel0s + nrows)[order][-1] == M
     dense = np.zeros((M, K))
-    for kb, ks, off, mel0 in blocks:
+    for kb, ks, off, fw in blocks:
+        mel0, nrow = fw & 0xFFFF, fw >> 16
         assert ks % 4 == 0
         assert 0 <= kb and (kb + 4 * ks <= K or (kb == 0 and 4 * ks <= K + 15))
         for s_ in range(ks):
             for lane in range(64):
                 m, k = mel0 + lane % 16, kb + 4 * s_ + lane // 16
                 v = wts[off + 64 * s_ + lane]
-                if m >= M or k >= K:
+                if lane % 16 >= nrow or m >= M or k >= K:
                     assert v == 0.0
                 elif v != 0.0:
                     assert dense[m, k] == 0.0
@@ -223,7 +229,7 @@ def test_mel_block_reads_stay_in_written_or_zeroed_floats(n_fft):
             p = N.Plan(device=False, sample_rate=sr, n_fft=n_fft, hop_length=n_fft // 4,
                        n_mels=n_mels, f_max=f_max)
             blocks, _, wts = p.mel_blocks()
-            for kb, ks, off, mel0 in blocks:
+            for kb, ks, off, fw in blocks:
                 assert kb >= 0
                 end = kb + 4 * ks                       # one past the last bin read
                 assert end - K < MEL_ROW_OVERRUN, (n_fft, n_mels, f_max, kb, ks)
