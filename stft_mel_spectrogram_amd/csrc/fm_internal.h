@@ -79,10 +79,9 @@ constexpr int kMelStageMinFrames = 33;
 // shares.  The threshold is measured (same box, us per launch, against the
 // matrix-core blocks): n_fft 400, 8 x 480000 (47-frame tiles): 14.5 against
 // 15.9; 4 x 480000 (24 frames): 12.1 against 13.4; n_fft 256, 8 x 480000:
-// 21.0 against 22.1; 1 x 16000 (26 frames): 6.5 against 6.7; below 17
-// frames half a wave's lanes or more idle and the wider filters of the
-// larger FFTs lose (n_fft 2048, 16-frame tiles: 97.6 against 83.7; n_fft
-// 400, 1 x 480000, 12 frames: 8.4 against 7.6).
+// 21.0 against 22.1.  Below 17 frames half a wave's lanes or more idle, and
+// the wider filters of the larger FFTs lose (n_fft 2048, 16-frame tiles:
+// 97.6 against 83.7; n_fft 400, 1 x 480000, 12 frames: 8.4 against 7.6).
 constexpr int kMelValuMinFrames = 17;
 constexpr int kMelShares = 8;
 constexpr int kQuadHdr = 8;  // int32 per quad: 4 start bins, run length, weight offset (float4s), 2 pad
