@@ -317,6 +317,23 @@ int fm_plan_tables(const fm_plan* plan, float* window, int32_t* mel_first,
 int fm_plan_mel_blocks(const fm_plan* plan, int32_t* blocks, int32_t* wave_beg,
                        float* weights, int32_t* n_blocks, int64_t* n_weights);
 
+/*
+ * fm_plan_mel_quads -- the mel stage's layout on the vector units (host copy,
+ * for tests; the same projection as the blocks above, used by tiles of 17
+ * frames or more).  Filters in quads of 4 consecutive filters (quad q: filters
+ * 4q .. 4q+3, those past n_mels empty); a quad runs L steps of one bin, filter
+ * a of the quad over bins start_a .. start_a + L - 1, weight w[4*(off + i) + a]
+ * at step i (0 outside the filter).
+ *   headers[6*n_quads]   int32 {start_0, start_1, start_2, start_3, L, off}
+ *                        per quad;
+ *   share_beg[9]         share s holds quads share_beg[s] .. share_beg[s+1]-1
+ *                        (a workgroup of w waves gives each wave 8/w shares);
+ *   weights[n_weights]   every quad's weights, 4 per step.
+ * Any pointer may be NULL; call once with NULL arrays to learn the sizes.
+ */
+int fm_plan_mel_quads(const fm_plan* plan, int32_t* headers, int32_t* share_beg,
+                      float* weights, int32_t* n_quads, int64_t* n_weights);
+
 #ifdef __cplusplus
 }
 #endif

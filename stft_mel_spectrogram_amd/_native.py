@@ -85,6 +85,7 @@ def _load() -> ctypes.CDLL:
         "fm_plan_info_get": (I, [P, ctypes.POINTER(PlanInfo)]),
         "fm_plan_tables": (I, [P, P, P, P, P, P, P, P]),
         "fm_plan_mel_blocks": (I, [P, P, P, P, P, P]),
+        "fm_plan_mel_quads": (I, [P, P, P, P, P, P]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -195,6 +196,20 @@ class Plan:
         ptr = lambda a: a.ctypes.data_as(ctypes.c_void_p)  # noqa: E731
         check(lib.fm_plan_mel_blocks(self.handle, ptr(blocks), ptr(wave_beg), ptr(w), None, None))
         return blocks[:4 * nb.value].reshape(-1, 4), wave_beg, w[:nw.value]
+
+    def mel_quads(self):
+        """The vector-unit mel stage's layout: (headers[n,6] = start_0..3, L,
+        off; share_beg[9]; weights, 4 per step)."""
+        import numpy as np
+        nq = ctypes.c_int32()
+        nw = ctypes.c_int64()
+        check(lib.fm_plan_mel_quads(self.handle, None, None, None, ctypes.byref(nq), ctypes.byref(nw)))
+        hdr = np.zeros(max(nq.value, 1) * 6, np.int32)
+        share = np.zeros(9, np.int32)
+        w = np.zeros(max(nw.value, 1), np.float32)
+        ptr = lambda a: a.ctypes.data_as(ctypes.c_void_p)  # noqa: E731
+        check(lib.fm_plan_mel_quads(self.handle, ptr(hdr), ptr(share), ptr(w), None, None))
+        return hdr[:6 * nq.value].reshape(-1, 6), share, w[:nw.value]
 
     def forward_ptr(self, in_ptr: int, in_dtype: int, batch: int, length: int, out_ptr: int,
                     stream: int = 0) -> None:

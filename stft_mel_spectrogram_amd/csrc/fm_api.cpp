@@ -207,4 +207,20 @@ int fm_plan_mel_blocks(const fm_plan* plan, int32_t* blocks, int32_t* wave_beg, 
   return FM_OK;
 }
 
+int fm_plan_mel_quads(const fm_plan* plan, int32_t* headers, int32_t* share_beg, float* weights,
+                      int32_t* n_quads, int64_t* n_weights) {
+  if (!plan) return fm::set_error(FM_E_INVAL, "plan must not be NULL");
+  const fm::Plan& p = plan->p;
+  const size_t nq = p.quad_hdr.size() / fm::kQuadHdr;
+  if (headers)
+    for (size_t q = 0; q < nq; ++q)
+      for (int i = 0; i < 6; ++i) headers[6 * q + i] = p.quad_hdr[fm::kQuadHdr * q + i];
+  if (share_beg)
+    for (int s = 0; s <= fm::kMelShares; ++s) share_beg[s] = p.quad_beg[s];
+  if (weights) std::memcpy(weights, p.quad_w.data(), p.quad_w.size() * sizeof(float));
+  if (n_quads) *n_quads = static_cast<int32_t>(nq);
+  if (n_weights) *n_weights = static_cast<int64_t>(p.quad_w.size());
+  return FM_OK;
+}
+
 }  // extern "C"

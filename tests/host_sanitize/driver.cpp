@@ -32,6 +32,16 @@ static void inspect(fm_plan* h) {
   std::vector<int32_t> blocks(4 * (nb > 0 ? nb : 1)), wave_beg(5);
   std::vector<float> bw(nw > 0 ? nw : 1);
   EXPECT(fm_plan_mel_blocks(h, blocks.data(), wave_beg.data(), bw.data(), nullptr, nullptr) == FM_OK);
+  int32_t nq = 0;
+  int64_t nqw = 0;
+  EXPECT(fm_plan_mel_quads(h, nullptr, nullptr, nullptr, &nq, &nqw) == FM_OK);
+  EXPECT(nq == (in.n_mels + 3) / 4);
+  std::vector<int32_t> qh(6 * (nq > 0 ? nq : 1)), qs(9);
+  std::vector<float> qw(nqw > 0 ? nqw : 1);
+  EXPECT(fm_plan_mel_quads(h, qh.data(), qs.data(), qw.data(), nullptr, nullptr) == FM_OK);
+  EXPECT(qs[0] == 0 && qs[8] == nq);
+  for (int q = 0; q < nq; ++q)
+    for (int a = 0; a < 4; ++a) EXPECT(qh[6 * q + a] >= 0 && qh[6 * q + a] + qh[6 * q + 4] <= in.n_freqs);
   for (int m = 0; m < in.n_mels; ++m) {
     EXPECT(len[m] >= 0 && first[m] >= 0 && first[m] + len[m] <= in.n_freqs);
     EXPECT(off[m] >= 0 && off[m] + len[m] <= in.nnz);

@@ -207,6 +207,64 @@ def test_mel_blocks_equal_the_csr_filterbank(name, over):
     assert max(cost) - min(cost) <= max(blocks[:, 1]) + 2
 
 
+@pytest.mark.parametrize("name,over", [("whisper", {}), ("tiny", {}), ("pow2", {}), ("large", {}),
+                                       ("tiny", dict(n_fft=64, win_length=64, hop_length=16, n_mels=40)),
+                                       ("whisper", dict(n_mels=37)),
+                                       ("whisper", dict(mel_scale="slaney", norm="slaney"))])
+def test_mel_quads_equal_the_csr_filterbank(name, over):
+    """The vector-unit mel layout (quads of 4 consecutive filters, runs
+    padded to the quad's longest, 4 weights per step) holds exactly the CSR
+    weights; every padded run lies inside the frame's bins (the kernel reads
+    no float outside a valid power row); each quad's length is its longest
+    filter's run; the 8 shares tile the quads in order."""
+    cfg = dict(W.WORKLOADS[name])
+    cfg.update(over)
+    p = host_plan(cfg)
+    t = p.tables()
+    hdr, share, w = p.mel_quads()
+    K = cfg["n_fft"] // 2 + 1
+    M = cfg["n_mels"]
+    nq = (M + 3) // 4
+    assert len(hdr) == nq
+    assert share[0] == 0 and share[8] == nq and np.all(np.diff(share) >= 0)
+    dense = np.zeros((M, K))
+    for q, (s0, s1, s2, s3, L, off) in enumerate(hdr):
+        lens = [t["len"][m] for m in range(4 * q, min(M, 4 * q + 4))]
+        assert L == max(lens)
+        for a, st in enumerate((s0, s1, s2, s3)):
+            assert 0 <= st and st + L <= K
+            for i in range(L):
+                v = w[4 * (off + i) + a]
+                m = 4 * q + a
+                if m >= M:
+                    assert v == 0.0
+                elif v != 0.0:
+                    assert dense[m, st + i] == 0.0
+                    dense[m, st + i] = v
+    assert len(w) == 4 * int(hdr[:, 4].sum())
+    csr = np.zeros((M, K))
+    for m in range(M):
+        a, ln, o = t["first"][m], t["len"][m], t["off"][m]
+        csr[m, a:a + ln] = t["weights"][o:o + ln]
+    assert np.array_equal(dense, csr)
+
+
+@pytest.mark.parametrize("n_fft", [64, 128, 256, 400, 512, 1024, 2048])
+def test_mel_quad_runs_stay_in_the_row(n_fft):
+    """For every n_mels 1..256 and f_max at or below Nyquist, every padded
+    quad run starts at bin >= 0 and ends at the last bin at most: the vector
+    units read only inside the rows of valid frames."""
+    sr = 16000
+    K = n_fft // 2 + 1
+    for f_max in (sr / 2, 0.43 * sr):
+        for n_mels in range(1, 257):
+            p = N.Plan(device=False, sample_rate=sr, n_fft=n_fft, hop_length=n_fft // 4,
+                       n_mels=n_mels, f_max=f_max)
+            hdr, share, _ = p.mel_quads()
+            assert len(hdr) == (n_mels + 3) // 4 and share[8] == len(hdr)
+            assert np.all(hdr[:, :4] >= 0) and np.all(hdr[:, :4] + hdr[:, 4:5] <= K), (n_fft, n_mels, f_max)
+
+
 # Floats the forward kernel zeroes after the last valid frame's power row
 # (the mel stage may read that far past a row).
 MEL_ROW_OVERRUN = 16
