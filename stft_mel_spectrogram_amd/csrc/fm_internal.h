@@ -212,6 +212,7 @@ struct Plan {
   int tile_max = 0;      // most frames a workgroup tile may hold
   int tile_override = 0; // FM_TILE_FRAMES, for sweeps (0: chosen per call)
   int copy_override = -1; // FM_TILE_COPY=0|1, for A/B measurements (-1: chosen per call)
+  int prio_override = -1; // FM_PRIO=0|1, for A/B measurements (-1: chosen per call)
   int threads = 256;
   int lds_bytes = 0;     // dynamic LDS of a tile of tile_max frames
   // mel blocks in wave order: wave w takes blocks [wave_beg[w], wave_beg[w+1])
@@ -336,6 +337,7 @@ struct FwdChoice {
   int tile = 1;
   int64_t workgroups = 0;
   bool copy = false;
+  bool phase_prio = false;  // waves raise their issue priority by phase (mel_forward_kernel)
 };
 FwdChoice choose_forward(const Plan& p, int64_t batch, int64_t T);
 int launch_forward(const Plan& p, const void* in, int in_dtype, int64_t batch,

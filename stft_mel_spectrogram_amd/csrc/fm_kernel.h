@@ -371,7 +371,10 @@ constexpr bool kCopyCapable = copy_capable(N1, N2);
 template <int N1, int N2>
 constexpr bool kRowsCapable = N1 <= kRowsMaxN1;
 
-template <int N1, int N2, typename InT, int PMODE, bool COPY, bool ROWS>
+// PRIO: the waves lower their issue priority phase by phase (pass 1
+// highest, the mel stage lowest), so that of two workgroups sharing a CU the
+// one that is behind issues first (chosen per call, choose_forward).
+template <int N1, int N2, typename InT, int PMODE, bool COPY, bool ROWS, bool PRIO>
 __global__ __launch_bounds__((kThreads<N1, N2, ROWS>), (kMinWavesPerSimd<N1, N2, ROWS>)) void mel_forward_kernel(KArgs a) {
   constexpr int M = N1 * N2;
   constexpr int K = M + 1;        // one-sided bins
@@ -436,6 +439,7 @@ __global__ __launch_bounds__((kThreads<N1, N2, ROWS>), (kMinWavesPerSimd<N1, N2,
     const int nvalid = min(G, a.n_frames - t0);
     const InT* x = static_cast<const InT*>(a.in) + static_cast<long long>(b) * L;
 
+    if constexpr (PRIO) __builtin_amdgcn_s_setprio(3);  // pass 1
     // ---- pass 1: window + N1-point DFTs, twiddle, exchange through LDS ----
     const bool p1 = slot < SLOTS;  // threads with a pass-1 role
     {
@@ -617,6 +621,7 @@ __global__ __launch_bounds__((kThreads<N1, N2, ROWS>), (kMinWavesPerSimd<N1, N2,
     }
     __syncthreads();
 
+    if constexpr (PRIO) __builtin_amdgcn_s_setprio(2);  // second-pass DFTs
     // ---- pass 2: N2-point DFTs, real split, power -> P (aliases Y) --
     const bool has = f2 < nvalid;
     if constexpr (ROWS) {
@@ -656,6 +661,7 @@ __global__ __launch_bounds__((kThreads<N1, N2, ROWS>), (kMinWavesPerSimd<N1, N2,
             __int_as_float(__builtin_amdgcn_ds_bpermute(partner, __float_as_int(za[N2 - 1 - j].x))),
             __int_as_float(__builtin_amdgcn_ds_bpermute(partner, __float_as_int(za[N2 - 1 - j].y))));
       if constexpr (kTwLds) __builtin_amdgcn_s_waitcnt(0);  // the twiddle copies have landed
+      if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);  // split
       __syncthreads();
       // every read of the exchange buffer is done: weights into LDS behind
       // the power tile while the split runs, and the mel stage's overrun
@@ -713,6 +719,7 @@ __global__ __launch_bounds__((kThreads<N1, N2, ROWS>), (kMinWavesPerSimd<N1, N2,
       // (the twiddle copies have landed: a wave without samples to load in
       // pass 1 has not waited for its loads yet)
       if constexpr (kTwLds) __builtin_amdgcn_s_waitcnt(0);
+      if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);  // split
       __syncthreads();
       // Every read of the exchange buffer is done: stream the mel weights into
       // LDS behind the power tile (direct global -> LDS loads, 1 KB per wave
@@ -760,6 +767,7 @@ __global__ __launch_bounds__((kThreads<N1, N2, ROWS>), (kMinWavesPerSimd<N1, N2,
       }
     }
     __builtin_amdgcn_s_waitcnt(0);  // the weight copies have landed in LDS
+    if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);  // mel stage
     __syncthreads();
 
     // ---- mel projection on the matrix cores: each wave its filter blocks,
@@ -828,14 +836,22 @@ __global__ __launch_bounds__((kThreads<N1, N2, ROWS>), (kMinWavesPerSimd<N1, N2,
 // support it) and the second pass's layout (rows: one thread per row, 512
 // threads; else one per pair of rows); instantiated in fm_shape_<N1>x<N2>.hip.
 template <int N1, int N2>
-void* kernel_for(int in_dtype, int pmode, bool copy, bool rows) {
-  auto pick = [](auto in_tag, auto copy_tag, auto rows_tag, int pm) -> void* {
+void* kernel_for(int in_dtype, int pmode, bool copy, bool rows, bool prio) {
+  // (the phase-priority variant is built for the tile-copy kernels only)
+  auto pick = [prio](auto in_tag, auto copy_tag, auto rows_tag, int pm) -> void* {
     using InT = decltype(in_tag);
     constexpr bool C = decltype(copy_tag)::value;
     constexpr bool R = decltype(rows_tag)::value;
-    if (pm == 0) return reinterpret_cast<void*>(&mel_forward_kernel<N1, N2, InT, 0, C, R>);
-    if (pm == 1) return reinterpret_cast<void*>(&mel_forward_kernel<N1, N2, InT, 1, C, R>);
-    return reinterpret_cast<void*>(&mel_forward_kernel<N1, N2, InT, 2, C, R>);
+    if constexpr (C) {
+      if (prio) {
+        if (pm == 0) return reinterpret_cast<void*>(&mel_forward_kernel<N1, N2, InT, 0, C, R, true>);
+        if (pm == 1) return reinterpret_cast<void*>(&mel_forward_kernel<N1, N2, InT, 1, C, R, true>);
+        return reinterpret_cast<void*>(&mel_forward_kernel<N1, N2, InT, 2, C, R, true>);
+      }
+    }
+    if (pm == 0) return reinterpret_cast<void*>(&mel_forward_kernel<N1, N2, InT, 0, C, R, false>);
+    if (pm == 1) return reinterpret_cast<void*>(&mel_forward_kernel<N1, N2, InT, 1, C, R, false>);
+    return reinterpret_cast<void*>(&mel_forward_kernel<N1, N2, InT, 2, C, R, false>);
   };
   auto by_layout = [&](auto in_tag, auto copy_tag) -> void* {
     if constexpr (kRowsCapable<N1, N2>) {
@@ -858,7 +874,7 @@ void* kernel_for(int in_dtype, int pmode, bool copy, bool rows) {
 // Shapes built into the library (n_fft/2 = N1 * N2).
 #define FM_FOR_EACH_SHAPE(X) \
   X(8, 4) X(8, 8) X(8, 16) X(8, 25) X(16, 16) X(32, 16) X(32, 32) X(64, 32)
-#define FM_DECLARE_SHAPE(A, B) extern template void* kernel_for<A, B>(int, int, bool, bool);
+#define FM_DECLARE_SHAPE(A, B) extern template void* kernel_for<A, B>(int, int, bool, bool, bool);
 FM_FOR_EACH_SHAPE(FM_DECLARE_SHAPE)
 #undef FM_DECLARE_SHAPE
 

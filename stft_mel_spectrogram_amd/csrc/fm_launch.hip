@@ -26,10 +26,10 @@ void* select_backward_kernel(const Plan& p) {
   return nullptr;
 }
 
-void* select_kernel(const Plan& p, int in_dtype, bool copy, bool rows) {
+void* select_kernel(const Plan& p, int in_dtype, bool copy, bool rows, bool prio = false) {
   const int pm = power_mode(p);
 #define FM_SELECT_SHAPE(A, B) \
-  if (p.fft.n1 == A && p.fft.n2 == B) return kernel_for<A, B>(in_dtype, pm, copy, rows);
+  if (p.fft.n1 == A && p.fft.n2 == B) return kernel_for<A, B>(in_dtype, pm, copy, rows, prio);
   FM_FOR_EACH_SHAPE(FM_SELECT_SHAPE)
 #undef FM_SELECT_SHAPE
   return nullptr;
@@ -143,11 +143,13 @@ int upload_plan(Plan& p) {
   for (int dt : {FM_F32, FM_I16}) {
     for (bool copy : {false, true}) {
       for (bool rows : {false, true}) {
-        if (rows && !rows_built) continue;
-        void* k = select_kernel(p, dt, copy, rows);
-        if (!k) return set_error(FM_E_UNSUPPORTED, "no kernel for this n_fft");
-        e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, p.lds_bytes);
-        if (e != hipSuccess) return hip_fail(e, "hipFuncSetAttribute");
+        for (bool prio : {false, true}) {
+          if ((rows && !rows_built) || (prio && !copy)) continue;
+          void* k = select_kernel(p, dt, copy, rows, prio);
+          if (!k) return set_error(FM_E_UNSUPPORTED, "no kernel for this n_fft");
+          e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, p.lds_bytes);
+          if (e != hipSuccess) return hip_fail(e, "hipFuncSetAttribute");
+        }
       }
     }
   }
@@ -339,7 +341,7 @@ int launch_forward(const Plan& p, const void* in, int in_dtype, int64_t batch, i
   a.tab_lds = tile_tables_offset(p, G);
   a.twn_lds = tile_twiddles_offset(p, G, rows);
 
-  void* k = select_kernel(p, in_dtype, c.copy, rows);
+  void* k = select_kernel(p, in_dtype, c.copy, rows, c.phase_prio && c.copy);
   if (!k) return set_error(FM_E_UNSUPPORTED, "no kernel for this n_fft");
   void* args[] = {&a};
   e = hipLaunchKernel(k, dim3(static_cast<unsigned>(n_tiles)), dim3(rows ? kRowsThreads : p.threads),

@@ -2,6 +2,6 @@
 #include "fm_backward.h"
 
 namespace fm {
-template void* kernel_for<8, 4>(int, int, bool, bool);
+template void* kernel_for<8, 4>(int, int, bool, bool, bool);
 template void* backward_kernel_for<8, 4>(int);
 }  // namespace fm

@@ -185,3 +185,25 @@ def test_vector_mel_equals_matrix_mel(n_fft, tiles, dtype, monkeypatch):
                 torch.cuda.synchronize()
                 print(f"[case] n_fft={n_fft} {dtype} mels={n_mels} {layout} tile={g}", flush=True)
                 assert torch.equal(outs["valu"], outs["mfma"]), (n_fft, dtype, n_mels, layout, g)
+
+
+@pytest.mark.parametrize("n_fft,hop", [(400, 160), (512, 160), (1024, 256)])
+def test_phase_priority_variant_equals_plain(n_fft, hop, monkeypatch):
+    """The phase-priority kernels (each wave lowering its issue priority
+    phase by phase; chosen for calls of one round with two or more
+    workgroups on a CU, FM_PRIO=1 forces them) only reorder issue: outputs
+    equal the plain kernels' bit for bit, in both second-pass layouts."""
+    from stft_mel_spectrogram_amd import MelSpectrogram
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    rng = np.random.default_rng(n_fft + hop)
+    x = torch.from_numpy(rng.standard_normal((4, 60 * hop + 311)).astype(np.float32)).to("cuda")
+    for layout in ("rows", "split"):
+        outs = {}
+        for prio in ("0", "1"):
+            monkeypatch.setenv("FM_FORWARD", layout)
+            monkeypatch.setenv("FM_PRIO", prio)
+            outs[prio] = MelSpectrogram(sample_rate=16000, n_fft=n_fft, hop_length=hop, n_mels=64)(x)
+        torch.cuda.synchronize()
+        print(f"[case] n_fft={n_fft} hop={hop} {layout}: FM_PRIO 0 vs 1", flush=True)
+        assert torch.equal(outs["0"], outs["1"]), (n_fft, layout)
