@@ -233,12 +233,36 @@ __device__ __forceinline__ void mel_valu(const float* P, CInt* qt, CFloat* qw, i
     const float* p2 = prow + h[2];
     const float* p3 = prow + h[3];
     float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
-#pragma unroll 4
-    for (int i = 0; i < L; ++i) {
-      a0 = fmaf(w[4 * i + 0], p0[i], a0);
-      a1 = fmaf(w[4 * i + 1], p1[i], a1);
-      a2 = fmaf(w[4 * i + 2], p2[i], a2);
-      a3 = fmaf(w[4 * i + 3], p3[i], a3);
+    // four steps per round from running pointers, so that a round's reads
+    // share one address per filter (immediate LDS offsets) and its 16
+    // weights are one scalar load; then the last 0-3 steps as a pair and a
+    // single, straight-line
+    int i = 0;
+    for (; i + 4 <= L; i += 4, p0 += 4, p1 += 4, p2 += 4, p3 += 4, w += 16) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        a0 = fmaf(w[4 * u + 0], p0[u], a0);
+        a1 = fmaf(w[4 * u + 1], p1[u], a1);
+        a2 = fmaf(w[4 * u + 2], p2[u], a2);
+        a3 = fmaf(w[4 * u + 3], p3[u], a3);
+      }
+    }
+    if (L - i >= 2) {
+      a0 = fmaf(w[0], p0[0], a0);
+      a1 = fmaf(w[1], p1[0], a1);
+      a2 = fmaf(w[2], p2[0], a2);
+      a3 = fmaf(w[3], p3[0], a3);
+      a0 = fmaf(w[4], p0[1], a0);
+      a1 = fmaf(w[5], p1[1], a1);
+      a2 = fmaf(w[6], p2[1], a2);
+      a3 = fmaf(w[7], p3[1], a3);
+      i += 2, p0 += 2, p1 += 2, p2 += 2, p3 += 2, w += 8;
+    }
+    if (L - i >= 1) {
+      a0 = fmaf(w[0], p0[0], a0);
+      a1 = fmaf(w[1], p1[0], a1);
+      a2 = fmaf(w[2], p2[0], a2);
+      a3 = fmaf(w[3], p3[0], a3);
     }
     if (st) {
       const int m = 4 * q;  // < n_mels
