@@ -271,7 +271,7 @@ typedef struct fm_plan_info {
  * row's values exchanged between lanes); built for n_fft 64 ... 2048.
  * AUTO (the default for n_fft 64 ... 2048): ROWS or SPLIT chosen per call
  * from the call's size (fm_forward_config reports the choice):
- * n_fft 400 and 2048 always ROWS; the other sizes ROWS when its
+ * n_fft 256, 400, 512 and 2048 always ROWS; the other sizes ROWS when its
  * workgroups number at most the device's compute units.  FM_FORWARD=rows or
  * FM_FORWARD=split at plan creation forces one of them.  ROWS and SPLIT
  * compute the same operations in the same order: their outputs are

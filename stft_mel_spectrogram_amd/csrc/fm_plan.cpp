@@ -664,19 +664,24 @@ int choose_tile(const Plan& p, int64_t batch, int64_t T, int threads, const std:
 // Kernel and tiling of one forward call.  FM_FWD_AUTO plans choose the
 // second pass's layout per call, from same-box A/B measurements of the two
 // (identical outputs):
-// - n_fft 400 (8 x 25) and 2048 (32 x 32): rows always.  At n_fft 2048 the
+// - n_fft 400 (8 x 25), 2048 (32 x 32), 256 (8 x 16) and 512 (16 x 16): rows
+//   always.  At n_fft 2048 the
 //   pair layout leaves half of its 512 threads idle in pass 2 at the
 //   14-17-frame tiles that fit the LDS (64 x 220500: 94.1 against 103.1
 //   us).  At n_fft 400 rows measured 1-17% faster at every call size tried
 //   with the tile copy below (8 x 480000: 16.76-16.87 against 17.24-17.31
 //   us; int16: 16.36 against 17.29; 16 x 480000: 30.3 against 32.5; 1 x
-//   16000: 6.6 against 8.1).
+//   16000: 6.6 against 8.1).  At n_fft 256 and 512 (hop 64 and 160, with
+//   the vector-unit mel stage) rows measured 1-9% faster at every call size
+//   tried: n_fft 256, 2 / 4 / 8 / 16 x 480000: 8.22 / 10.13 / 18.43 / 34.79
+//   against 8.56 / 10.56 / 20.33 / 36.96 us; n_fft 512: 8.36 / 9.87 / 18.14
+//   / 28.97 against 8.51 / 10.17 / 18.19 / 30.54 us.
 // - the other shapes built with both layouts: rows when its workgroups fit
 //   one per compute unit (the latency-bound calls: n_fft 1024, 16 x 32768:
-//   13.7 against 14.5 us; n_fft 512, 1 x 480000: 9.1 against 9.7 us); the
-//   pair layout for larger calls, where its workgroups share the CUs with
-//   fewer barriers per frame (n_fft 1024, 32 x 32768: 17.3 against 24.1 us;
-//   n_fft 256, 4 x 480000: 13.3 against 13.7 us).
+//   13.7 against 14.5 us); the pair layout for larger calls, where its
+//   workgroups share the CUs with fewer barriers per frame (n_fft 1024,
+//   32 x 32768: 17.3 against 24.1 us; n_fft 128, 8 x 480000: 17.4 against
+//   22.4 us; n_fft 64: 21.8 against 23.5 us).
 // Whole-tile sample copy (COPY variant; shapes with copy_capable): the
 // exchange buffer (G x (n_fft/2 + 4) complex) holds a tile's span ((G-1)
 // hop + n_fft samples + 32 bytes of alignment) whenever hop <= n_fft.  Every
@@ -729,7 +734,8 @@ FwdChoice choose_forward(const Plan& p, int64_t batch, int64_t T) {
   const int64_t rows_tiles = nb * ((T + rows_tile - 1) / rows_tile);
   bool rows = p.fwd_variant == kFwdRows;
   if (p.fwd_variant == kFwdAuto) {
-    const bool always = (p.fft.n1 == 32 && p.fft.n2 == 32) || (p.fft.n1 == 8 && p.fft.n2 == 25);
+    const bool always = (p.fft.n1 == 32 && p.fft.n2 == 32) || (p.fft.n1 == 8 && p.fft.n2 == 25) ||
+                        (p.fft.n1 == 8 && p.fft.n2 == 16) || (p.fft.n1 == 16 && p.fft.n2 == 16);
     rows = always || rows_tiles <= ncu;
   }
   if (rows) {

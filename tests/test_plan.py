@@ -508,14 +508,18 @@ def test_forward_config(monkeypatch):
         assert ps.forward_config(batch, 480000)[0] == N.FM_FWD_SPLIT
         assert pr.forward_config(batch, 480000)[0] == N.FM_FWD_ROWS
     monkeypatch.delenv("FM_FORWARD")
-    # n_fft 2048: always rows; the other sizes: rows while its workgroups fit
-    # one per compute unit
+    # n_fft 2048, 256 and 512: always rows; the other sizes: rows while its
+    # workgroups fit one per compute unit
     p2 = N.Plan(device=False, sample_rate=22050, n_fft=2048, hop_length=512, n_mels=128)
     for batch in (1, 64, 512):
         assert p2.forward_config(batch, 220500)[0] == N.FM_FWD_ROWS
+    for n in (256, 512):
+        pn = N.Plan(device=False, sample_rate=16000, n_fft=n, hop_length=n // 4, n_mels=40)
+        for batch in (1, 8, 64):
+            assert pn.forward_config(batch, 480000)[0] == N.FM_FWD_ROWS
     monkeypatch.setenv("FM_FORWARD", "rows")
     forced = {n: N.Plan(device=False, sample_rate=16000, n_fft=n, hop_length=n // 4, n_mels=40)
-              for n in (64, 256, 512, 1024)}
+              for n in (64, 128, 1024)}
     monkeypatch.delenv("FM_FORWARD")
     for n, pf in forced.items():
         pa = N.Plan(device=False, sample_rate=16000, n_fft=n, hop_length=n // 4, n_mels=40)
