@@ -625,13 +625,19 @@ int occupancy(const std::vector<int>& tab, int g) {
 }
 
 // Frames per tile for a tile-per-workgroup kernel of `threads` threads with
-// residency table `occ`.  Rounds of resident workgroups times the time of
-// one workgroup, which grows with its pass-1 rounds (frames per thread) on
-// top of a fixed part (pass 2, split, mel) worth about 3 of them; ties go to
-// smaller tiles (more compute units busy for small calls).  Measured: n_fft
-// 2048 x 64 signals picks 16 frames (7 rounds of 1 per CU: 127 us) where
-// "fewest frames on the busiest CU" picked 12 (9 rounds: 160 us); the
-// whisper shape keeps 47.  Calls with fewer tiles than CUs then shrink the
+// residency table `occ`.  The busiest CU's workgroups, in rounds of up to k
+// resident ones, where a round of j costs 1 + 0.7 (j - 1) workgroup times
+// (they share the SIMDs), times the time of one workgroup, which grows with
+// its pass-1 rounds (frames per thread) on top of a fixed part (pass 2,
+// split, mel) worth about 3 of them; ties go to smaller tiles (more compute
+// units busy for small calls).  Against counting whole rounds of k (same
+// box, us per launch): n_fft 400, 4 x 480000: 47-frame tiles, one per CU,
+// 9.89 against 32-frame ones 11.04; n_fft 512, 8 x 480000: 32 frames 17.12
+// against 24 frames 18.12; n_fft 128, 8 / 16 x 480000: 16.62 / 31.79
+// against 17.09 / 34.18; n_fft 64, 4 / 8 x 480000: 12.02 / 19.70 against
+// 13.32 / 21.70; the other benchmark calls keep their tiles.  Earlier:
+// n_fft 2048 x 64 signals picks 16 frames (7 rounds of 1 per CU: 127 us)
+// where "fewest frames on the busiest CU" picked 12 (9 rounds: 160 us).  Calls with fewer tiles than CUs then shrink the
 // tile while every tile still gets a CU of its own (1 x 16000 samples:
 // 1-frame tiles, 8.2 us, against 10.0 us with 32-frame tiles; below that
 // point, in calls of several rounds, the model above does not rank small
@@ -644,9 +650,12 @@ int choose_tile(const Plan& p, int64_t batch, int64_t T, int threads, const std:
   int64_t best_cost = INT64_MAX;
   for (int g = (p.tile_max + 1) / 2; g <= p.tile_max; ++g) {
     const int64_t tiles = batch * ((T + g - 1) / g);
-    const int64_t per_round = ncu * occupancy(occ, g);
-    const int64_t rounds = (tiles + per_round - 1) / per_round;
-    const int64_t cost = rounds * ((g + slots - 1) / slots + 3);
+    const int64_t k = occupancy(occ, g);
+    const int64_t w = (tiles + ncu - 1) / ncu;  // workgroups on the busiest CU
+    // tenths of a workgroup's time per round of j resident workgroups: 10 +
+    // 7 (j - 1) (they share the SIMDs)
+    const int64_t span = (w / k) * (10 + 7 * (k - 1)) + (w % k ? 10 + 7 * (w % k - 1) : 0);
+    const int64_t cost = span * ((g + slots - 1) / slots + 3);
     if (cost < best_cost) {
       best_cost = cost;
       best = g;
