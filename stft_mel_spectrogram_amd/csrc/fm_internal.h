@@ -196,6 +196,11 @@ constexpr int large_lds_bytes(int a, int c, int d, int nnz) {
 }
 // Frames one large-kernel workgroup takes at most per launch.
 constexpr int kLargeTileMax = 1024;
+// Three-pass shape that may serve the forward calls of a two-pass size
+// (n_fft 4096: 2048 = 16 * 16 * 8), or n3 == 0.
+constexpr FftShape large_alt_shape_for(int n_fft) {
+  return n_fft == 4096 ? FftShape{16, 16, 8} : FftShape{0, 0, 0};
+}
 
 struct Plan {
   // transform arguments
@@ -269,6 +274,13 @@ struct Plan {
   int pair_w_lds = 0;          //   float offset of the mel weights
   int pair_wg_per_cu = 1;      // paired: resident workgroups per CU (device)
   int large_wg_per_cu = 1;     // large-FFT kernel: resident workgroups per CU (device)
+  // The three-pass kernel serving forward calls: the plan's own shape for
+  // n_fft 8192 and 16384; for n_fft 4096 a second kernel beside the split
+  // one (fft 64 x 32, which also backs the backward), chosen per call.
+  FftShape lfft{0, 0, 0};      // n3 == 0: none
+  int large_threads = 0;       // its workgroup size (n2 * n3: one thread per filter too)
+  int large_lds = 0;           // its dynamic LDS per workgroup
+  int large_override = -1;     // FM_FORWARD=large|split at n_fft 4096, for A/B (-1: per call)
   // backward
   std::vector<BinTap> taps;      // [n_fft/2 + 1]
   int bwd_chunk_max = 0;         // frames per backward pass at most

@@ -263,7 +263,7 @@ void* large_kernel_for(int in_dtype, int pmode) {
 }
 
 // Large shapes built into the library (n_fft/2 = A * C * D).
-#define FM_FOR_EACH_LARGE_SHAPE(X) X(16, 16, 16) X(16, 16, 32)
+#define FM_FOR_EACH_LARGE_SHAPE(X) X(16, 16, 8) X(16, 16, 16) X(16, 16, 32)
 #define FM_DECLARE_LARGE_SHAPE(A, C, D) extern template void* large_kernel_for<A, C, D>(int, int);
 FM_FOR_EACH_LARGE_SHAPE(FM_DECLARE_LARGE_SHAPE)
 #undef FM_DECLARE_LARGE_SHAPE

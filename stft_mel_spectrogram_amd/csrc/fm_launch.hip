@@ -38,7 +38,7 @@ void* select_kernel(const Plan& p, int in_dtype, bool copy, bool rows, bool prio
 void* select_large_kernel(const Plan& p, int in_dtype) {
   const int pm = power_mode(p);
 #define FM_SELECT_LARGE(A, C, D) \
-  if (p.fft.n1 == A && p.fft.n2 == C && p.fft.n3 == D) return large_kernel_for<A, C, D>(in_dtype, pm);
+  if (p.lfft.n1 == A && p.lfft.n2 == C && p.lfft.n3 == D) return large_kernel_for<A, C, D>(in_dtype, pm);
   FM_FOR_EACH_LARGE_SHAPE(FM_SELECT_LARGE)
 #undef FM_SELECT_LARGE
   return nullptr;
@@ -123,17 +123,19 @@ int upload_plan(Plan& p) {
   p.d_quad = base + o_quad;
   p.d_quad_w = base + o_qw;
   // The large-FFT kernel: LDS opt-in and residency (no other kernel).
-  if (p.fwd_variant == kFwdLarge) {
+  if (p.lfft.n3) {  // the three-pass kernel (n_fft 8192, 16384; 4096 beside the split one)
     for (int dt : {FM_F32, FM_I16}) {
       void* k = select_large_kernel(p, dt);
       if (!k) return set_error(FM_E_UNSUPPORTED, "no large-FFT kernel for this n_fft");
-      e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, p.lds_bytes);
+      e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, p.large_lds);
       if (e != hipSuccess) return hip_fail(e, "hipFuncSetAttribute (large)");
     }
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, select_large_kernel(p, FM_F32), p.threads,
-                                                     p.lds_bytes) == hipSuccess)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, select_large_kernel(p, FM_F32), p.large_threads,
+                                                     p.large_lds) == hipSuccess)
       p.large_wg_per_cu = std::max(1, n);
+  }
+  if (p.fwd_variant == kFwdLarge) {
     p.has_device = true;
     return FM_OK;
   }
@@ -292,12 +294,12 @@ int launch_forward(const Plan& p, const void* in, int in_dtype, int64_t batch, i
                ((p.pad_left + p.zpad) % 2 == 0);
     a.out_f16 = p.out_dtype == FM_F16 ? 1 : 0;
     a.w16 = (p.nnz + 3) / 4;
-    a.w_lds = large_exchange_bytes(p.fft.n1, p.fft.n2, p.fft.n3);
+    a.w_lds = large_exchange_bytes(p.lfft.n1, p.lfft.n2, p.lfft.n3);
     void* k = select_large_kernel(p, in_dtype);
     if (!k) return set_error(FM_E_UNSUPPORTED, "no large-FFT kernel for this n_fft");
     void* args[] = {&a};
-    e = hipLaunchKernel(k, dim3(static_cast<unsigned>(tiles * batch)), dim3(p.threads), args,
-                        static_cast<size_t>(p.lds_bytes), static_cast<hipStream_t>(stream));
+    e = hipLaunchKernel(k, dim3(static_cast<unsigned>(tiles * batch)), dim3(p.large_threads), args,
+                        static_cast<size_t>(p.large_lds), static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "kernel launch (large)");
     return FM_OK;
   }

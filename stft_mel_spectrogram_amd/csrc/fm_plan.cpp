@@ -518,6 +518,22 @@ int build_host_plan(Plan& p, const fm_args& a) {
     const int v = std::atoi(e);
     if (v >= 1 && v <= 64) p.mel_valu_from = v;
   }
+  // ---- the three-pass kernel beside a two-pass size -------------------------
+  // Chosen per call in choose_forward where it fits: one thread per filter
+  // (n_mels <= its n2 * n3 threads) and its buffer plus the weights in LDS.
+  {
+    const FftShape ls = large_alt_shape_for(n_fft);
+    if (ls.n3 && n_mels <= large_threads(ls.n2, ls.n3) &&
+        large_lds_bytes(ls.n1, ls.n2, ls.n3, p.nnz) <= 160 * 1024) {
+      p.lfft = ls;
+      p.large_threads = large_threads(ls.n2, ls.n3);
+      p.large_lds = large_lds_bytes(ls.n1, ls.n2, ls.n3, p.nnz);
+      if (const char* e = std::getenv("FM_FORWARD")) {
+        if (std::string(e) == "large") p.large_override = 1;
+        if (std::string(e) == "split") p.large_override = 0;
+      }
+    }
+  }
   // ---- tile geometry -------------------------------------------------------
   if (fs.n3) {
     // The large-FFT kernel holds one frame's exchange buffer and walks its
@@ -528,6 +544,9 @@ int build_host_plan(Plan& p, const fm_args& a) {
       return set_error(FM_E_UNSUPPORTED, "mel filterbank too large for the LDS of one workgroup");
     p.bwd_chunk_max = 0;
     p.fwd_variant = kFwdLarge;
+    p.lfft = fs;
+    p.large_threads = p.threads;
+    p.large_lds = p.lds_bytes;
     p.tile_override = 0;
     p.bwd_chunk_override = 0;
     if (const char* e = std::getenv("FM_TILE_FRAMES")) {
@@ -714,18 +733,21 @@ FwdChoice choose_forward(const Plan& p, int64_t batch, int64_t T) {
     c.workgroups = std::min(batch * T, ncu * p.pair_wg_per_cu);
     return c;
   }
-  if (p.fwd_variant == kFwdLarge) {
-    // the fewest frames per workgroup that put every frame in the first
-    // round of resident workgroups (each walks its frames one at a time)
+  // the three-pass kernel: the fewest frames per workgroup that put every
+  // frame in the first round of resident workgroups (each walks its frames
+  // one at a time)
+  auto large = [&](int override_tile) {
     const int64_t slots = ncu * p.large_wg_per_cu;
-    int64_t g = p.tile_override > 0 ? p.tile_override : 1;
-    if (p.tile_override <= 0)
-      while (g < p.tile_max && nb * ((T + g - 1) / g) > slots) ++g;
-    c.variant = kFwdLarge;
-    c.tile = static_cast<int>(g);
-    c.workgroups = batch * ((T + g - 1) / g);
-    return c;
-  }
+    int64_t g = override_tile > 0 ? override_tile : 1;
+    if (override_tile <= 0)
+      while (g < kLargeTileMax && nb * ((T + g - 1) / g) > slots) ++g;
+    FwdChoice l;
+    l.variant = kFwdLarge;
+    l.tile = static_cast<int>(g);
+    l.workgroups = batch * ((T + g - 1) / g);
+    return l;
+  };
+  if (p.fwd_variant == kFwdLarge) return large(p.tile_override);
   auto tile_copy = [&](int g) {
     if (!copy_capable(p.fft.n1, p.fft.n2)) return false;
     // the exchange buffer must hold the span ((g - 1) hop + n_fft samples of
@@ -738,6 +760,14 @@ FwdChoice choose_forward(const Plan& p, int64_t batch, int64_t T) {
   c.tile = choose_tile(p, nb, T, p.threads, p.wg_per_cu);
   c.workgroups = batch * ((T + c.tile - 1) / c.tile);
   c.copy = tile_copy(c.tile);
+  // n_fft 4096: the three-pass kernel (16 x 16 x 8, two waves, several
+  // resident per CU) once the split kernel's 8-frame tiles, one per CU at a
+  // time, would take more than one round (same box, us per launch: 4 x
+  // 1323000 samples 46.3 against 57.6; 16 x 1323000: 137.0 against 196.7;
+  // 1 x 1323000, 216 tiles: 20.8 against 19.7)
+  if (p.lfft.n3 && p.fwd_variant == kFwdSplit &&
+      (p.large_override == 1 || (p.large_override < 0 && c.workgroups > ncu)))
+    return large(p.large_override == 1 ? p.tile_override : 0);  // FM_TILE_FRAMES when forced
   if (p.fwd_variant != kFwdRows && p.fwd_variant != kFwdAuto) return c;
   const int rows_tile = choose_tile(p, nb, T, kRowsThreads, p.rows_wg_per_cu);
   const int64_t rows_tiles = nb * ((T + rows_tile - 1) / rows_tile);

@@ -76,3 +76,65 @@ def test_large_fft_full_workloads(name):
     assert np.array_equal(got, run_gpu(x, **targs))
     rows = [0, cfg["batch"] - 1]
     assert_parity(got[rows], oracle(x[rows], **targs), f"full {name} (rows {rows})")
+
+
+# n_fft 4096 runs on the three-pass kernel (16 x 16 x 8) in calls where the
+# two-pass kernel's tiles would take more than one round; FM_FORWARD=large
+# forces it for the small cases here.
+CASES_4096 = [
+    (4096, 1024, 128, 60001, dict()),                                 # ragged last tile
+    (4096, 1000, 64, 30000, dict(power=1.0)),                         # hop not dividing n_fft
+    (4096, 333, 40, 20000, dict(power=1.5)),                          # odd hop: unpaired loads
+    (4096, 4096, 128, 40000, dict()),                                 # frames do not overlap
+    (4096, 1024, 1, 9000, dict(f_max=22050.0)),                       # one filter
+    (4096, 1024, 8, 4097, dict()),                                    # shortest reflect signal
+    (4096, 1024, 96, 25000, dict(center=False)),
+    (4096, 512, 128, 40000, dict(win_length=3000, normalized=True)),
+    (4096, 1024, 80, 30000, dict(mel_scale="slaney", norm="slaney", f_min=50.0)),
+    (4096, 1024, 128, 30000, dict(pad_mode="constant", pad=777)),
+    (4096, 1024, 128, 30000, dict(pad_mode="replicate")),
+    (4096, 1024, 128, 30000, dict(pad_mode="circular", pad=5)),
+]
+
+
+@pytest.mark.parametrize("n_fft,hop,mels,L,extra", CASES_4096,
+                         ids=[f"{c[0]}-{c[1]}-{c[2]}-{c[3]}-{'-'.join(c[4])}" for c in CASES_4096])
+def test_three_pass_4096_parity(monkeypatch, n_fft, hop, mels, L, extra):
+    monkeypatch.setenv("FM_FORWARD", "large")
+    x = np.random.default_rng(n_fft + hop + L + 1).standard_normal((2, L)).astype(np.float32) * 0.3
+    targs = dict(sample_rate=44100, n_fft=n_fft, hop_length=hop, n_mels=mels, **extra)
+    print(f"[case] three-pass n_fft {n_fft} hop {hop} mels {mels} L {L} {extra}", flush=True)
+    assert_parity(run_gpu(x, **targs), oracle(x, **targs), f"three-pass {n_fft}/{hop} {extra}")
+
+
+def test_three_pass_4096_int16_f16_and_tiles(monkeypatch):
+    monkeypatch.setenv("FM_FORWARD", "large")
+    q = np.random.default_rng(4096).integers(-32768, 32768, size=(3, 50001)).astype(np.int16)
+    targs = dict(sample_rate=44100, n_fft=4096, hop_length=1024, n_mels=128)
+    print("[case] three-pass int16 n_fft 4096", flush=True)
+    ref = oracle(q, **targs)
+    assert_parity(run_gpu(q, **targs), ref, "three-pass i16 4096")
+    assert_parity_f16(run_gpu(q, out_dtype=torch.float16, **targs), ref, "three-pass i16 -> f16 4096")
+    for tile in (1, 3, 5):
+        monkeypatch.setenv("FM_TILE_FRAMES", str(tile))
+        print(f"[case] three-pass n_fft 4096 tile {tile}", flush=True)
+        assert_parity(run_gpu(q, **targs), ref, f"three-pass 4096 tile {tile}")
+
+
+def test_music4096_full_workload_takes_three_pass():
+    """Full size (4 x 1323000 samples, 128 mels): the call takes the
+    three-pass kernel; every output finite, non-negative and identical on a
+    second launch; the first and last signals against the oracle."""
+    from stft_mel_spectrogram_amd import _native as N
+    cfg = W.workload("music4096")
+    x = W.make_signal(cfg)
+    targs = W.transform_args(cfg)
+    p = N.Plan(**targs)
+    assert p.forward_config(cfg["batch"], x.shape[1])[0] == N.FM_FWD_LARGE
+    p.close()
+    print(f"[case] full music4096 {x.shape}", flush=True)
+    got = run_gpu(x, **targs)
+    assert np.all(np.isfinite(got)) and np.all(got >= 0)
+    assert np.array_equal(got, run_gpu(x, **targs))
+    rows = [0, cfg["batch"] - 1]
+    assert_parity(got[rows], oracle(x[rows], **targs), f"full music4096 (rows {rows})")

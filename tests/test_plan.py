@@ -533,3 +533,32 @@ def test_forward_config(monkeypatch):
                 f_max=22050.0)
     v, g, wg = pl.forward_config(16, 441000)
     assert v == N.FM_FWD_LARGE and wg == 16 * -(-pl.out_frames(441000) // g)
+
+
+def test_n_fft_4096_three_pass_choice(monkeypatch):
+    """n_fft 4096 keeps its two-pass kernel (and the backward) and takes the
+    three-pass kernel in calls whose two-pass tiles outnumber the compute
+    units; more filters than its threads, or FM_FORWARD, keep it off."""
+    monkeypatch.delenv("FM_FORWARD", raising=False)
+    p = N.Plan(device=False, sample_rate=44100, n_fft=4096, hop_length=1024, n_mels=128)
+    assert p.info().fft_n3 == 0 and p.info().fft_n1 == 64  # its own (two-pass) shape
+    v1, g1, w1 = p.forward_config(1, 1323000)
+    assert v1 == N.FM_FWD_SPLIT and w1 <= 256
+    for batch in (4, 16):
+        v, g, wg = p.forward_config(batch, 1323000)
+        T = p.out_frames(1323000)
+        assert v == N.FM_FWD_LARGE and wg == batch * -(-T // g)
+        assert batch * -(-T // (g - 1)) > 256 if g > 1 else True  # fewest frames in one round
+    wide = N.Plan(device=False, sample_rate=44100, n_fft=4096, hop_length=1024, n_mels=200)
+    assert wide.forward_config(16, 1323000)[0] == N.FM_FWD_SPLIT
+    monkeypatch.setenv("FM_FORWARD", "split")
+    ps = N.Plan(device=False, sample_rate=44100, n_fft=4096, hop_length=1024, n_mels=128)
+    monkeypatch.setenv("FM_FORWARD", "large")
+    pl = N.Plan(device=False, sample_rate=44100, n_fft=4096, hop_length=1024, n_mels=128)
+    assert ps.forward_config(16, 1323000)[0] == N.FM_FWD_SPLIT
+    assert pl.forward_config(1, 16000)[0] == N.FM_FWD_LARGE
+    # other sizes never take it
+    monkeypatch.delenv("FM_FORWARD")
+    for n in (1024, 2048):
+        pn = N.Plan(device=False, sample_rate=44100, n_fft=n, hop_length=n // 4, n_mels=128)
+        assert pn.forward_config(64, 1323000)[0] != N.FM_FWD_LARGE
