@@ -266,7 +266,7 @@ typedef struct fm_plan_info {
  * LARGE: n_fft 8192 and 16384, whose complex FFT of n_fft/2 points runs in
  * three passes over one LDS buffer, one frame at a time per workgroup, with
  * the mel projection over the CSR rows (these sizes have no backward).  A
- * SPLIT plan of n_fft 4096 with at most 128 filters also holds this kernel
+ * SPLIT plan of n_fft 4096 also holds this kernel
  * (2048 = 16 x 16 x 8) and runs a call on it when the SPLIT tiles would
  * outnumber the compute units (fm_forward_config reports LARGE then; the
  * plan's own shape, its info and its backward stay SPLIT); FM_FORWARD=large

@@ -39,6 +39,7 @@ constexpr int32_t mel_filter_word(int mel0, int nrow) { return mel0 | (nrow << 1
 // <= (n_fft/2 + 1 + 3)/4 + 3 <= 516 for n_fft <= 4096: ten bits.
 constexpr int32_t mel_step_word(int ksteps, int s_hi) { return ksteps | (s_hi << 20); }
 constexpr int kMelBlock = 16;
+constexpr int kMaxMels = 256;      // filters per plan at most
 constexpr int kMaxMelBlocks = 16;  // n_mels <= 256
 constexpr int kMelWaves = 4;       // waves of a workgroup
 // The kernel runs steps in groups of this many (blocks are zero-padded to
@@ -278,7 +279,7 @@ struct Plan {
   // n_fft 8192 and 16384; for n_fft 4096 a second kernel beside the split
   // one (fft 64 x 32, which also backs the backward), chosen per call.
   FftShape lfft{0, 0, 0};      // n3 == 0: none
-  int large_threads = 0;       // its workgroup size (n2 * n3: one thread per filter too)
+  int large_threads = 0;       // its workgroup size (n2 * n3)
   int large_lds = 0;           // its dynamic LDS per workgroup
   int large_override = -1;     // FM_FORWARD=large|split at n_fft 4096, for A/B (-1: per call)
   // backward

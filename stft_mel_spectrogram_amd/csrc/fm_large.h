@@ -21,13 +21,15 @@
 //           which holds Z[ka + A kc + A C kd];
 // then per bin k the real split X[k] = (Z[k] + conj Z[M-k])
 // - i W_N^k (Z[k] - conj Z[M-k]) and |X|^p into a power row (aliasing the
-// buffer), and the mel projection of that row, one thread per filter over
-// its CSR run of nonzero weights (copied into LDS behind the buffer once per
-// workgroup).  Each pass writes back the positions it
+// buffer), and the mel projection of that row, thread t taking filters t,
+// t + NT, ... over their CSR runs of nonzero weights (copied into LDS behind
+// the buffer once per workgroup).  Each pass writes back the positions it
 // read, so one buffer serves all three; its strides (D + 1 per c, an odd
 // C (D + 1) + 1 per a) put the threads of a pass, and the split's reads of
 // consecutive bins, on distinct banks or at most two to a bank.
 #pragma once
+
+#include <type_traits>
 
 #include "fm_kernel.h"
 
@@ -88,7 +90,7 @@ __device__ __forceinline__ void large_frame_samples(float2 (&v)[A], const InT* x
   }
 }
 
-template <int A, int C, int D, typename InT, int PMODE>
+template <int A, int C, int D, typename InT, int PMODE, bool MANY>
 __global__ __launch_bounds__((kLargeThreads<A, C, D>), 2) void mel_forward_large_kernel(LArgs a) {
   constexpr int B = C * D;
   constexpr int M = A * B;
@@ -143,9 +145,10 @@ __global__ __launch_bounds__((kLargeThreads<A, C, D>), 2) void mel_forward_large
 #pragma unroll
     for (int kc = 0; kc < C; ++kc) tw2[kc] = a.tw_m[A * d1 * kc];
   }
-  // this thread's filter (the mel stage), read once
-  MelRow row{0, 0, 0, 0};
-  if (tid < a.n_mels) row = a.rows[tid];
+  // this thread's filter in the mel stage, read once (MANY: more filters
+  // than threads, thread t also takes t + NT, ..., their rows read per frame)
+  MelRow row0{0, 0, 0, 0};
+  if (tid < a.n_mels) row0 = a.rows[tid];
   // split twiddles W_N^k for k = tid + NT*j: the per-thread factor W_N^tid
   // times the wave-uniform W_N^(NT*j), read through the scalar unit
   const float2 wt = a.tw_n[tid];
@@ -232,15 +235,29 @@ __global__ __launch_bounds__((kLargeThreads<A, C, D>), 2) void mel_forward_large
     if (tid == 0) P[M] = p_nyq;
     if (f == 0) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the weight copies have landed
     __syncthreads();
-    // ---- mel projection: thread m over its CSR run ------------------------
-    if (tid < a.n_mels) {
-      const float* pr = P + row.first;
-      const float* wr = WL + row.off;
-      float acc = 0.0f;
-      for (int j = 0; j < row.len; ++j) acc = fmaf(pr[j], wr[j], acc);
-      const long long o = obase + static_cast<long long>(tid) * a.n_frames + f;
-      if (a.out_f16) static_cast<_Float16*>(a.out)[o] = static_cast<_Float16>(acc);
-      else static_cast<float*>(a.out)[o] = acc;
+    // ---- mel projection: filter m over its CSR run ------------------------
+    if constexpr (!MANY) {
+      if (tid < a.n_mels) {
+        const float* pr = P + row0.first;
+        const float* wr = WL + row0.off;
+        float acc = 0.0f;
+        for (int j = 0; j < row0.len; ++j) acc = fmaf(pr[j], wr[j], acc);
+        const long long o = obase + static_cast<long long>(tid) * a.n_frames + f;
+        if (a.out_f16) static_cast<_Float16*>(a.out)[o] = static_cast<_Float16>(acc);
+        else static_cast<float*>(a.out)[o] = acc;
+      }
+    } else {
+#pragma unroll 1
+      for (int m = tid; m < a.n_mels; m += NT) {
+        const MelRow row = m == tid ? row0 : a.rows[m];
+        const float* pr = P + row.first;
+        const float* wr = WL + row.off;
+        float acc = 0.0f;
+        for (int j = 0; j < row.len; ++j) acc = fmaf(pr[j], wr[j], acc);
+        const long long o = obase + static_cast<long long>(m) * a.n_frames + f;
+        if (a.out_f16) static_cast<_Float16*>(a.out)[o] = static_cast<_Float16>(acc);
+        else static_cast<float*>(a.out)[o] = acc;
+      }
     }
     __syncthreads();  // P is read before the next frame's pass 1 overwrites it
   }
@@ -248,23 +265,34 @@ __global__ __launch_bounds__((kLargeThreads<A, C, D>), 2) void mel_forward_large
 
 }  // namespace
 
-// Kernel entry of one large shape for an input type and a power mode (0: p =
-// 2, 1: p = 1, 2: general p); instantiated in fm_large_<A>x<C>x<D>.hip.
+// Kernel entry of one large shape for an input type, a power mode (0: p =
+// 2, 1: p = 1, 2: general p) and whether the plan has more filters than the
+// workgroup has threads (built only for shapes of fewer than 256 threads;
+// nullptr otherwise); instantiated in fm_large_<A>x<C>x<D>.hip.
 template <int A, int C, int D>
-void* large_kernel_for(int in_dtype, int pmode) {
-  auto pick = [](auto in_tag, int pm) -> void* {
+void* large_kernel_for(int in_dtype, int pmode, bool many) {
+  auto pick = [](auto in_tag, auto many_tag, int pm) -> void* {
     using InT = decltype(in_tag);
-    if (pm == 0) return reinterpret_cast<void*>(&mel_forward_large_kernel<A, C, D, InT, 0>);
-    if (pm == 1) return reinterpret_cast<void*>(&mel_forward_large_kernel<A, C, D, InT, 1>);
-    return reinterpret_cast<void*>(&mel_forward_large_kernel<A, C, D, InT, 2>);
+    constexpr bool M = decltype(many_tag)::value;
+    if (pm == 0) return reinterpret_cast<void*>(&mel_forward_large_kernel<A, C, D, InT, 0, M>);
+    if (pm == 1) return reinterpret_cast<void*>(&mel_forward_large_kernel<A, C, D, InT, 1, M>);
+    return reinterpret_cast<void*>(&mel_forward_large_kernel<A, C, D, InT, 2, M>);
   };
-  if (in_dtype == FM_I16) return pick(int16_t{}, pmode);
-  return pick(float{}, pmode);
+  if (many) {
+    if constexpr (kLargeThreads<A, C, D> < kMaxMels) {
+      if (in_dtype == FM_I16) return pick(int16_t{}, std::true_type{}, pmode);
+      return pick(float{}, std::true_type{}, pmode);
+    } else {
+      return nullptr;
+    }
+  }
+  if (in_dtype == FM_I16) return pick(int16_t{}, std::false_type{}, pmode);
+  return pick(float{}, std::false_type{}, pmode);
 }
 
 // Large shapes built into the library (n_fft/2 = A * C * D).
 #define FM_FOR_EACH_LARGE_SHAPE(X) X(16, 16, 8) X(16, 16, 16) X(16, 16, 32)
-#define FM_DECLARE_LARGE_SHAPE(A, C, D) extern template void* large_kernel_for<A, C, D>(int, int);
+#define FM_DECLARE_LARGE_SHAPE(A, C, D) extern template void* large_kernel_for<A, C, D>(int, int, bool);
 FM_FOR_EACH_LARGE_SHAPE(FM_DECLARE_LARGE_SHAPE)
 #undef FM_DECLARE_LARGE_SHAPE
 

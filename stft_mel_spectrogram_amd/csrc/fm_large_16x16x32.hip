@@ -2,5 +2,5 @@
 #include "fm_large.h"
 
 namespace fm {
-template void* large_kernel_for<16, 16, 32>(int, int);
+template void* large_kernel_for<16, 16, 32>(int, int, bool);
 }  // namespace fm

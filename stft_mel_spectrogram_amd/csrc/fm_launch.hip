@@ -38,7 +38,8 @@ void* select_kernel(const Plan& p, int in_dtype, bool copy, bool rows, bool prio
 void* select_large_kernel(const Plan& p, int in_dtype) {
   const int pm = power_mode(p);
 #define FM_SELECT_LARGE(A, C, D) \
-  if (p.lfft.n1 == A && p.lfft.n2 == C && p.lfft.n3 == D) return large_kernel_for<A, C, D>(in_dtype, pm);
+  if (p.lfft.n1 == A && p.lfft.n2 == C && p.lfft.n3 == D) \
+    return large_kernel_for<A, C, D>(in_dtype, pm, p.n_mels > p.large_threads);
   FM_FOR_EACH_LARGE_SHAPE(FM_SELECT_LARGE)
 #undef FM_SELECT_LARGE
   return nullptr;

@@ -233,7 +233,7 @@ int build_host_plan(Plan& p, const fm_args& a) {
     return set_error(FM_E_INVAL, fmt("unknown normalized", a.normalized));
   if (a.out_dtype != FM_F32 && a.out_dtype != FM_F16)
     return set_error(FM_E_INVAL, fmt("out_dtype must be FM_F32 or FM_F16", a.out_dtype));
-  if (n_mels > 256) return set_error(FM_E_UNSUPPORTED, fmt("n_mels > 256 is not supported", n_mels));
+  if (n_mels > kMaxMels) return set_error(FM_E_UNSUPPORTED, fmt("n_mels > 256 is not supported", n_mels));
   FftShape fs;
   if (!fft_shape_for(n_fft, &fs))
     return set_error(FM_E_UNSUPPORTED, fmt("n_fft not built (supported: 400 and powers of two 64..16384)", n_fft));
@@ -519,12 +519,11 @@ int build_host_plan(Plan& p, const fm_args& a) {
     if (v >= 1 && v <= 64) p.mel_valu_from = v;
   }
   // ---- the three-pass kernel beside a two-pass size -------------------------
-  // Chosen per call in choose_forward where it fits: one thread per filter
-  // (n_mels <= its n2 * n3 threads) and its buffer plus the weights in LDS.
+  // Chosen per call in choose_forward where its buffer plus the weights fit
+  // the LDS.
   {
     const FftShape ls = large_alt_shape_for(n_fft);
-    if (ls.n3 && n_mels <= large_threads(ls.n2, ls.n3) &&
-        large_lds_bytes(ls.n1, ls.n2, ls.n3, p.nnz) <= 160 * 1024) {
+    if (ls.n3 && large_lds_bytes(ls.n1, ls.n2, ls.n3, p.nnz) <= 160 * 1024) {
       p.lfft = ls;
       p.large_threads = large_threads(ls.n2, ls.n3);
       p.large_lds = large_lds_bytes(ls.n1, ls.n2, ls.n3, p.nnz);

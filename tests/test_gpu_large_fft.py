@@ -94,6 +94,8 @@ CASES_4096 = [
     (4096, 1024, 128, 30000, dict(pad_mode="constant", pad=777)),
     (4096, 1024, 128, 30000, dict(pad_mode="replicate")),
     (4096, 1024, 128, 30000, dict(pad_mode="circular", pad=5)),
+    (4096, 1024, 256, 30000, dict()),                                 # two filters per thread
+    (4096, 1024, 129, 30000, dict(power=1.0)),                        # one thread takes a second
 ]
 
 

@@ -355,7 +355,7 @@ def test_large_fft_geometry(n_fft, shape):
         ybytes = a * (c * (d + 1) + 1) * 8                   # exchange buffer (complex)
         assert inf.lds_bytes == ybytes + 16 * (-(-inf.nnz // 4)) <= 160 * 1024   # + CSR weights
         assert ybytes >= 4 * (n_fft // 2 + 1)                 # the power row fits the buffer
-        assert n_mels <= inf.threads                          # one thread per filter
+        assert n_mels <= 256 and -(-256 // inf.threads) >= -(-n_mels // inf.threads)  # filters tid + threads r
         # the largest position the passes touch is inside the buffer
         assert ((a - 1) * (c * (d + 1) + 1) + (c - 1) * (d + 1) + d - 1) * 8 < ybytes
     # every bin position (ka, kc, kd) maps to a distinct buffer slot
@@ -538,7 +538,7 @@ def test_forward_config(monkeypatch):
 def test_n_fft_4096_three_pass_choice(monkeypatch):
     """n_fft 4096 keeps its two-pass kernel (and the backward) and takes the
     three-pass kernel in calls whose two-pass tiles outnumber the compute
-    units; more filters than its threads, or FM_FORWARD, keep it off."""
+    units, or as FM_FORWARD says."""
     monkeypatch.delenv("FM_FORWARD", raising=False)
     p = N.Plan(device=False, sample_rate=44100, n_fft=4096, hop_length=1024, n_mels=128)
     assert p.info().fft_n3 == 0 and p.info().fft_n1 == 64  # its own (two-pass) shape
@@ -549,8 +549,9 @@ def test_n_fft_4096_three_pass_choice(monkeypatch):
         T = p.out_frames(1323000)
         assert v == N.FM_FWD_LARGE and wg == batch * -(-T // g)
         assert batch * -(-T // (g - 1)) > 256 if g > 1 else True  # fewest frames in one round
-    wide = N.Plan(device=False, sample_rate=44100, n_fft=4096, hop_length=1024, n_mels=200)
-    assert wide.forward_config(16, 1323000)[0] == N.FM_FWD_SPLIT
+    # more filters than its 128 threads: two per thread
+    wide = N.Plan(device=False, sample_rate=44100, n_fft=4096, hop_length=1024, n_mels=256)
+    assert wide.forward_config(16, 1323000)[0] == N.FM_FWD_LARGE
     monkeypatch.setenv("FM_FORWARD", "split")
     ps = N.Plan(device=False, sample_rate=44100, n_fft=4096, hop_length=1024, n_mels=128)
     monkeypatch.setenv("FM_FORWARD", "large")
